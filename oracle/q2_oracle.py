@@ -1,0 +1,275 @@
+"""CPU oracle for the Q2_0 ternary linear, its low-rank side branch and the
+4-bit nibble variant.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, obviously correct
+definition of what the HIP library computes.  Only the test suite, the smoke
+check and the CPU-baseline leg of the benchmark may import it; the library and
+its Python binding never do, and the two share no code.
+
+Everything is NumPy float64 (or exact Python integers/fractions in the scalar
+helpers).  Every decoded value below is exact in float64: bf16 and f16 values
+are exact, a bf16 x f16 product has at most 8 + 11 significant bits, and the
+4-bit dequantised weight (q - z) * s is computed exactly from f16 inputs.  The
+only rounding is float64 summation inside a BLAS dgemm, far below the 1e-4
+relative tolerance the GPU path is held to.
+
+Sources (web pages on ternary-weight image models):
+* "We're Teaching Your Browser to Paint" (aitherium.com), section "The lucky
+  break that wasn't luck": codes {0,1,2} packed LSB-first four per byte along
+  the input axis; 128-weight blocks with one f16 scale; a weight is (q - 1) x d;
+  the converter's only rounding is the f32 -> f16 scale cast and it aborts when
+  that cast is not exact.
+* same page, section "The GPU driver...": 2-bit rows are independent byte runs,
+  so a row slice of the weight is a byte-range slice; a projection can be split
+  along its input axis into two products that are summed.
+* "You Can Now Just Ask for an Image" (aitherium.com), section "The bug that
+  hid in one flipped bit": two 4-bit codes per byte, the low nibble holding the
+  even position; and "We're Teaching..." section "What's left": the 4-bit
+  encoder weights dequantise as (q - zero) x scale.
+* mindview-t2i-turbo model card, section "One step": the side branch is
+  y = W x + B (A x).
+
+Readings where the pages leave a step open (each also listed in the design
+notes): consecutive codes share a byte (code k sits in bits 2(k%4)..2(k%4)+1
+of byte k//4); scales are a separate array [N, K/128] (structure-of-arrays);
+code 3 is rejected by the packer; f32 -> f16 rounds to nearest even and
+non-finite scales are rejected; the 4-bit group is 128 with an f16 zero point
+in code units; the low-rank branch has no extra scale factor; outputs are
+float32 on the GPU and float64 here.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+GROUP = 128
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+def f16_decode_scalar(bits: int) -> float:
+    """IEEE 754 binary16 bit pattern -> Python float, from the format's definition
+    (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits)."""
+    sign = -1.0 if (bits >> 15) & 1 else 1.0
+    exp = (bits >> 10) & 0x1F
+    frac = bits & 0x3FF
+    if exp == 0x1F:
+        return sign * math.inf if frac == 0 else math.nan
+    if exp == 0:
+        return sign * math.ldexp(frac, -24)            # subnormal: frac * 2^-14 * 2^-10
+    return sign * math.ldexp(1024 + frac, exp - 25)     # (1 + frac/2^10) * 2^(exp-15)
+
+
+def bf16_decode_scalar(bits: int) -> float:
+    """bfloat16 bit pattern -> Python float (1 sign, 8 exponent bits with bias
+    127, 7 fraction bits)."""
+    sign = -1.0 if (bits >> 15) & 1 else 1.0
+    exp = (bits >> 7) & 0xFF
+    frac = bits & 0x7F
+    if exp == 0xFF:
+        return sign * math.inf if frac == 0 else math.nan
+    if exp == 0:
+        return sign * math.ldexp(frac, -133)           # frac * 2^-126 * 2^-7
+    return sign * math.ldexp(128 + frac, exp - 134)
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    """Vectorised f16 decode: u16 bit patterns -> float64 values."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Vectorised bf16 decode: a bf16 pattern is the top half of a float32."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Q2_0 pack (load-time conversion)
+# ---------------------------------------------------------------------------
+
+class PackError(ValueError):
+    """Raised by pack_q2.  kind is 'code' or 'scale'; index is the flat
+    row-major index of the first offending element of codes [N, K] or of
+    scales [N, K/128].  Codes are checked before scales."""
+
+    def __init__(self, kind: str, index: int):
+        super().__init__(f"q2 pack: bad {kind} at flat index {index}")
+        self.kind = kind
+        self.index = index
+
+
+def pack_q2(codes: np.ndarray, scales: np.ndarray):
+    """codes u8 [N, K] in {0,1,2}, scales float32 [N, K/128]
+    -> (packed u8 [N, K/4], scale bits u16 [N, K/128]).
+
+    Byte j of a row holds codes 4j..4j+3, code 4j+i in bits 2i and 2i+1
+    (least significant pair first).  Each scale is cast to f16 (nearest even)
+    and must come back unchanged when cast back to float32; NaN and inf are
+    refused.
+    """
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    n, k = codes.shape
+    if k % GROUP or scales.shape != (n, k // GROUP):
+        raise ValueError("q2 pack: K must be a multiple of 128 and scales [N, K/128]")
+    bad = np.flatnonzero(codes > 2)
+    if bad.size:
+        raise PackError("code", int(bad[0]))
+    half = scales.astype(np.float16)
+    back = half.astype(np.float32)
+    ok = np.isfinite(scales) & (back == scales)
+    bad = np.flatnonzero(~ok)
+    if bad.size:
+        raise PackError("scale", int(bad[0]))
+    c = codes.reshape(n, k // 4, 4).astype(np.uint32)
+    packed = c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)
+    return packed.astype(np.uint8), half.view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Q2_0 unpack and linear
+# ---------------------------------------------------------------------------
+
+def unpack_q2_scalar(packed, scale_bits, n: int, k: int):
+    """Literal per-element decode (tiny inputs only): list of rows of floats.
+    q = (byte[k // 4] >> 2 (k % 4)) & 3 ;  w = (q - 1) * d[k // 128]."""
+    w = []
+    for row in range(n):
+        out = []
+        for col in range(k):
+            byte = int(packed[row][col // 4])
+            q = (byte >> (2 * (col % 4))) & 3
+            d = f16_decode_scalar(int(scale_bits[row][col // GROUP]))
+            out.append((q - 1) * d)
+        w.append(out)
+    return w
+
+
+def codes_q2(packed: np.ndarray) -> np.ndarray:
+    """u8 [N, K/4] -> codes u8 [N, K]: column k takes bits 2(k%4).. of byte k//4."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    n, kb = p.shape
+    col = np.arange(kb * 4)
+    return ((p[:, col // 4] >> (2 * (col % 4)).astype(np.uint8)) & 3).astype(np.uint8)
+
+
+def unpack_q2(packed: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Vectorised decode to float64 [N, K]: w[n, k] = (q[n, k] - 1) * d[n, k // 128]."""
+    q = codes_q2(packed).astype(np.float64)
+    d = f16_to_f64(scale_bits)
+    col = np.arange(q.shape[1])
+    w = (q - 1.0) * d[:, col // GROUP]
+    return w + 0.0          # q == 1 with d < 0 gives -0; values compare equal either way
+
+
+def q2_linear(x_bits: np.ndarray, packed: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """y [M, N] = X W^T in float64, X from bf16 bits [M, K]."""
+    x = bf16_to_f64(x_bits)
+    return x @ unpack_q2(packed, scale_bits).T
+
+
+def q2_linear_cols(x_bits, packed, scale_bits, cols) -> np.ndarray:
+    """The columns `cols` of q2_linear, decoding only those weight rows."""
+    cols = np.asarray(cols)
+    return bf16_to_f64(x_bits) @ unpack_q2(packed[cols], scale_bits[cols]).T
+
+
+# ---------------------------------------------------------------------------
+# Low-rank side branch  y = W x + B (A x)
+# ---------------------------------------------------------------------------
+
+def lowrank_t(x_bits: np.ndarray, a_bits: np.ndarray) -> np.ndarray:
+    """t [M, r] = X A^T with A f16 [r, K]."""
+    return bf16_to_f64(x_bits) @ f16_to_f64(a_bits).T
+
+
+def q2_linear_lowrank(x_bits, packed, scale_bits, a_bits, b_bits) -> np.ndarray:
+    """y = X W^T + (X A^T) B^T, A f16 [r, K], B f16 [N, r]; r may be 0."""
+    y = q2_linear(x_bits, packed, scale_bits)
+    a = np.asarray(a_bits)
+    if a.size == 0:
+        return y
+    return y + lowrank_t(x_bits, a) @ f16_to_f64(b_bits).T
+
+
+# ---------------------------------------------------------------------------
+# 4-bit nibble variant
+# ---------------------------------------------------------------------------
+
+def codes_q4(packed4: np.ndarray) -> np.ndarray:
+    """u8 [N, K/2] -> codes [N, K]: column k is (byte[k // 2] >> 4 (k & 1)) & 15,
+    i.e. the low nibble holds the even column."""
+    p = np.ascontiguousarray(packed4, dtype=np.uint8)
+    col = np.arange(p.shape[1] * 2)
+    return ((p[:, col // 2] >> (4 * (col & 1)).astype(np.uint8)) & 15).astype(np.uint8)
+
+
+def unpack_q4(packed4, scale_bits, zero_bits) -> np.ndarray:
+    """w[n, k] = (q[n, k] - z[n, k // 128]) * s[n, k // 128] in float64 (exact)."""
+    q = codes_q4(packed4).astype(np.float64)
+    col = np.arange(q.shape[1])
+    s = f16_to_f64(scale_bits)[:, col // GROUP]
+    z = f16_to_f64(zero_bits)[:, col // GROUP]
+    return (q - z) * s
+
+
+def q4_linear(x_bits, packed4, scale_bits, zero_bits) -> np.ndarray:
+    return bf16_to_f64(x_bits) @ unpack_q4(packed4, scale_bits, zero_bits).T
+
+
+def q4_linear_cols(x_bits, packed4, scale_bits, zero_bits, cols) -> np.ndarray:
+    cols = np.asarray(cols)
+    return bf16_to_f64(x_bits) @ unpack_q4(packed4[cols], scale_bits[cols], zero_bits[cols]).T
+
+
+# ---------------------------------------------------------------------------
+# Exact rational evaluation (brute force for tiny inputs)
+# ---------------------------------------------------------------------------
+
+def exact_linear(x_rows, w_rows):
+    """y[m][n] = sum_k x[m][k] * w[n][k] with Fractions (inputs are floats)."""
+    xs = [[Fraction(v) for v in row] for row in x_rows]
+    ws = [[Fraction(v) for v in row] for row in w_rows]
+    return [[sum((a * b for a, b in zip(xr, wr)), Fraction(0)) for wr in ws] for xr in xs]
+
+
+# ---------------------------------------------------------------------------
+# Acceptance
+# ---------------------------------------------------------------------------
+
+REL_L2_TOL = 1e-4       # over the whole output
+ROW_MAX_TOL = 1e-3      # per output row, relative to the oracle row's RMS
+
+
+def acceptance(y, y_ref) -> dict:
+    """Compare an output against the oracle.
+
+    rel_l2 = ||y - y_ref||_2 / ||y_ref||_2 over the whole tensor;
+    row_ratio = max over rows m of max_n |y - y_ref| / rms_n(y_ref[m, :]).
+    A row of y_ref that is exactly zero must be matched exactly.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    if y.shape != y_ref.shape:
+        raise ValueError(f"shape {y.shape} != {y_ref.shape}")
+    if y_ref.size == 0:
+        return dict(rel_l2=0.0, row_ratio=0.0, ok=True)
+    err = y - y_ref
+    if not np.all(np.isfinite(y)):
+        return dict(rel_l2=math.inf, row_ratio=math.inf, ok=False)
+    ref_norm = float(np.linalg.norm(y_ref))
+    rel_l2 = float(np.linalg.norm(err)) / ref_norm if ref_norm > 0 else (0.0 if not err.any() else math.inf)
+    y2 = y_ref.reshape(y_ref.shape[0], -1) if y_ref.ndim > 1 else y_ref.reshape(1, -1)
+    e2 = np.abs(err).reshape(y2.shape)
+    rms = np.sqrt(np.mean(y2 * y2, axis=1))
+    emax = e2.max(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(rms > 0, emax / np.where(rms > 0, rms, 1.0), np.where(emax > 0, math.inf, 0.0))
+    row_ratio = float(ratio.max())
+    return dict(rel_l2=rel_l2, row_ratio=row_ratio,
+                ok=bool(rel_l2 <= REL_L2_TOL and row_ratio <= ROW_MAX_TOL))

@@ -1,0 +1,95 @@
+"""Seeded synthetic inputs for the Q2_0 ternary linear and its variants.
+
+This module is the only code shared by the CPU oracle's callers and the HIP
+path's callers.  It draws random numbers and stores them in the storage types
+the library consumes (bf16 / f16 bit patterns, u8 codes, u8 nibble bytes); it
+holds none of the method's arithmetic: no packing of 2-bit codes, no
+dequantisation, no matrix products.  It imports NumPy only.
+
+Workload recipe (stated for the synthetic stand-ins of a ~4B MMDiT denoise step
+and a 4-bit text-encoder linear):
+
+* every tensor draws from its own stream ``np.random.default_rng([0, config, tensor])``;
+* Q2_0 codes are i.i.d. over {0, 1, 2} with probabilities {0.3, 0.4, 0.3};
+* Q2_0 block scales are |N(0, 1)| * 0.02, rounded to the nearest f16 value and
+  handed over as float32 (so the pack step's exact-roundtrip check passes);
+* activations are N(0, 1) float32 rounded to bf16 (round to nearest even);
+* low-rank factors A [r, K] and B [N, r] are N(0, std 0.01) rounded to f16;
+* 4-bit weights are uniform random bytes, i.e. two independent codes uniform on
+  0..15 per byte; their group scales are |N(0,1)| * 0.02 and zero points
+  U(0, 15), both rounded to f16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128  # weights per Q2_0 block / per 4-bit group
+
+# tensor ids inside a config's seed tuple
+T_CODES, T_SCALES, T_X, T_A, T_B, T_Q4, T_Q4S, T_Q4Z = range(8)
+
+
+def stream(config_id: int, tensor_id: int, seed: int = 0) -> np.random.Generator:
+    """Independent counter-seeded stream for one tensor of one config."""
+    return np.random.default_rng([seed, config_id, tensor_id])
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round finite float32 values to bf16 (nearest, ties to even); return u16 bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (NumPy's nearest-even cast); u16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def q2_codes(config_id: int, n: int, k: int, p=(0.3, 0.4, 0.3)) -> np.ndarray:
+    """u8 [n, k] codes in {0, 1, 2}."""
+    g = stream(config_id, T_CODES)
+    return g.choice(3, size=(n, k), p=list(p)).astype(np.uint8)
+
+
+def q2_scales(config_id: int, n: int, k: int) -> np.ndarray:
+    """float32 [n, k/128] block scales whose values are exactly representable in f16."""
+    g = stream(config_id, T_SCALES)
+    s = np.abs(g.standard_normal((n, k // GROUP), dtype=np.float32)) * np.float32(0.02)
+    return s.astype(np.float16).astype(np.float32)
+
+
+def activations_bf16(config_id: int, m: int, k: int) -> np.ndarray:
+    """u16 [m, k] bf16 bit patterns of N(0, 1) float32 samples."""
+    g = stream(config_id, T_X)
+    return f32_to_bf16_bits(g.standard_normal((m, k), dtype=np.float32))
+
+
+def lowrank_factors(config_id: int, r: int, k: int, n: int, std: float = 0.01):
+    """(A u16 [r, k], B u16 [n, r]) f16 bit patterns of N(0, std) samples."""
+    a = stream(config_id, T_A).standard_normal((r, k), dtype=np.float32) * np.float32(std)
+    b = stream(config_id, T_B).standard_normal((n, r), dtype=np.float32) * np.float32(std)
+    return f32_to_f16_bits(a), f32_to_f16_bits(b)
+
+
+def q4_weights(config_id: int, n: int, k: int):
+    """(bytes u8 [n, k/2], scale u16 [n, k/128], zero u16 [n, k/128]).
+
+    Bytes are uniform on 0..255, which makes both 4-bit codes of a byte
+    independent and uniform on 0..15 whatever order they are read in.
+    """
+    g = stream(config_id, T_Q4)
+    p4 = g.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    s = np.abs(stream(config_id, T_Q4S).standard_normal((n, k // GROUP), dtype=np.float32))
+    z = stream(config_id, T_Q4Z).uniform(0.0, 15.0, size=(n, k // GROUP)).astype(np.float32)
+    return p4, f32_to_f16_bits(s * np.float32(0.02)), f32_to_f16_bits(z)
+
+
+# The five workload families, with their shapes.
+CONFIG_TINY = dict(id=1, M=4, K=256, N=64)
+GEMV_SHAPES = [(3072, 3072), (3072, 9216), (3072, 12288), (12288, 3072)]   # (K, N), M = 1
+GEMM_M = 1536                                                              # 1024 image + 512 text tokens
+GEMM_SHAPES = [(3072, 3072), (3072, 9216), (3072, 12288), (12288, 3072)]   # (K, N)
+LOWRANK = dict(M=1536, K=3072, N=9216, ranks=(4, 32, 64), linears=100, steps=4)
+Q4_M = 128
+Q4_SHAPES = [(2560, 9728), (9728, 2560), (2560, 2560)]                     # (K, N)

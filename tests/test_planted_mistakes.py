@@ -1,0 +1,88 @@
+"""Each pin must catch a plausible mistake.  The mistakes are planted in copies
+of the oracle's functions, on the CPU; the pins are the check_* functions of
+test_oracle_pins run against those copies."""
+import numpy as np
+import pytest
+
+import oracle.q2_oracle as O
+from tests import test_oracle_pins as P
+
+
+def unpack_msb_first(packed, sc):
+    p = np.asarray(packed)
+    col = np.arange(p.shape[1] * 4)
+    q = (p[:, col // 4] >> (6 - 2 * (col % 4)).astype(np.uint8)) & 3
+    return (q - 1.0) * O.f16_to_f64(sc)[:, col // 128]
+
+
+def unpack_no_offset(packed, sc):            # (q) * d instead of (q - 1) * d
+    return O.unpack_q2(packed, sc) + O.f16_to_f64(sc)[:, np.arange(np.asarray(packed).shape[1] * 4) // 128]
+
+
+def unpack_block64(packed, sc):              # scale index with the wrong block length
+    q = O.codes_q2(packed).astype(np.float64)
+    col = np.arange(q.shape[1])
+    d = O.f16_to_f64(sc)
+    return (q - 1.0) * d[:, np.minimum(col // 64, d.shape[1] - 1)]
+
+
+def linear_with(unpack):
+    return lambda xb, p, s: O.bf16_to_f64(xb) @ unpack(p, s).T
+
+
+def pack_msb_first(codes, scales):
+    p, s = O.pack_q2(codes, scales)
+    c = np.asarray(codes).reshape(codes.shape[0], -1, 4).astype(np.uint32)
+    return (c[..., 3] | c[..., 2] << 2 | c[..., 1] << 4 | c[..., 0] << 6).astype(np.uint8), s
+
+
+def lowrank_b_transposed(xb, p, s, a, b):
+    y = O.q2_linear(xb, p, s)
+    if np.asarray(a).size == 0:
+        return y
+    return y + O.lowrank_t(xb, a) @ O.f16_to_f64(b)
+
+
+def lowrank_dropped_branch(xb, p, s, a, b):
+    return O.q2_linear(xb, p, s)
+
+
+def q4_swapped_nibbles(xb, p4, s, z):
+    p = np.asarray(p4)
+    swapped = ((p >> 4) | (p << 4)).astype(np.uint8)
+    return O.q4_linear(xb, swapped, s, z)
+
+
+def q4_zero_sign(xb, p4, s, z):              # (q + z) * s
+    q = O.codes_q4(p4).astype(np.float64)
+    col = np.arange(q.shape[1])
+    w = (q + O.f16_to_f64(z)[:, col // 128]) * O.f16_to_f64(s)[:, col // 128]
+    return O.bf16_to_f64(xb) @ w.T
+
+
+MUTANTS = {
+    "unpack MSB-first": lambda: P.check_q2_bit_order(O.pack_q2, unpack_msb_first, linear_with(unpack_msb_first)),
+    "pack MSB-first": lambda: P.check_q2_bit_order(pack_msb_first, O.unpack_q2, O.q2_linear),
+    "zero point 0": lambda: P.check_q2_closed_forms(linear_with(unpack_no_offset)),
+    "block length 64": lambda: P.check_q2_closed_forms(linear_with(unpack_block64)),
+    "block length 64 (brute force)": lambda: P.check_q2_exact_bruteforce(linear_with(unpack_block64)),
+    "input axis reversed": lambda: P.check_q2_exact_bruteforce(lambda xb, p, s: O.bf16_to_f64(xb) @ O.unpack_q2(p, s)[:, ::-1].T),
+    "rows and columns swapped": lambda: P.check_q2_exact_bruteforce(lambda xb, p, s: (O.bf16_to_f64(xb) @ O.unpack_q2(p, s).T)[::-1]),
+    "low-rank B transposed": lambda: P.check_lowrank(lowrank_b_transposed),
+    "low-rank branch dropped": lambda: P.check_lowrank(lowrank_dropped_branch),
+    "q4 nibbles swapped": lambda: P.check_q4(q4_swapped_nibbles),
+    "q4 zero sign": lambda: P.check_q4(q4_zero_sign),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pin_catches(name):
+    with pytest.raises(Exception):
+        MUTANTS[name]()
+
+
+def test_unmutated_checks_pass():
+    P.check_q2_bit_order(O.pack_q2, O.unpack_q2, O.q2_linear)
+    P.check_q2_closed_forms(O.q2_linear)
+    P.check_lowrank(O.q2_linear_lowrank)
+    P.check_q4(O.q4_linear)
