@@ -1,0 +1,156 @@
+/*
+ * q2.h - C ABI of libq2: the Q2_0 ternary dequantize-and-multiply linear, its
+ * rank-r side branch and the 4-bit nibble variant, as hand-written HIP kernels
+ * for AMD CDNA4 (gfx950, MI355X).
+ *
+ * Format (We're Teaching Your Browser to Paint, aitherium.com, section "The
+ * lucky break that wasn't luck"): a weight row of K inputs is cut into blocks
+ * of 128; each block has 128 two-bit codes q in {0,1,2} and one f16 scale d;
+ * the weight is (q - 1) * d.  Codes run along the input axis, four per byte,
+ * least significant pair first: code k of a row is bits 2(k%4) and 2(k%4)+1
+ * of byte k/4.  This library stores the codes and the scales as two arrays
+ * (structure of arrays): packed u8 [N, K/4] and scales f16 [N, K/128], both
+ * row-major.  A row is an independent byte run, so a row slice of a weight is
+ * a plain pointer offset (same page, section "The GPU driver...").
+ *
+ * Conventions shared by every entry point:
+ *  - Sizes are int64.  M, N, K, r >= 0; K must be a multiple of 128.  A call
+ *    with M == 0 or N == 0 does nothing and returns Q2_OK; K == 0 writes
+ *    zeros (an empty sum).  Pointers to buffers of zero bytes may be NULL.
+ *  - All array pointers are device pointers; all arrays are dense row-major.
+ *    The caller owns every buffer; the library keeps no state between calls
+ *    except a per-device architecture check, and is safe to call from several
+ *    host threads.
+ *  - x, the packed codes, the q2_pack codes and the low-rank factor A must be
+ *    16-byte aligned; every other array must be aligned to its element size;
+ *    the low-rank workspace to 256 bytes.
+ *  - bf16 activations and f16 scales / factors are passed as their uint16
+ *    bit patterns.  Outputs are float32.
+ *  - Every compute entry point is asynchronous on `stream` (0 = the null
+ *    stream) and returns only argument, device or launch errors.  Arguments
+ *    are checked before any HIP call, so argument errors are reported even on
+ *    a host without a GPU.  q2_pack is the exception: it synchronizes on
+ *    `stream` to report bad codes or scales.
+ *  - Errors are negative q2_status values; nothing is thrown across the ABI.
+ *    q2_strerror() names a status, q2_last_error() gives the calling thread's
+ *    detail message for its most recent failed call.
+ *  - Packed bytes holding the 2-bit value 3 are outside the format: q2_pack
+ *    refuses to produce them, q2_dequant decodes them as (3 - 1) * d, and the
+ *    products of q2_linear / q2_linear_lowrank treat them the same way.
+ */
+#ifndef Q2_H
+#define Q2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  Q2_OK = 0,
+  Q2_ERR_ARG = -1,       /* NULL pointer for a non-empty buffer, negative size      */
+  Q2_ERR_SHAPE = -2,     /* K not a multiple of 128                                 */
+  Q2_ERR_ALIGN = -3,     /* pointer not aligned as stated above                     */
+  Q2_ERR_CODE = -4,      /* q2_pack: a code above 2                                 */
+  Q2_ERR_SCALE = -5,     /* q2_pack: scale not exactly representable in f16, or NaN/inf */
+  Q2_ERR_DEVICE = -6,    /* current device is not gfx950                            */
+  Q2_ERR_HIP = -7,       /* HIP runtime or launch error                             */
+  Q2_ERR_WORKSPACE = -8  /* low-rank workspace too small                            */
+} q2_status;
+
+/*
+ * q2_pack - load-time conversion to the Q2_0 layout.
+ * Source: We're Teaching Your Browser to Paint (aitherium.com), section "The
+ * lucky break that wasn't luck": the conversion changes no value; the only
+ * rounding is the f32 -> f16 scale cast, which must round-trip exactly or the
+ * conversion stops.
+ *   codes      u8  [N, K], each in {0, 1, 2}                    (in)
+ *   scales     f32 [N, K/128]                                   (in)
+ *   packed     u8  [N, K/4]; byte j = c[4j] | c[4j+1]<<2 | c[4j+2]<<4 | c[4j+3]<<6   (out)
+ *   scales_f16 u16 [N, K/128]: f16 bits of scales, nearest-even  (out)
+ *   bad_index  host int64*, may be NULL: on Q2_ERR_CODE / Q2_ERR_SCALE, the
+ *              flat row-major index of the first bad code / scale; -1 on success.
+ * Codes are checked before scales.  Synchronizes `stream`, and allocates and
+ * frees a 16-byte device buffer for the two error flags.  The outputs are
+ * fully written even when an error is returned, but must not be used then.
+ */
+int q2_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K,
+            uint8_t* packed, uint16_t* scales_f16, int64_t* bad_index, hipStream_t stream);
+
+/*
+ * q2_linear - y = x W^T with W[n, k] = (q[n, k] - 1) * d[n, k/128].
+ * Source: We're Teaching Your Browser to Paint, section "The lucky break that
+ * wasn't luck" (format and formula) and section "The GPU driver..." (the
+ * 2-bit matmul is the projection kernel of the image transformer).
+ *   x_bf16     u16 [M, K] bf16 activations                      (in)
+ *   packed     u8  [N, K/4] codes as produced by q2_pack          (in)
+ *   scales_f16 u16 [N, K/128]                                   (in)
+ *   y          f32 [M, N], overwritten                          (out)
+ * Products are exact and accumulate in fp32; every call is run-to-run
+ * bitwise deterministic.  M <= 16 runs a streaming GEMV kernel, larger M a
+ * matrix-core GEMM.  Asynchronous.
+ */
+int q2_linear(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
+              float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * q2_lowrank_workspace_bytes - device bytes q2_linear_lowrank needs for M
+ * rows and rank r: M * r * 4 rounded up to a multiple of 256 (0 when M or r
+ * is 0).  Negative arguments give 0.
+ */
+size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r);
+
+/*
+ * q2_linear_lowrank - y = x W^T + (x A^T) B^T: the Q2_0 linear plus a rank-r
+ * side branch.  Source: mindview-t2i-turbo model card, section "One step"
+ * (the branch y = W x + B (A x) on the transformer's large matrices; ranks
+ * 4, 32 and 64 appear there and in "Two and four steps").
+ *   A_f16      u16 [r, K] f16                                   (in)
+ *   B_f16      u16 [N, r] f16                                   (in)
+ *   r          rank, >= 0; r == 0 is exactly q2_linear
+ *   workspace  device scratch of >= q2_lowrank_workspace_bytes(M, r) bytes,
+ *              256-byte aligned, owned by the caller; overwritten.
+ * x A^T is computed once per call (into the workspace) and B (x A^T) is
+ * added inside the epilogue of the Q2_0 kernel.  Asynchronous; calls that
+ * share a workspace must be ordered on one stream.
+ */
+int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
+                      const uint16_t* A_f16, const uint16_t* B_f16, int64_t r,
+                      float* y, int64_t M, int64_t N, int64_t K,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * q4_linear - 4-bit variant: y = x W^T with W[n, k] = (q[n, k] - z[n, k/128]) * s[n, k/128],
+ * q[n, k] = (packed4[n, k/2] >> (4 * (k & 1))) & 15 (the low nibble holds the even k).
+ * Source: You Can Now Just Ask for an Image (aitherium.com), section "The bug
+ * that hid in one flipped bit" (nibble order), and We're Teaching Your
+ * Browser to Paint, section "What's left" ((q - zero) * scale).  The group
+ * length 128 and the f16 zero point in code units are this library's reading.
+ *   packed4    u8  [N, K/2]  (in);  scale_f16, zero_f16  u16 [N, K/128]  (in)
+ *   y          f32 [M, N]    (out).   Asynchronous.
+ */
+int q4_linear(const uint16_t* x_bf16, const uint8_t* packed4, const uint16_t* scale_f16,
+              const uint16_t* zero_f16, float* y, int64_t M, int64_t N, int64_t K,
+              hipStream_t stream);
+
+/*
+ * q2_dequant - test export: w[n, k] = (q - 1) * d as float32 [N, K], exact;
+ * a zero weight is written as +0.  Same layout rules as q2_linear.  Asynchronous.
+ */
+int q2_dequant(const uint8_t* packed, const uint16_t* scales_f16, float* w,
+               int64_t N, int64_t K, hipStream_t stream);
+
+/* q2_strerror - static name of a status code; never NULL. */
+const char* q2_strerror(int status);
+
+/* q2_last_error - the calling thread's detail message for its last failed call
+ * ("" if none).  Valid until that thread's next call into the library. */
+const char* q2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q2_H */

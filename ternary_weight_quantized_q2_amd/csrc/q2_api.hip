@@ -1,0 +1,227 @@
+// q2_api.hip - the C ABI of libq2: argument validation, device check, dispatch.
+// Every argument check runs before the first HIP call, so a host without a GPU
+// still gets argument, shape and alignment errors.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "q2.h"
+#include "q2_internal.h"
+
+namespace {
+
+thread_local char g_detail[320];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_detail[0] = '\0';
+  return Q2_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// pointer must be non-NULL when the buffer is non-empty, and aligned
+int check_ptr(const void* p, bool nonempty, size_t align, const char* name) {
+  if (nonempty && p == nullptr) return fail(Q2_ERR_ARG, "%s is NULL for a non-empty buffer", name);
+  if (p != nullptr && !aligned(p, align)) return fail(Q2_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return Q2_OK;
+}
+
+int check_sizes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return fail(Q2_ERR_ARG, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
+                                           (long long)N, (long long)K);
+  if (K % 128 != 0) return fail(Q2_ERR_SHAPE, "K=%lld is not a multiple of 128", (long long)K);
+  // keep every element index inside int64 with room to spare
+  const int64_t lim = (int64_t)1 << 46;
+  if (M > lim || N > lim || K > lim || (M > 0 && K > lim / M) || (N > 0 && K > lim / N) ||
+      (M > 0 && N > lim / M))
+    return fail(Q2_ERR_ARG, "sizes too large");
+  return Q2_OK;
+}
+
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(Q2_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  const int slot = (dev >= 0 && dev < 64) ? dev : -1;
+  if (slot >= 0) {
+    const int st = g_arch_ok[slot].load(std::memory_order_relaxed);
+    if (st == 1) return Q2_OK;
+    if (st == -1) return fail(Q2_ERR_DEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(Q2_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (slot >= 0) g_arch_ok[slot].store(good ? 1 : -1, std::memory_order_relaxed);
+  if (!good) return fail(Q2_ERR_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return Q2_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(Q2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Test-only override of the M <= 16 dispatch: Q2_FORCE_PATH=gemv|gemm.
+int forced_path() {
+  const char* v = std::getenv("Q2_FORCE_PATH");
+  if (v == nullptr) return 0;
+  if (std::strcmp(v, "gemv") == 0) return 1;
+  if (std::strcmp(v, "gemm") == 0) return 2;
+  return 0;
+}
+
+int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* s, const uint16_t* z, float* y,
+                  int64_t M, int64_t N, int64_t K, const uint16_t* lr_t, const uint16_t* lr_b, int64_t r,
+                  hipStream_t stream) {
+  q2dev::LinearArgs a;
+  a.x = x; a.w = w; a.s = s; a.z = z; a.y = y;
+  a.M = M; a.N = N; a.K = K;
+  a.lr_t = lr_t; a.lr_b = lr_b; a.r = (int)r;
+  int path = forced_path();
+  if (path == 1 && M > 16) path = 0;
+  return hip_status(q2dev::launch_linear(a, fmt, path, stream), fmt == 0 ? "q2 linear launch" : "q4 linear launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* q2_strerror(int status) {
+  switch (status) {
+    case Q2_OK: return "Q2_OK";
+    case Q2_ERR_ARG: return "Q2_ERR_ARG: invalid argument";
+    case Q2_ERR_SHAPE: return "Q2_ERR_SHAPE: K must be a multiple of 128";
+    case Q2_ERR_ALIGN: return "Q2_ERR_ALIGN: misaligned pointer";
+    case Q2_ERR_CODE: return "Q2_ERR_CODE: code outside {0,1,2}";
+    case Q2_ERR_SCALE: return "Q2_ERR_SCALE: scale not exactly representable in f16";
+    case Q2_ERR_DEVICE: return "Q2_ERR_DEVICE: current device is not gfx950";
+    case Q2_ERR_HIP: return "Q2_ERR_HIP: HIP runtime error";
+    case Q2_ERR_WORKSPACE: return "Q2_ERR_WORKSPACE: workspace too small or misaligned";
+    default: return "unknown q2 status";
+  }
+}
+
+const char* q2_last_error(void) { return g_detail; }
+
+size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r) {
+  if (M <= 0 || r <= 0) return 0;
+  const size_t b = (size_t)M * (size_t)r * 4u;
+  return (b + 255u) & ~(size_t)255u;
+}
+
+int q2_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K, uint8_t* packed,
+            uint16_t* scales_f16, int64_t* bad_index, hipStream_t stream) {
+  if (bad_index) *bad_index = -1;
+  int st = check_sizes(0, N, K);
+  if (st) return st;
+  const bool ne = N > 0 && K > 0;
+  if ((st = check_ptr(codes, ne, 16, "codes")) || (st = check_ptr(scales, ne, 4, "scales")) ||
+      (st = check_ptr(packed, ne, 16, "packed")) || (st = check_ptr(scales_f16, ne, 2, "scales_f16")))
+    return st;
+  if (!ne) return ok();
+  if ((st = check_device())) return st;
+
+  unsigned long long* flags = nullptr;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&flags), 2 * sizeof(unsigned long long));
+  if (e != hipSuccess) return hip_status(e, "hipMalloc(pack flags)");
+  unsigned long long host[2] = {~0ull, ~0ull};
+  e = hipMemsetAsync(flags, 0xFF, sizeof host, stream);
+  if (e == hipSuccess) e = q2dev::launch_pack(codes, scales, N, K, packed, scales_f16, flags, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(host, flags, sizeof host, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  hipError_t ef = hipFree(flags);
+  if (e != hipSuccess) return hip_status(e, "q2_pack");
+  if (ef != hipSuccess) return hip_status(ef, "hipFree(pack flags)");
+  if (host[0] != ~0ull) {
+    if (bad_index) *bad_index = (int64_t)host[0];
+    return fail(Q2_ERR_CODE, "code above 2 at flat index %llu", host[0]);
+  }
+  if (host[1] != ~0ull) {
+    if (bad_index) *bad_index = (int64_t)host[1];
+    return fail(Q2_ERR_SCALE, "scale at flat index %llu is not an exact f16 value", host[1]);
+  }
+  return ok();
+}
+
+int q2_linear(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16, float* y, int64_t M,
+              int64_t N, int64_t K, hipStream_t stream) {
+  int st = check_sizes(M, N, K);
+  if (st) return st;
+  if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
+      (st = check_ptr(packed, N > 0 && K > 0, 16, "packed")) ||
+      (st = check_ptr(scales_f16, N > 0 && K > 0, 2, "scales_f16")) ||
+      (st = check_ptr(y, M > 0 && N > 0, 4, "y")))
+    return st;
+  if (M == 0 || N == 0) return ok();
+  if ((st = check_device())) return st;
+  return linear_common(0, x_bf16, packed, scales_f16, nullptr, y, M, N, K, nullptr, nullptr, 0, stream);
+}
+
+int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
+                      const uint16_t* A_f16, const uint16_t* B_f16, int64_t r, float* y, int64_t M, int64_t N,
+                      int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_sizes(M, N, K);
+  if (st) return st;
+  if (r < 0) return fail(Q2_ERR_ARG, "negative rank r=%lld", (long long)r);
+  if (r > (1 << 20)) return fail(Q2_ERR_ARG, "rank r=%lld too large", (long long)r);
+  if (r == 0) return q2_linear(x_bf16, packed, scales_f16, y, M, N, K, stream);
+  if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
+      (st = check_ptr(packed, N > 0 && K > 0, 16, "packed")) ||
+      (st = check_ptr(scales_f16, N > 0 && K > 0, 2, "scales_f16")) ||
+      (st = check_ptr(A_f16, K > 0, 16, "A")) || (st = check_ptr(B_f16, N > 0, 2, "B")) ||
+      (st = check_ptr(y, M > 0 && N > 0, 4, "y")))
+    return st;
+  if (M == 0 || N == 0) return ok();
+  const size_t need = q2_lowrank_workspace_bytes(M, r);
+  if (workspace_bytes < need)
+    return fail(Q2_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (workspace == nullptr) return fail(Q2_ERR_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(Q2_ERR_ALIGN, "workspace is not 256-byte aligned");
+  if ((st = check_device())) return st;
+  uint16_t* tl = static_cast<uint16_t*>(workspace);
+  if ((st = hip_status(q2dev::launch_lowrank_t(x_bf16, A_f16, tl, M, K, (int)r, stream), "low-rank x A^T launch")))
+    return st;
+  return linear_common(0, x_bf16, packed, scales_f16, nullptr, y, M, N, K, tl, B_f16, r, stream);
+}
+
+int q4_linear(const uint16_t* x_bf16, const uint8_t* packed4, const uint16_t* scale_f16, const uint16_t* zero_f16,
+              float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  int st = check_sizes(M, N, K);
+  if (st) return st;
+  if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
+      (st = check_ptr(packed4, N > 0 && K > 0, 16, "packed4")) ||
+      (st = check_ptr(scale_f16, N > 0 && K > 0, 2, "scale_f16")) ||
+      (st = check_ptr(zero_f16, N > 0 && K > 0, 2, "zero_f16")) || (st = check_ptr(y, M > 0 && N > 0, 4, "y")))
+    return st;
+  if (M == 0 || N == 0) return ok();
+  if ((st = check_device())) return st;
+  return linear_common(1, x_bf16, packed4, scale_f16, zero_f16, y, M, N, K, nullptr, nullptr, 0, stream);
+}
+
+int q2_dequant(const uint8_t* packed, const uint16_t* scales_f16, float* w, int64_t N, int64_t K,
+               hipStream_t stream) {
+  int st = check_sizes(0, N, K);
+  if (st) return st;
+  const bool ne = N > 0 && K > 0;
+  if ((st = check_ptr(packed, ne, 16, "packed")) || (st = check_ptr(scales_f16, ne, 2, "scales_f16")) ||
+      (st = check_ptr(w, ne, 4, "w")))
+    return st;
+  if (!ne) return ok();
+  if ((st = check_device())) return st;
+  return hip_status(q2dev::launch_dequant(packed, scales_f16, w, N, K, stream), "dequant launch");
+}
+
+}  // extern "C"

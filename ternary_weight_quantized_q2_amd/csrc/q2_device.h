@@ -1,0 +1,125 @@
+// q2_device.h - device-side building blocks shared by the gfx950 kernels.
+//
+// Matrix-core layout used everywhere (v_mfma_f32_16x16x32_bf16, wave64):
+//   lane l, column c = l % 16, lane group g = l / 16.
+//   A operand: 8 bf16 of row c;  B operand: 8 bf16 of column c;  both hold the
+//   K-slots 8g .. 8g+7 of the instruction's 32-wide K window, so a dot product
+//   is correct whenever A and B put the same real k in the same (g, element).
+//   C/D: 4 fp32 of column c, rows 4g + 0..3.
+//
+// Weight decoding by a floating-point "magic number": a 2-bit or 4-bit code q
+// is OR-ed into the fraction bits of bf16 1.0, which gives the exact bf16
+// value 1 + q/4 (2-bit code in fraction bits 5-6) or 1 + q/16 (4-bit code in
+// fraction bits 3-6).  One shift and one and-or build two bf16 weights (the
+// two 16-bit halves of a dword), so the decode costs about one VALU op per
+// weight.  The constant 1 is removed through the accumulator: per 128-block
+// the MFMA accumulator starts at -1.25 * sum(x) (2-bit) so that it ends at
+// sum x (q - 1) / 4 exactly in real arithmetic; the 4-bit path starts it at
+// -(1 + z/16) * sum(x) and ends at sum x (q - z) / 16.
+//
+// Because a dword's two halves are 16 bits apart, a 2-bit pair holds codes
+// (j, j+8) of the dword's 16 codes and a 4-bit pair holds codes (j, j+4) of
+// its 8 codes.  The activations are stored in shared memory in the same pair
+// order, built once per block by the staging threads.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 q2_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 q2_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float q2_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t q2_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t q2_u32x2 __attribute__((ext_vector_type(2)));
+
+namespace q2dev {
+
+constexpr int WAVE = 64;
+constexpr int BLOCK_K = 128;          // weights per Q2_0 block / 4-bit group
+
+__device__ __forceinline__ q2_f32x4 mfma(q2_u32x4 a, q2_u32x4 b, q2_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(q2_bf16x8, a),
+                                                  __builtin_bit_cast(q2_bf16x8, b), c, 0, 0, 0);
+}
+
+// ---- 2-bit codes -----------------------------------------------------------
+// Pair J (0..7) of dword w: halves = bf16(1 + c_J/4), bf16(1 + c_{J+8}/4).
+template <int J>
+__device__ __forceinline__ uint32_t q2_pair(uint32_t w) {
+  const uint32_t s = (J <= 2) ? (w << (5 - 2 * J)) : (w >> (2 * J - 5));
+  return (s & 0x00600060u) | 0x3F803F80u;
+}
+// B operand for half H (0/1) of a codes dword: pairs 4H .. 4H+3.
+template <int H>
+__device__ __forceinline__ q2_u32x4 q2_bfrag(uint32_t w) {
+  return q2_u32x4{q2_pair<4 * H>(w), q2_pair<4 * H + 1>(w), q2_pair<4 * H + 2>(w), q2_pair<4 * H + 3>(w)};
+}
+
+// ---- 4-bit codes -----------------------------------------------------------
+// Pair J (0..3) of dword w (8 nibbles): halves = bf16(1 + q_J/16), bf16(1 + q_{J+4}/16).
+template <int J>
+__device__ __forceinline__ uint32_t q4_pair(uint32_t w) {
+  const uint32_t s = (J == 0) ? (w << 3) : (w >> (4 * J - 3));
+  return (s & 0x00780078u) | 0x3F803F80u;
+}
+__device__ __forceinline__ q2_u32x4 q4_bfrag(uint32_t w) {
+  return q2_u32x4{q4_pair<0>(w), q4_pair<1>(w), q4_pair<2>(w), q4_pair<3>(w)};
+}
+
+// ---- activation pair order -------------------------------------------------
+// nx[h] = (x[2h], x[2h+1]) for 16 consecutive x.  2-bit order: out[j] =
+// (x[j], x[j+8]) for j = 0..7.
+__device__ __forceinline__ void q2_xpairs(const uint32_t nx[8], uint32_t out[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t a = nx[j >> 1], b = nx[4 + (j >> 1)];
+    out[j] = (j & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+  }
+}
+// 4-bit order, two groups of 8 x: out[4i + j] = (x[8i + j], x[8i + j + 4]).
+__device__ __forceinline__ void q4_xpairs(const uint32_t nx[8], uint32_t out[8]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t a = nx[4 * i + (j >> 1)], b = nx[4 * i + 2 + (j >> 1)];
+      out[4 * i + j] = (j & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+    }
+  }
+}
+
+// Sum of 16 bf16 (8 dwords) in fp32, fixed order.
+__device__ __forceinline__ float bf16_sum16(const uint32_t nx[8]) {
+  const q2_bf16x2 one = __builtin_bit_cast(q2_bf16x2, 0x3F803F80u);
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int h = 0; h < 8; h += 2) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(q2_bf16x2, nx[h]), one, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(q2_bf16x2, nx[h + 1]), one, s1, false);
+  }
+  return s0 + s1;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Exact split of an f16 value into bf16 hi + lo (8 + at most 3 significant bits).
+__device__ __forceinline__ void f16_split_bf16(uint16_t h, uint16_t& hi, uint16_t& lo) {
+  const float f = f16_to_f32(h);
+  const uint32_t fb = __builtin_bit_cast(uint32_t, f);
+  const float fh = __builtin_bit_cast(float, fb & 0xFFFF0000u);
+  hi = (uint16_t)(fb >> 16);
+  lo = (uint16_t)(__builtin_bit_cast(uint32_t, f - fh) >> 16);
+}
+
+// Round fp32 to bf16 (nearest even; finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rn(float f) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, f);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+}  // namespace q2dev

@@ -1,0 +1,34 @@
+// q2_internal.h - host-side launchers shared between the C ABI and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q2dev {
+
+// One linear call: x [M, K] bf16, weights in format fmt (0 = Q2_0, 1 = 4-bit),
+// y [M, N] fp32.  lr_t / lr_b / r describe an optional low-rank term added
+// in the epilogue (lr_t = bf16 limbs [M, 2r] of x A^T, lr_b = B f16 [N, r]).
+struct LinearArgs {
+  const uint16_t* x;
+  const uint8_t* w;
+  const uint16_t* s;     // f16 scale per (row, block)
+  const uint16_t* z;     // f16 zero point per (row, block), 4-bit only
+  float* y;
+  int64_t M, N, K;
+  const uint16_t* lr_t;
+  const uint16_t* lr_b;
+  int r;
+};
+
+// Path selection for tests: 0 = automatic, 1 = force GEMV, 2 = force GEMM.
+hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, hipStream_t stream);
+hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* t_limbs,
+                            int64_t M, int64_t K, int r, hipStream_t stream);
+hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K,
+                       uint8_t* packed, uint16_t* scales_f16, unsigned long long* flags,
+                       hipStream_t stream);
+hipError_t launch_dequant(const uint8_t* packed, const uint16_t* scales, float* w,
+                          int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_zero_fill(float* y, int64_t count, hipStream_t stream);
+
+}  // namespace q2dev

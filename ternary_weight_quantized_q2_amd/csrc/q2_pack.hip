@@ -1,0 +1,102 @@
+// q2_pack.hip - load-time Q2_0 packing with validation, and the exact decode
+// used by tests.
+//
+// Packing follows the Q2_0 layout of "We're Teaching Your Browser to Paint"
+// (aitherium.com), section "The lucky break that wasn't luck": four 2-bit
+// codes per byte along the input axis, the first code in the two least
+// significant bits; one f16 scale per 128 weights.  The only rounding allowed
+// is the f32 -> f16 scale cast and it must round-trip exactly.  Bad inputs are
+// reported through two 64-bit device flags that hold the smallest offending
+// flat index (atomicMin, so the reported index is independent of scheduling).
+#include "q2_device.h"
+#include "q2_internal.h"
+
+namespace q2dev {
+
+// One thread per 16 codes (16 bytes in, one packed dword out).
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* codes, uint32_t* packed, int64_t n16,
+                                                         unsigned long long* flags) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const q2_u32x4 v = reinterpret_cast<const q2_u32x4*>(codes)[i];
+    uint32_t out = 0;
+    int first_bad = -1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t code = (v[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      if (code > 2u && first_bad < 0) first_bad = k;
+      out |= (code & 3u) << (2 * k);
+    }
+    packed[i] = out;
+    if (first_bad >= 0) atomicMin(&flags[0], (unsigned long long)(16 * i + first_bad));
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_scales_kernel(const float* s, uint16_t* sh, int64_t count,
+                                                          unsigned long long* flags) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const float f = s[i];
+    const _Float16 h = (_Float16)f;                 // round to nearest even
+    sh[i] = __builtin_bit_cast(uint16_t, h);
+    const bool finite = __builtin_isfinite(f);
+    if (!finite || (float)h != f) atomicMin(&flags[1], (unsigned long long)i);
+  }
+}
+
+// One thread per 16 weights.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* packed, const uint16_t* s, float* w,
+                                                     int64_t N, int64_t K) {
+  const int64_t per_row = K / 16;
+  const int64_t total = N * per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t row = i / per_row;
+    const int64_t k0 = (i - row * per_row) * 16;
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(packed + row * (K / 4) + k0 / 4);
+    const float d = f16_to_f32(s[row * (K / BLOCK_K) + k0 / BLOCK_K]);
+    float* out = w + row * K + k0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int q = (int)((word >> (2 * k)) & 3u);
+      out[k] = (q == 1) ? 0.0f : (float)(q - 1) * d;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(float* y, int64_t count) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0.0f;
+}
+
+static unsigned grid_for(int64_t work) {
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  return (unsigned)blocks;
+}
+
+hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K, uint8_t* packed,
+                       uint16_t* scales_f16, unsigned long long* flags, hipStream_t stream) {
+  const int64_t n16 = N * K / 16;
+  const int64_t ns = N * (K / BLOCK_K);
+  hipLaunchKernelGGL(pack_codes_kernel, dim3(grid_for(n16)), dim3(256), 0, stream, codes,
+                     reinterpret_cast<uint32_t*>(packed), n16, flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(ns)), dim3(256), 0, stream, scales, scales_f16, ns, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* packed, const uint16_t* scales, float* w, int64_t N, int64_t K,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL(dequant_kernel, dim3(grid_for(N * K / 16)), dim3(256), 0, stream, packed, scales, w, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_fill(float* y, int64_t count, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(grid_for(count)), dim3(256), 0, stream, y, count);
+  return hipGetLastError();
+}
+
+}  // namespace q2dev

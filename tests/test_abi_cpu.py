@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/q2.h declares, and rejects bad arguments before any HIP
+call.  No compute entry point is driven past its argument checks here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_quantized_q2_amd as q2
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "q2.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(q[24]_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q2.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    assert header_functions() == sorted(q2.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_workspace_size(lib):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        assert lib.q2_strerror(st)
+    assert b"unknown" in lib.q2_strerror(-99)
+    assert lib.q2_lowrank_workspace_bytes(0, 32) == 0
+    assert lib.q2_lowrank_workspace_bytes(1536, 0) == 0
+    assert lib.q2_lowrank_workspace_bytes(-1, 5) == 0
+    assert lib.q2_lowrank_workspace_bytes(1, 4) == 256
+    assert lib.q2_lowrank_workspace_bytes(1536, 64) == 1536 * 64 * 4
+    assert lib.q2_lowrank_workspace_bytes(3, 5) == 256
+
+
+FAKE = 1 << 20          # 16-byte aligned fake device address (never dereferenced)
+
+
+def test_linear_argument_errors(lib):
+    L = lib.q2_linear
+    assert L(FAKE, FAKE, FAKE, FAKE, -1, 8, 128, None) == q2.Q2_ERR_ARG
+    assert L(FAKE, FAKE, FAKE, FAKE, 4, 8, 100, None) == q2.Q2_ERR_SHAPE
+    assert L(None, FAKE, FAKE, FAKE, 4, 8, 128, None) == q2.Q2_ERR_ARG
+    assert L(FAKE, None, FAKE, FAKE, 4, 8, 128, None) == q2.Q2_ERR_ARG
+    assert L(FAKE, FAKE, FAKE, None, 4, 8, 128, None) == q2.Q2_ERR_ARG
+    assert L(FAKE + 8, FAKE, FAKE, FAKE, 4, 8, 128, None) == q2.Q2_ERR_ALIGN
+    assert L(FAKE, FAKE + 4, FAKE, FAKE, 4, 8, 128, None) == q2.Q2_ERR_ALIGN
+    assert L(FAKE, FAKE, FAKE + 1, FAKE, 4, 8, 128, None) == q2.Q2_ERR_ALIGN
+    assert L(FAKE, FAKE, FAKE, FAKE + 2, 4, 8, 128, None) == q2.Q2_ERR_ALIGN
+    assert L(FAKE, FAKE, FAKE, FAKE, 4, 8, 100, None) == q2.Q2_ERR_SHAPE and b"K=100" in lib.q2_last_error()
+    # empty problems are valid no-ops that touch nothing, NULL pointers allowed
+    assert L(None, FAKE, FAKE, None, 0, 8, 128, None) == q2.Q2_OK
+    assert L(FAKE, None, None, None, 4, 0, 128, None) == q2.Q2_OK
+    assert L(None, None, None, None, 0, 0, 0, None) == q2.Q2_OK
+    assert L(None, FAKE, FAKE, None, 0, 8, 128, None) == q2.Q2_OK
+    assert lib.q4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 5, 64, None) == q2.Q2_ERR_SHAPE
+    assert lib.q4_linear(FAKE, FAKE, FAKE, None, FAKE, 3, 5, 128, None) == q2.Q2_ERR_ARG
+    assert lib.q2_dequant(FAKE, FAKE, FAKE, 4, 130, None) == q2.Q2_ERR_SHAPE
+    assert lib.q2_dequant(None, None, None, 0, 128, None) == q2.Q2_OK
+
+
+def test_lowrank_argument_errors(lib):
+    LR = lib.q2_linear_lowrank
+    need = lib.q2_lowrank_workspace_bytes(16, 8)
+    assert LR(FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 16, 8, 128, FAKE, need, None) == q2.Q2_ERR_ARG
+    assert LR(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 16, 8, 128, FAKE, need - 1, None) == q2.Q2_ERR_WORKSPACE
+    assert LR(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 16, 8, 128, FAKE + 16, need, None) == q2.Q2_ERR_ALIGN
+    assert LR(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 16, 8, 128, None, need, None) == q2.Q2_ERR_ARG
+    assert LR(FAKE, FAKE, FAKE, FAKE + 2, FAKE, 8, FAKE, 16, 8, 128, FAKE, need, None) == q2.Q2_ERR_ALIGN
+    assert LR(FAKE, FAKE, FAKE, None, FAKE, 8, FAKE, 16, 8, 128, FAKE, need, None) == q2.Q2_ERR_ARG
+    assert LR(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 16, 8, 96, FAKE, need, None) == q2.Q2_ERR_SHAPE
+
+
+def test_pack_argument_errors(lib):
+    bad = ctypes.c_int64(123)
+    P = lib.q2_pack
+    assert P(FAKE, FAKE, 4, 100, FAKE, FAKE, ctypes.byref(bad), None) == q2.Q2_ERR_SHAPE
+    assert bad.value == -1
+    assert P(FAKE + 4, FAKE, 4, 128, FAKE, FAKE, None, None) == q2.Q2_ERR_ALIGN
+    assert P(FAKE, None, 4, 128, FAKE, FAKE, None, None) == q2.Q2_ERR_ARG
+    assert P(None, None, 0, 128, None, None, None, None) == q2.Q2_OK
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "ternary_weight_quantized_q2_amd")
+    pat = re.compile(r"^\s*(import\s+oracle|from\s+oracle)|q2_oracle|oracle[/.]", re.M)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                assert not pat.search(open(os.path.join(dirpath, f)).read()), f
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    saved = q2._lib
+    q2._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            q2.load(str(tmp_path / "missing.so"))
+    finally:
+        q2._lib = saved

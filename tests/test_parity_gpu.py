@@ -1,0 +1,318 @@
+"""GPU parity: the HIP library (called through its C ABI via the binding)
+against the CPU oracle on the same seeded inputs.
+
+Bars: packed bytes, scale bits and dequantised weights bit-exact; outputs
+within relative L2 <= 1e-4 over the tensor and, per row, max |err| <= 1e-3 of
+the oracle row's RMS.  Where the oracle computes only sampled columns of a
+full-size output, the row RMS is taken over those columns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.q2_oracle as O
+import ternary_weight_quantized_q2_amd as q2
+from ternary_weight_quantized_q2_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU; they must not be skipped silently"
+    torch.cuda.set_device(0)
+    q2.load()
+    yield
+
+
+DEV = "cuda:0"
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(DEV)
+
+
+def dev_bits(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(DEV).view(dtype)
+
+
+def host_bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def q2_weights(cfg, n, k):
+    """GPU-packed and oracle-packed copies of the same seeded Q2_0 weight."""
+    codes = I.q2_codes(cfg, n, k)
+    scales = I.q2_scales(cfg, n, k)
+    p_dev, s_dev = q2.q2_pack(dev_u8(codes), torch.from_numpy(scales).to(DEV))
+    p_ref, s_ref = O.pack_q2(codes, scales)
+    return p_dev, s_dev, p_ref, s_ref
+
+
+def acts(cfg, m, k):
+    xb = I.activations_bf16(cfg, m, k)
+    return xb, dev_bits(xb, torch.bfloat16)
+
+
+def assert_close(y, ref, what=""):
+    r = O.acceptance(np.asarray(y, np.float64), ref)
+    assert r["ok"], f"{what}: rel_l2={r['rel_l2']:.3e} row_ratio={r['row_ratio']:.3e}"
+    return r
+
+
+def sample_cols(n, count=128, seed=0):
+    rng = np.random.default_rng(seed)
+    cols = np.concatenate([[0, n - 1], rng.choice(n, min(count, n), replace=False)])
+    return np.unique(cols)
+
+
+@pytest.fixture
+def path(request, monkeypatch):
+    p = request.param
+    if p != "auto":
+        monkeypatch.setenv("Q2_FORCE_PATH", p)
+    else:
+        monkeypatch.delenv("Q2_FORCE_PATH", raising=False)
+    return p
+
+
+# ---------------------------------------------------------------------------
+# pack / dequant
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(64, 256), (1000, 1280), (9216, 3072)])
+def test_pack_bitexact(n, k):
+    p_dev, s_dev, p_ref, s_ref = q2_weights(11, n, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(p_dev.cpu().numpy(), p_ref)
+    assert np.array_equal(host_bits(s_dev), s_ref)
+
+
+def test_pack_errors_report_first_index():
+    n, k = 6, 384
+    codes = np.ones((n, k), np.uint8)
+    scales = np.full((n, k // 128), 0.5, np.float32)
+    codes[5, 200] = 3
+    codes[4, 7] = 9
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_pack(dev_u8(codes), torch.from_numpy(scales).to(DEV))
+    assert e.value.status == q2.Q2_ERR_CODE and e.value.bad_index == 4 * k + 7
+    codes[:] = 2
+    scales[2, 1] = 1.000244140625          # not an f16 value
+    scales[3, 0] = np.nan
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_pack(dev_u8(codes), torch.from_numpy(scales).to(DEV))
+    assert e.value.status == q2.Q2_ERR_SCALE and e.value.bad_index == 2 * 3 + 1
+    scales[2, 1] = 0.5
+    scales[3, 0] = 65520.0                  # rounds to infinity in f16
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_pack(dev_u8(codes), torch.from_numpy(scales).to(DEV))
+    assert e.value.status == q2.Q2_ERR_SCALE and e.value.bad_index == 9
+    scales[3, 0] = 2.0 ** -24               # smallest f16 subnormal is accepted
+    q2.q2_pack(dev_u8(codes), torch.from_numpy(scales).to(DEV))
+
+
+def test_dequant_exact():
+    n, k = 300, 640
+    codes = I.q2_codes(12, n, k)
+    codes[0, :8] = 3                        # outside the format, decoded by the same formula
+    scales = I.q2_scales(12, n, k) * np.where(np.arange(n)[:, None] % 2, -1, 1).astype(np.float32)
+    c = codes.reshape(n, k // 4, 4).astype(np.uint32)
+    packed = (c[..., 0] | c[..., 1] << 2 | c[..., 2] << 4 | c[..., 3] << 6).astype(np.uint8)
+    sc16 = I.f32_to_f16_bits(scales)
+    w = q2.q2_dequant(dev_u8(packed), dev_bits(sc16, torch.float16)).cpu().numpy()
+    ref = O.unpack_q2(packed, sc16)
+    assert np.array_equal(w.astype(np.float64), ref)
+    assert not np.any(np.signbit(w[w == 0]))   # zero weights are +0
+
+
+# ---------------------------------------------------------------------------
+# Q2_0 linear
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["auto", "gemv", "gemm"], indirect=True)
+def test_linear_tiny_config(path):
+    c = I.CONFIG_TINY
+    p_dev, s_dev, p_ref, s_ref = q2_weights(c["id"], c["N"], c["K"])
+    xb, x = acts(c["id"], c["M"], c["K"])
+    y = q2.q2_linear(x, p_dev, s_dev).cpu().numpy()
+    assert_close(y, O.q2_linear(xb, p_ref, s_ref), f"tiny {path}")
+
+
+@pytest.mark.parametrize("path,m", [("gemv", 16), ("gemm", 16), ("auto", 256), ("gemm", 1)], indirect=["path"])
+def test_linear_identity_is_exact(path, m):
+    k, n = 256, 200
+    p_dev, s_dev, p_ref, s_ref = q2_weights(13, n, k)
+    eye = np.zeros((m, k), np.float32)
+    eye[np.arange(m), np.arange(m)] = 1.0
+    y = q2.q2_linear(dev_bits(I.f32_to_bf16_bits(eye), torch.bfloat16), p_dev, s_dev).cpu().numpy()
+    w = O.unpack_q2(p_ref, s_ref)
+    assert np.array_equal(y.astype(np.float64), w[:, :m].T)
+
+
+SHAPES = [(1, 1, 128), (1, 17, 384), (3, 130, 1280), (7, 1000, 256), (16, 257, 512), (17, 65, 640),
+          (33, 200, 128), (100, 333, 384), (257, 190, 1024), (96, 192, 3072), (300, 450, 2048)]
+
+
+@pytest.mark.parametrize("path", ["auto", "gemm"], indirect=True)
+@pytest.mark.parametrize("m,n,k", SHAPES)
+def test_linear_ragged(path, m, n, k):
+    p_dev, s_dev, p_ref, s_ref = q2_weights(14, n, k)
+    xb, x = acts(14, m, k)
+    y = q2.q2_linear(x, p_dev, s_dev).cpu().numpy()
+    assert_close(y, O.q2_linear(xb, p_ref, s_ref), f"{path} M={m} N={n} K={k}")
+
+
+def test_linear_empty_and_k_zero():
+    n = 40
+    x = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
+    p = torch.empty((n, 0), dtype=torch.uint8, device=DEV)
+    s = torch.empty((n, 0), dtype=torch.float16, device=DEV)
+    y = torch.full((5, n), float("nan"), device=DEV)
+    q2.q2_linear(x, p, s, y)
+    assert torch.all(y == 0)
+    y17 = torch.full((17, n), float("nan"), device=DEV)
+    q2.q2_linear(torch.empty((17, 0), dtype=torch.bfloat16, device=DEV), p, s, y17)
+    assert torch.all(y17 == 0)
+    p_dev, s_dev, _, _ = q2_weights(15, n, 256)
+    y0 = q2.q2_linear(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV), p_dev, s_dev)
+    assert y0.shape == (0, n)
+
+
+@pytest.mark.parametrize("k,n", I.GEMV_SHAPES)
+def test_gemv_full_shapes(k, n):
+    p_dev, s_dev, p_ref, s_ref = q2_weights(20, n, k)
+    for m in (1, 4, 16):
+        xb, x = acts(20 + m, m, k)
+        y = q2.q2_linear(x, p_dev, s_dev).cpu().numpy()
+        assert_close(y, O.q2_linear(xb, p_ref, s_ref), f"gemv M={m} K={k} N={n}")
+
+
+@pytest.mark.parametrize("k,n", I.GEMM_SHAPES)
+def test_gemm_full_shapes(k, n):
+    m = I.GEMM_M
+    p_dev, s_dev, p_ref, s_ref = q2_weights(30, n, k)
+    xb, x = acts(30, m, k)
+    y = q2.q2_linear(x, p_dev, s_dev).cpu().numpy()
+    if (k, n) == (3072, 3072):
+        assert_close(y, O.q2_linear(xb, p_ref, s_ref), "gemm full")
+    cols = sample_cols(n)
+    assert_close(y[:, cols], O.q2_linear_cols(xb, p_ref, s_ref, cols), f"gemm K={k} N={n} sampled")
+
+
+def test_determinism_and_guards():
+    for m, n, k in ((1, 3072, 3072), (1536, 3072, 3072), (9, 1000, 1280)):
+        p_dev, s_dev, p_ref, s_ref = q2_weights(40, n, k)
+        xb, x = acts(40, m, k)
+        guard = 16384
+        buf = torch.full((2 * guard + m * n,), float("nan"), device=DEV)
+        buf[:guard] = 1234.5
+        buf[-guard:] = -4321.5
+        y = buf[guard:guard + m * n].view(m, n)
+        q2.q2_linear(x, p_dev, s_dev, y)
+        y2 = q2.q2_linear(x, p_dev, s_dev)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y).any(), "output not fully written"
+        assert torch.all(buf[:guard] == 1234.5) and torch.all(buf[-guard:] == -4321.5), "write outside y"
+        assert torch.equal(y, y2), "not bitwise reproducible"
+
+
+# ---------------------------------------------------------------------------
+# low-rank branch
+# ---------------------------------------------------------------------------
+
+def lowrank_case(cfg, m, k, n, r):
+    p_dev, s_dev, p_ref, s_ref = q2_weights(cfg, n, k)
+    xb, x = acts(cfg, m, k)
+    a, b = I.lowrank_factors(cfg, r, k, n)
+    return p_dev, s_dev, p_ref, s_ref, xb, x, a, b, dev_bits(a, torch.float16), dev_bits(b, torch.float16)
+
+
+@pytest.mark.parametrize("m,k,n,r", [(4, 256, 64, 4), (4, 256, 64, 32), (1, 3072, 9216, 32), (17, 384, 100, 5),
+                                     (16, 1280, 333, 64), (200, 640, 250, 7), (96, 3072, 192, 64)])
+def test_lowrank_parity(m, k, n, r):
+    p_dev, s_dev, p_ref, s_ref, xb, x, a, b, A, B = lowrank_case(50, m, k, n, r)
+    y = q2.q2_linear_lowrank(x, p_dev, s_dev, A, B).cpu().numpy()
+    assert_close(y, O.q2_linear_lowrank(xb, p_ref, s_ref, a, b), f"lowrank M={m} K={k} N={n} r={r}")
+
+
+@pytest.mark.parametrize("r", I.LOWRANK["ranks"])
+def test_lowrank_full_shape_sampled(r):
+    c = I.LOWRANK
+    m, k, n = c["M"], c["K"], c["N"]
+    p_dev, s_dev, p_ref, s_ref, xb, x, a, b, A, B = lowrank_case(60 + r, m, k, n, r)
+    y = q2.q2_linear_lowrank(x, p_dev, s_dev, A, B).cpu().numpy()
+    cols = sample_cols(n)
+    ref = O.q2_linear_cols(xb, p_ref, s_ref, cols) + O.lowrank_t(xb, a) @ O.f16_to_f64(b[cols]).T
+    assert_close(y[:, cols], ref, f"lowrank full r={r}")
+
+
+def test_lowrank_rank_zero_is_linear():
+    p_dev, s_dev, _, _, _, x, _, _, _, B = lowrank_case(70, 40, 512, 96, 3)
+    A0 = torch.empty((0, 512), dtype=torch.float16, device=DEV)
+    B0 = torch.empty((96, 0), dtype=torch.float16, device=DEV)
+    assert torch.equal(q2.q2_linear_lowrank(x, p_dev, s_dev, A0, B0), q2.q2_linear(x, p_dev, s_dev))
+
+
+def test_layer_list_steps_are_reproducible():
+    m, k, n, r, layers = 1536, 3072, 3072, 32, 6
+    xb, x = acts(80, m, k)
+    ws = torch.empty(q2.lowrank_workspace_bytes(m, r), dtype=torch.uint8, device=DEV)
+    weights = []
+    for i in range(layers):
+        p_dev, s_dev, p_ref, s_ref = q2_weights(800 + i, n, k)
+        a, b = I.lowrank_factors(800 + i, r, k, n)
+        weights.append((p_dev, s_dev, p_ref, s_ref, a, b, dev_bits(a, torch.float16), dev_bits(b, torch.float16)))
+    outs = [[torch.empty((m, n), device=DEV) for _ in range(layers)] for _ in range(2)]
+    for step in range(2):
+        for i, (p_dev, s_dev, _, _, _, _, A, B) in enumerate(weights):
+            q2.q2_linear_lowrank(x, p_dev, s_dev, A, B, y=outs[step][i], workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(layers):
+        assert torch.equal(outs[0][i], outs[1][i])
+    p_dev, s_dev, p_ref, s_ref, a, b, _, _ = weights[0]
+    cols = sample_cols(n, 64)
+    ref = O.q2_linear_cols(xb, p_ref, s_ref, cols) + O.lowrank_t(xb, a) @ O.f16_to_f64(b[cols]).T
+    assert_close(outs[1][0].cpu().numpy()[:, cols], ref, "layer list")
+
+
+# ---------------------------------------------------------------------------
+# 4-bit nibble variant
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["auto", "gemm"], indirect=True)
+def test_q4_hand_nibble_order(path):
+    k = 128
+    p4 = np.zeros((1, k // 2), np.uint8)
+    p4[0, :2] = [0x21, 0x43]
+    x = np.zeros((1, k), np.float32)
+    x[0, :4] = [1, 10, 100, 1000]
+    y = q2.q4_linear(dev_bits(I.f32_to_bf16_bits(x), torch.bfloat16), dev_u8(p4),
+                     dev_bits(np.full((1, 1), 0x3C00, np.uint16), torch.float16),
+                     dev_bits(np.zeros((1, 1), np.uint16), torch.float16)).cpu().numpy()
+    assert y[0, 0] == 4321.0
+
+
+def q4_case(cfg, m, k, n):
+    p4, s, z = I.q4_weights(cfg, n, k)
+    xb, x = acts(cfg, m, k)
+    return p4, s, z, xb, x, dev_u8(p4), dev_bits(s, torch.float16), dev_bits(z, torch.float16)
+
+
+@pytest.mark.parametrize("path", ["auto", "gemm"], indirect=True)
+@pytest.mark.parametrize("m,n,k", [(1, 64, 256), (5, 77, 384), (16, 300, 1280), (17, 100, 256), (128, 257, 640)])
+def test_q4_ragged(path, m, n, k):
+    p4, s, z, xb, x, P, S, Z = q4_case(90, m, k, n)
+    y = q2.q4_linear(x, P, S, Z).cpu().numpy()
+    assert_close(y, O.q4_linear(xb, p4, s, z), f"q4 {path} M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("k,n", I.Q4_SHAPES)
+def test_q4_full_shapes(k, n):
+    m = I.Q4_M
+    p4, s, z, xb, x, P, S, Z = q4_case(95, m, k, n)
+    y = q2.q4_linear(x, P, S, Z).cpu().numpy()
+    if (k, n) == (2560, 2560):
+        assert_close(y, O.q4_linear(xb, p4, s, z), "q4 full")
+    cols = sample_cols(n)
+    assert_close(y[:, cols], O.q4_linear_cols(xb, p4, s, z, cols), f"q4 K={k} N={n} sampled")
