@@ -1,0 +1,258 @@
+"""Benchmark of the Q2_0 ternary linear on one MI355X.
+
+One step is one pass of the whole hot path over synthetic inputs shaped like a
+~4B MMDiT denoise step and its text encoder:
+  * the Q2_0 linear at M = 1536 tokens (1024 image + 512 text) for
+    (K, N) = (3072, 3072), (3072, 9216), (3072, 12288), (12288, 3072);
+  * the Q2_0 linear at M = 1 for the same four weight shapes (streaming path),
+    each call on a different copy of the weight so that >= 1 GiB rotates
+    through HBM and the 256 MB Infinity Cache cannot serve it;
+  * the Q2_0 linear with a rank-32 side branch, M = 1536, K = 3072, N = 9216;
+  * the 4-bit linear at M = 128 for (2560, 9728), (9728, 2560), (2560, 2560).
+All inputs are resident in HBM before timing starts.  value = effective
+TFLOP/s (2 M N K per linear, low-rank flops added) of the whole step; the
+per-row figures (TFLOP/s for M > 1, packed-weight GB/s for M = 1) and their
+roofline fractions are reported beside it.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+Q2_BYTES_PER_WEIGHT = 0.265625  # 2 bits + one f16 per 128 weights
+Q4_BYTES_PER_WEIGHT = 0.53125
+ROTATE_BYTES = 1 << 30
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "ternary_weight_quantized_q2_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM traffic per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemm_m1536_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline():
+    """The CPU oracle (float64 NumPy + BLAS) on a bounded sample: the Q2_0
+    linear at M = 1536, K = N = 3072, repeated for about 10 s."""
+    from threadpoolctl import threadpool_info
+    from oracle import q2_oracle as O
+    from ternary_weight_quantized_q2_amd import inputs as I
+
+    m, k, n = 1536, 3072, 3072
+    packed, sc = O.pack_q2(I.q2_codes(30, n, k), I.q2_scales(30, n, k))
+    xb = I.activations_bf16(30, m, k)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.q2_linear(xb, packed, sc)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(2.0 * m * n * k * reps / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} x Q2_0 linear M={m} K={k} N={n} (unpack + float64 dgemm), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(sharding is described in DESIGN.md, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ternary_weight_quantized_q2_amd as q2
+    from ternary_weight_quantized_q2_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q2.load()
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bits(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(dt)
+
+    def q2w(cfg, n, k):
+        return q2.q2_pack(u8(I.q2_codes(cfg, n, k)), torch.from_numpy(I.q2_scales(cfg, n, k)).to(dev))
+
+    calls = []   # (family, flops, weight_bytes, fn)
+    # M = 1536 GEMMs
+    m = I.GEMM_M
+    x_by_k = {k: bits(I.activations_bf16(300 + k, m, k), torch.bfloat16) for k in (3072, 12288)}
+    for k, n in I.GEMM_SHAPES:
+        copies = [q2w(310 + i, n, k) for i in range(2)]
+        y = torch.empty((m, n), device=dev)
+        state = {"i": 0}
+
+        def fn(k=k, copies=copies, y=y, state=state):
+            p, s = copies[state["i"] % len(copies)]
+            state["i"] += 1
+            q2.q2_linear(x_by_k[k], p, s, y)
+        calls.append(("gemm_m1536", 2.0 * m * n * k, Q2_BYTES_PER_WEIGHT * n * k, fn, f"M={m} K={k} N={n}"))
+    # M = 1 streaming GEMVs over rotated weight copies
+    for k, n in I.GEMV_SHAPES:
+        wbytes = Q2_BYTES_PER_WEIGHT * n * k
+        ncopies = int(np.ceil(ROTATE_BYTES / wbytes))
+        base_p, base_s = q2w(320, n, k)
+        copies = [(base_p.clone(), base_s.clone()) for _ in range(ncopies)]
+        x1 = bits(I.activations_bf16(321, 1, k), torch.bfloat16)
+        y = torch.empty((1, n), device=dev)
+        state = {"i": 0}
+
+        def fn(copies=copies, x1=x1, y=y, state=state):
+            p, s = copies[state["i"] % len(copies)]
+            state["i"] += 1
+            q2.q2_linear(x1, p, s, y)
+        calls.append(("gemv_m1", 2.0 * n * k, wbytes, fn, f"M=1 K={k} N={n} x{ncopies} copies"))
+    # low-rank branch, rank 32
+    lr = I.LOWRANK
+    r = 32
+    lp, ls = q2w(330, lr["N"], lr["K"])
+    a, b = I.lowrank_factors(330, r, lr["K"], lr["N"])
+    A, B = bits(a, torch.float16), bits(b, torch.float16)
+    xl = x_by_k[lr["K"]]
+    yl = torch.empty((lr["M"], lr["N"]), device=dev)
+    ws = torch.empty(q2.lowrank_workspace_bytes(lr["M"], r), dtype=torch.uint8, device=dev)
+    calls.append(("lowrank_r32", 2.0 * lr["M"] * lr["N"] * lr["K"] + 2.0 * lr["M"] * r * (lr["K"] + lr["N"]),
+                  Q2_BYTES_PER_WEIGHT * lr["N"] * lr["K"],
+                  lambda: q2.q2_linear_lowrank(xl, lp, ls, A, B, y=yl, workspace=ws),
+                  f"M={lr['M']} K={lr['K']} N={lr['N']} r={r}"))
+    # 4-bit encoder linears
+    for k, n in I.Q4_SHAPES:
+        p4, s4, z4 = I.q4_weights(340, n, k)
+        P, S, Z = u8(p4), bits(s4, torch.float16), bits(z4, torch.float16)
+        xq = bits(I.activations_bf16(341, I.Q4_M, k), torch.bfloat16)
+        yq = torch.empty((I.Q4_M, n), device=dev)
+        calls.append(("q4_m128", 2.0 * I.Q4_M * n * k, Q4_BYTES_PER_WEIGHT * n * k,
+                      lambda xq=xq, P=P, S=S, Z=Z, yq=yq: q2.q4_linear(xq, P, S, Z, yq),
+                      f"M={I.Q4_M} K={k} N={n}"))
+
+    def step(events=None):
+        for ci, c in enumerate(calls):
+            if events is not None:
+                events[ci][0].record()
+            c[3]()
+            if events is not None:
+                events[ci][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: the K steps are captured once into a HIP graph and replayed,
+    # so the host's per-call launch cost does not leave the GPU idle.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    step_flops = sum(c[1] for c in calls)
+
+    # Per-call durations: the same calls again, each bracketed by HIP events on
+    # torch's current stream (the stream the library launches on).  A GPU spin
+    # queued first lets the host enqueue the whole step before the GPU reaches
+    # it, so each event pair brackets back-to-back GPU execution only.
+    per = [[] for _ in calls]
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+        torch.cuda._sleep(5_000_000)
+        step(ev)
+        torch.cuda.synchronize()
+        for ci, (e0, e1) in enumerate(ev):
+            per[ci].append(e0.elapsed_time(e1) * 1e-3)
+
+    parts = {}
+    fam_time, fam_flops, fam_bytes = {}, {}, {}
+    for c, ts in zip(calls, per):
+        fam, flops, wbytes, _, label = c
+        t = float(np.mean(ts))
+        d = {"us": round(t * 1e6, 3), "tflops": round(flops / t / 1e12, 3),
+             "weight_gbs": round(wbytes / t / 1e9, 2)}
+        d["frac"] = round((wbytes / t / 1e9) / PEAK_HBM_GBS, 4) if fam == "gemv_m1" else \
+            round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        parts[f"{fam} {label}"] = d
+        fam_time[fam] = fam_time.get(fam, 0.0) + t
+        fam_flops[fam] = fam_flops.get(fam, 0.0) + flops
+        fam_bytes[fam] = fam_bytes.get(fam, 0.0) + wbytes
+
+    gemm_ach = fam_flops["gemm_m1536"] / fam_time["gemm_m1536"] / 1e12
+    gemv_ach = fam_bytes["gemv_m1"] / fam_time["gemv_m1"] / 1e9
+    traffic = measured_traffic()
+    out = {
+        "metric": "Q2_0 linear eff. TFLOP/s (M=1536) + packed-weight GB/s (M=1), % roofline",
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "one denoise-step pass of the Q2_0 hot path: Q2_0 linear M=1536 x "
+                        "{(3072,3072),(3072,9216),(3072,12288),(12288,3072)}; M=1 GEMV on the same shapes "
+                        "(>=1 GiB rotated per shape); rank-32 branch M=1536 K=3072 N=9216; 4-bit M=128 x "
+                        "{(2560,9728),(9728,2560),(2560,2560)}",
+            "weights": "Q2_0 codes {0,1,2} p=(.3,.4,.3), f16 scales |N(0,1)|*0.02; 4-bit codes U(0..15)",
+            "activations": "bf16 N(0,1)",
+            "parallelism": "single GPU",
+        },
+        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (Q2_0, M=1536)",
+                     "achieved": round(gemm_ach, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "roofline_gemv": {"bound": "hbm", "kernel": "gemv_kernel (Q2_0, M=1)", "achieved": round(gemv_ach, 2),
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gemv_ach / PEAK_HBM_GBS, 4)},
+        "m1536_tflops": round(gemm_ach, 3),
+        "m1_weight_gbs": round(gemv_ach, 2),
+        "parts": parts,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
