@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
+                    "gemm_m1536, gemv_m1, lowrank_r32, q4_m128")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -162,6 +164,12 @@ def main():
                       lambda xq=xq, P=P, S=S, Z=Z, yq=yq: q2.q4_linear(xq, P, S, Z, yq),
                       f"M={I.Q4_M} K={k} N={n}"))
 
+    if args.only:
+        keep = set(args.only.split(","))
+        calls = [c for c in calls if c[0] in keep]
+        if not calls:
+            sys.exit(f"--only {args.only}: no such call family")
+
     def step(events=None):
         for ci, c in enumerate(calls):
             if events is not None:
@@ -215,8 +223,8 @@ def main():
         fam_flops[fam] = fam_flops.get(fam, 0.0) + flops
         fam_bytes[fam] = fam_bytes.get(fam, 0.0) + wbytes
 
-    gemm_ach = fam_flops["gemm_m1536"] / fam_time["gemm_m1536"] / 1e12
-    gemv_ach = fam_bytes["gemv_m1"] / fam_time["gemv_m1"] / 1e9
+    gemm_ach = fam_flops["gemm_m1536"] / fam_time["gemm_m1536"] / 1e12 if "gemm_m1536" in fam_time else 0.0
+    gemv_ach = fam_bytes["gemv_m1"] / fam_time["gemv_m1"] / 1e9 if "gemv_m1" in fam_time else 0.0
     traffic = measured_traffic()
     out = {
         "metric": "Q2_0 linear eff. TFLOP/s (M=1536) + packed-weight GB/s (M=1), % roofline",

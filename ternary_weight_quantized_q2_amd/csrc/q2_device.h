@@ -41,28 +41,61 @@ __device__ __forceinline__ q2_f32x4 mfma(q2_u32x4 a, q2_u32x4 b, q2_f32x4 c) {
                                                   __builtin_bit_cast(q2_bf16x8, b), c, 0, 0, 0);
 }
 
+// (a & m) | o in one v_and_or_b32.  gfx950 VOP3 encodings take no literal
+// operands, so the two constants are passed in VGPRs (kept live by the caller);
+// written plainly, the compiler splits the expression into an AND and an OR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// Decoder constants: mask of the code field in each 16-bit half, and the bf16
+// pattern of 1.0 in both halves.
+struct DecodeConsts {
+  uint32_t mask, one;
+};
+__device__ __forceinline__ DecodeConsts q2_consts() {
+  DecodeConsts k;
+  // opaque to the optimiser so both stay in VGPRs
+  asm("v_mov_b32 %0, 0x00600060" : "=v"(k.mask));
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(k.one));
+  return k;
+}
+__device__ __forceinline__ DecodeConsts q4_consts() {
+  DecodeConsts k;
+  asm("v_mov_b32 %0, 0x00780078" : "=v"(k.mask));
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(k.one));
+  return k;
+}
+
 // ---- 2-bit codes -----------------------------------------------------------
 // Pair J (0..7) of dword w: halves = bf16(1 + c_J/4), bf16(1 + c_{J+8}/4).
 template <int J>
-__device__ __forceinline__ uint32_t q2_pair(uint32_t w) {
-  const uint32_t s = (J <= 2) ? (w << (5 - 2 * J)) : (w >> (2 * J - 5));
-  return (s & 0x00600060u) | 0x3F803F80u;
+__device__ __forceinline__ uint32_t q2_pair(uint32_t w, DecodeConsts k) {
+  uint32_t s;
+  if constexpr (J <= 2) s = w << (5 - 2 * J);
+  else s = w >> (2 * J - 5);
+  return and_or(s, k.mask, k.one);
 }
 // B operand for half H (0/1) of a codes dword: pairs 4H .. 4H+3.
 template <int H>
-__device__ __forceinline__ q2_u32x4 q2_bfrag(uint32_t w) {
-  return q2_u32x4{q2_pair<4 * H>(w), q2_pair<4 * H + 1>(w), q2_pair<4 * H + 2>(w), q2_pair<4 * H + 3>(w)};
+__device__ __forceinline__ q2_u32x4 q2_bfrag(uint32_t w, DecodeConsts k) {
+  return q2_u32x4{q2_pair<4 * H>(w, k), q2_pair<4 * H + 1>(w, k), q2_pair<4 * H + 2>(w, k),
+                  q2_pair<4 * H + 3>(w, k)};
 }
 
 // ---- 4-bit codes -----------------------------------------------------------
 // Pair J (0..3) of dword w (8 nibbles): halves = bf16(1 + q_J/16), bf16(1 + q_{J+4}/16).
 template <int J>
-__device__ __forceinline__ uint32_t q4_pair(uint32_t w) {
-  const uint32_t s = (J == 0) ? (w << 3) : (w >> (4 * J - 3));
-  return (s & 0x00780078u) | 0x3F803F80u;
+__device__ __forceinline__ uint32_t q4_pair(uint32_t w, DecodeConsts k) {
+  uint32_t s;
+  if constexpr (J == 0) s = w << 3;
+  else s = w >> (4 * J - 3);
+  return and_or(s, k.mask, k.one);
 }
-__device__ __forceinline__ q2_u32x4 q4_bfrag(uint32_t w) {
-  return q2_u32x4{q4_pair<0>(w), q4_pair<1>(w), q4_pair<2>(w), q4_pair<3>(w)};
+__device__ __forceinline__ q2_u32x4 q4_bfrag(uint32_t w, DecodeConsts k) {
+  return q2_u32x4{q4_pair<0>(w, k), q4_pair<1>(w, k), q4_pair<2>(w, k), q4_pair<3>(w, k)};
 }
 
 // ---- activation pair order -------------------------------------------------

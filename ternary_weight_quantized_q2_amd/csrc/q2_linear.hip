@@ -33,41 +33,38 @@ template <> struct WFmt<1> {           // 4-bit: 64 bytes per row and group
   static constexpr int LANE_DW = 4;    // lane group g holds dwords 4g .. 4g+3
 };
 
+// Packed codes, scale and zero point of one block of one weight row.  The row
+// index must already be clamped to a valid row: rows past N load row N-1,
+// whose outputs are computed but never stored, so loads never branch.
 template <int FMT>
 __device__ __forceinline__ void load_wblock(const LinearArgs& a, int64_t row, int64_t blk, int g,
                                             uint32_t (&out)[WFmt<FMT>::LANE_DW], float& sc, float& zp) {
   constexpr int DW = WFmt<FMT>::LANE_DW;
-  if (row < a.N) {
-    const int64_t row_bytes = (FMT == 0) ? a.K / 4 : a.K / 2;
-    const uint8_t* p = a.w + row * row_bytes + blk * WFmt<FMT>::BLOCK_BYTES + g * DW * 4;
-    if constexpr (DW == 2) {
-      const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(p);
-      out[0] = v[0]; out[1] = v[1];
-    } else {
-      const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(p);
-      out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
-    }
-    const int64_t si = row * (a.K / BLOCK_K) + blk;
-    sc = f16_to_f32(a.s[si]);
-    zp = (FMT == 1) ? f16_to_f32(a.z[si]) : 0.f;
+  const int64_t row_bytes = (FMT == 0) ? a.K / 4 : a.K / 2;
+  const uint8_t* p = a.w + row * row_bytes + blk * WFmt<FMT>::BLOCK_BYTES + g * DW * 4;
+  if constexpr (DW == 2) {
+    const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(p);
+    out[0] = v[0]; out[1] = v[1];
   } else {
-#pragma unroll
-    for (int i = 0; i < DW; ++i) out[i] = 0u;
-    sc = 0.f;
-    zp = 0.f;
+    const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(p);
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
   }
+  const int64_t si = row * (a.K / BLOCK_K) + blk;
+  sc = f16_to_f32(a.s[si]);
+  zp = (FMT == 1) ? f16_to_f32(a.z[si]) : 0.f;
 }
 
 template <int FMT>
-__device__ __forceinline__ void decode_block(const uint32_t (&w)[WFmt<FMT>::LANE_DW], q2_u32x4 (&bf)[4]) {
+__device__ __forceinline__ void decode_block(const uint32_t (&w)[WFmt<FMT>::LANE_DW], q2_u32x4 (&bf)[4],
+                                             DecodeConsts k) {
   if constexpr (FMT == 0) {
-    bf[0] = q2_bfrag<0>(w[0]);
-    bf[1] = q2_bfrag<1>(w[0]);
-    bf[2] = q2_bfrag<0>(w[1]);
-    bf[3] = q2_bfrag<1>(w[1]);
+    bf[0] = q2_bfrag<0>(w[0], k);
+    bf[1] = q2_bfrag<1>(w[0], k);
+    bf[2] = q2_bfrag<0>(w[1], k);
+    bf[3] = q2_bfrag<1>(w[1], k);
   } else {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) bf[t] = q4_bfrag(w[t]);
+    for (int t = 0; t < 4; ++t) bf[t] = q4_bfrag(w[t], k);
   }
 }
 
@@ -78,24 +75,18 @@ __device__ __forceinline__ q2_f32x4 block_cinit(q2_f32x4 s4, float zp) {
   return q2_f32x4{k * s4[0], k * s4[1], k * s4[2], k * s4[3]};
 }
 
-// Stage 16 activations (32 bytes) of one row: pair order + fp32 sum.
 template <int FMT>
 __device__ __forceinline__ void stage_pairs(const uint32_t (&nx)[8], uint32_t (&pr)[8]) {
   if constexpr (FMT == 0) q2_xpairs(nx, pr);
   else q4_xpairs(nx, pr);
 }
 
-__device__ __forceinline__ void load_x16(const uint16_t* x, int64_t row, int64_t M, int64_t K, int64_t k0,
-                                         uint32_t (&nx)[8]) {
-  if (row < M) {
-    const q2_u32x4* p = reinterpret_cast<const q2_u32x4*>(x + row * K + k0);
-    const q2_u32x4 v0 = p[0], v1 = p[1];
-    nx[0] = v0[0]; nx[1] = v0[1]; nx[2] = v0[2]; nx[3] = v0[3];
-    nx[4] = v1[0]; nx[5] = v1[1]; nx[6] = v1[2]; nx[7] = v1[3];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) nx[i] = 0u;
-  }
+// 16 activations (32 bytes) of one row; `row` must be a valid row.
+__device__ __forceinline__ void load_x16(const uint16_t* x, int64_t row, int64_t K, int64_t k0, uint32_t (&nx)[8]) {
+  const q2_u32x4* p = reinterpret_cast<const q2_u32x4*>(x + row * K + k0);
+  const q2_u32x4 v0 = p[0], v1 = p[1];
+  nx[0] = v0[0]; nx[1] = v0[1]; nx[2] = v0[2]; nx[3] = v0[3];
+  nx[4] = v1[0]; nx[5] = v1[1]; nx[6] = v1[2]; nx[7] = v1[3];
 }
 
 __device__ __forceinline__ float sum8_lanes(float v) {
@@ -107,16 +98,21 @@ __device__ __forceinline__ float sum8_lanes(float v) {
 
 // ---- low-rank epilogue operands -------------------------------------------
 // A'' = [T_hi, T_hi, T_lo] (row m of the limbs), B'' = [B_hi, B_lo, B_hi] (row n of B),
-// so sum_q A''[m,q] B''[n,q] = T_hi B_hi + T_hi B_lo + T_lo B_hi.
-__device__ __forceinline__ q2_u32x4 lr_afrag(const uint16_t* tl, int64_t m, int64_t M, int r, int q0) {
+// so sum_q A''[m,q] B''[n,q] = T_hi B_hi + T_hi B_lo + T_lo B_hi.  With r % 8 == 0 the
+// eight elements of a lane group lie in one part and one aligned 16-byte run.
+__device__ __forceinline__ q2_u32x4 lr_afrag(const uint16_t* tl, int64_t m, int r, int q0, bool vec) {
+  if (q0 >= 3 * r) return q2_u32x4{0u, 0u, 0u, 0u};
+  if (vec) {
+    const int part = q0 / r, jj = q0 - part * r;
+    return *reinterpret_cast<const q2_u32x4*>(tl + m * 2 * r + (part == 2 ? r : 0) + jj);
+  }
   uint32_t e[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int q = q0 + k;
     uint32_t v = 0;
-    if (m < M && q < 3 * r) {
-      const int part = q / r;
-      const int jj = q - part * r;
+    if (q < 3 * r) {
+      const int part = q / r, jj = q - part * r;
       v = tl[m * 2 * r + (part == 2 ? r : 0) + jj];
     }
     e[k] = v;
@@ -124,17 +120,29 @@ __device__ __forceinline__ q2_u32x4 lr_afrag(const uint16_t* tl, int64_t m, int6
   return q2_u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
 }
 
-__device__ __forceinline__ q2_u32x4 lr_bfrag(const uint16_t* B, int64_t n, int64_t N, int r, int q0) {
+__device__ __forceinline__ q2_u32x4 lr_bfrag(const uint16_t* B, int64_t n, int r, int q0, bool vec) {
+  if (q0 >= 3 * r) return q2_u32x4{0u, 0u, 0u, 0u};
+  uint16_t h[8];
+  const int part0 = q0 / r;
+  if (vec) {
+    const int jj = q0 - part0 * r;
+    const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(B + n * r + jj);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      h[2 * d] = (uint16_t)(v[d] & 0xFFFFu);
+      h[2 * d + 1] = (uint16_t)(v[d] >> 16);
+    }
+  }
   uint32_t e[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int q = q0 + k;
     uint32_t v = 0;
-    if (n < N && q < 3 * r) {
-      const int part = q / r;
-      const int jj = q - part * r;
+    if (q < 3 * r) {
+      const int part = vec ? part0 : q / r;
+      const uint16_t hv = vec ? h[k] : B[n * r + (q - part * r)];
       uint16_t hi, lo;
-      f16_split_bf16(B[n * r + jj], hi, lo);
+      f16_split_bf16(hv, hi, lo);
       v = (part == 1) ? lo : hi;
     }
     e[k] = v;
@@ -148,7 +156,7 @@ __device__ __forceinline__ q2_u32x4 lr_bfrag(const uint16_t* B, int64_t n, int64
 constexpr int XSTRIDE = 68;   // dwords per staged row-block: 64 pair dwords + 4 pad (bank spread)
 
 template <int FMT, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m) {
+__global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, int lr_vec) {
   constexpr int MT = BM / 16;            // 16-row tiles per wave
   constexpr int NT = BN / 64;            // 16-column tiles per wave (4 waves along N)
   constexpr int CPT = BM / 32;           // 16-element staging chunks per thread per block
@@ -164,16 +172,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m) {
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t nw = (int64_t)tn * BN + wv * (BN / 4);   // first row of W for this wave
   const int64_t M = a.M, K = a.K, KB = K / BLOCK_K;
+  const DecodeConsts kc = (FMT == 0) ? q2_consts() : q4_consts();
 
   const int part = tid & 7;
   const int row0 = tid >> 3;
-
-  uint32_t xr[CPT][8];
-  auto stage_load = [&](int64_t blk) {
+  int64_t xrow[CPT];
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) load_x16(a.x, m0 + row0 + 32 * q, M, K, blk * BLOCK_K + part * 16, xr[q]);
+  for (int q = 0; q < CPT; ++q) {
+    const int64_t r = m0 + row0 + 32 * q;
+    xrow[q] = r < M ? r : M - 1;
+  }
+  int64_t wrow[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int64_t r = nw + 16 * j + c;
+    wrow[j] = r < a.N ? r : a.N - 1;
+  }
+
+  auto x_load = [&](uint32_t (&xr)[CPT][8], int64_t blk) {
+    blk = blk < KB ? blk : KB - 1;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) load_x16(a.x, xrow[q], K, blk * BLOCK_K + part * 16, xr[q]);
   };
-  auto stage_store = [&](int buf) {
+  auto x_store = [&](const uint32_t (&xr)[CPT][8], int buf) {
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int row = row0 + 32 * q;
@@ -186,62 +207,71 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m) {
       if (part == 0) ss[buf][row] = sm;
     }
   };
+  auto w_load = [&](uint32_t (&w)[NT][DW], float (&d)[NT], float (&z)[NT], int64_t blk) {
+    blk = blk < KB ? blk : KB - 1;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) load_wblock<FMT>(a, wrow[j], blk, g, w[j], d[j], z[j]);
+  };
 
-  uint32_t wc[NT][DW], wn[NT][DW];
-  float dc[NT], dn[NT], zc[NT], zn[NT];
   q2_f32x4 acc[MT][NT];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (KB > 0) {
-    stage_load(0);
-    stage_store(0);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) load_wblock<FMT>(a, nw + 16 * j + c, 0, g, wc[j], dc[j], zc[j]);
-  }
-  __syncthreads();
-
-  for (int64_t b = 0; b < KB; ++b) {
-    const int cur = (int)(b & 1);
-    const bool more = b + 1 < KB;
-    if (more) {
-      stage_load(b + 1);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) load_wblock<FMT>(a, nw + 16 * j + c, b + 1, g, wn[j], dn[j], zn[j]);
-    }
+  // One block: decode this wave's weights, refill their registers with the
+  // block two ahead, then run the MFMAs over the staged activations.
+  auto compute = [&](int buf, uint32_t (&w)[NT][DW], float (&d)[NT], float (&z)[NT], int64_t next_blk) {
     q2_u32x4 bf[NT][4];
+    float dc[NT], zc[NT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) decode_block<FMT>(wc[j], bf[j]);
-
+    for (int j = 0; j < NT; ++j) {
+      decode_block<FMT>(w[j], bf[j], kc);
+      dc[j] = d[j];
+      zc[j] = z[j];
+    }
+    w_load(w, d, z, next_blk);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[cur][16 * i + 4 * g]);
+      const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[buf][16 * i + 4 * g]);
       q2_f32x4 tmp[NT];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const q2_u32x4 av = *reinterpret_cast<const q2_u32x4*>(&xs[cur][(16 * i + c) * XSTRIDE + 16 * g + 4 * t]);
+        const q2_u32x4 av = *reinterpret_cast<const q2_u32x4*>(&xs[buf][(16 * i + c) * XSTRIDE + 16 * g + 4 * t]);
 #pragma unroll
         for (int j = 0; j < NT; ++j) tmp[j] = mfma(av, bf[j][t], t == 0 ? block_cinit<FMT>(s4, zc[j]) : tmp[j]);
       }
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
+      for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(dc[j], tmp[j][e], acc[i][j][e]);
-      }
     }
-    if (more) {
-      stage_store(cur ^ 1);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-#pragma unroll
-        for (int d = 0; d < DW; ++d) wc[j][d] = wn[j][d];
-        dc[j] = dn[j];
-        zc[j] = zn[j];
-      }
-    }
+  };
+
+  if (KB > 0) {
+    uint32_t xA[CPT][8], xB[CPT][8];
+    uint32_t wA[NT][DW], wB[NT][DW];
+    float dA[NT], dB[NT], zA[NT], zB[NT];
+    x_load(xA, 0);
+    w_load(wA, dA, zA, 0);
+    x_load(xB, 1);
+    w_load(wB, dB, zB, 1);
+    x_store(xA, 0);
+    x_load(xA, 2);
     __syncthreads();
+    // Steady state at block b: LDS[b&1] holds X(b); the other X registers
+    // hold X(b+1) (to be staged after this block) and X(b+2) (in flight).
+    for (int64_t b = 0; b < KB; b += 2) {
+      compute(0, wA, dA, zA, b + 2);
+      if (b + 1 < KB) x_store(xB, 1);
+      x_load(xB, b + 3);
+      __syncthreads();
+      if (b + 1 >= KB) break;
+      compute(1, wB, dB, zB, b + 3);
+      if (b + 2 < KB) x_store(xA, 0);
+      x_load(xA, b + 4);
+      __syncthreads();
+    }
   }
 
   const float fin = (FMT == 0) ? 4.f : 16.f;
@@ -258,10 +288,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m) {
       const int q0 = 32 * t + 8 * g;
       q2_u32x4 bq[NT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) bq[j] = lr_bfrag(a.lr_b, nw + 16 * j + c, a.N, a.r, q0);
+      for (int j = 0; j < NT; ++j) bq[j] = lr_bfrag(a.lr_b, wrow[j], a.r, q0, lr_vec != 0);
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const q2_u32x4 aq = lr_afrag(a.lr_t, m0 + 16 * i + c, M, a.r, q0);
+        int64_t mr = m0 + 16 * i + c;
+        mr = mr < M ? mr : M - 1;
+        const q2_u32x4 aq = lr_afrag(a.lr_t, mr, a.r, q0, lr_vec != 0);
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
       }
@@ -287,12 +319,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m) {
 // ============================================================================
 // GEMV, M <= 16
 // ============================================================================
-constexpr int GEMV_WAVES = 4;
-constexpr int GEMV_PF = 8;                        // weight blocks in flight per wave
+constexpr int GEMV_WAVES = 8;
+constexpr int GEMV_QMAX = 12;                     // weight blocks per wave per chunk, all in flight at once
 constexpr int GEMV_X_BUDGET = 64 * 1024;          // LDS bytes for staged activations
 
 template <int FMT>
-__global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int cb) {
+__global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int cb, int lr_vec) {
   constexpr int DW = WFmt<FMT>::LANE_DW;
   extern __shared__ __align__(16) uint32_t smem[];
   const int M = (int)a.M;
@@ -303,20 +335,33 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int64_t n = (int64_t)blockIdx.x * 16 + c;        // weight row of this lane's MFMA column
+  const int64_t nc = n < a.N ? n : a.N - 1;
   const int64_t K = a.K, KB = K / BLOCK_K;
+  const int crow = c < M ? c : M - 1;
+  const DecodeConsts kc = (FMT == 0) ? q2_consts() : q4_consts();
 
   q2_f32x4 acc = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t cb0 = 0; cb0 < KB; cb0 += cb) {
     const int nb = (int)((KB - cb0) < cb ? (KB - cb0) : cb);
-    // stage this chunk of activations
+    const int mine = (nb - wv + GEMV_WAVES - 1) / GEMV_WAVES;   // blocks wv, wv + 8, ... of this chunk
+    // every weight load of this wave goes out first
+    uint32_t wq[GEMV_QMAX][DW];
+    float dq[GEMV_QMAX], zq[GEMV_QMAX];
+#pragma unroll
+    for (int q = 0; q < GEMV_QMAX; ++q) {
+      int bl = wv + GEMV_WAVES * q;
+      bl = bl < nb ? bl : nb - 1;
+      load_wblock<FMT>(a, nc, cb0 + bl, g, wq[q], dq[q], zq[q]);
+    }
+    // stage this chunk of activations while the weights are in flight
     const int nchunks = M * nb * 8;
     for (int idx = tid; idx < nchunks; idx += GEMV_WAVES * 64) {
       const int row = idx / (nb * 8);
       const int rem = idx - row * nb * 8;
       const int bl = rem >> 3, prt = rem & 7;
       uint32_t nx[8], pr[8];
-      load_x16(a.x, row, M, K, (cb0 + bl) * BLOCK_K + prt * 16, nx);
+      load_x16(a.x, row, K, (cb0 + bl) * BLOCK_K + prt * 16, nx);
       stage_pairs<FMT>(nx, pr);
       q2_u32x4* dst = reinterpret_cast<q2_u32x4*>(&xs[row * rs + bl * 64 + prt * 8]);
       dst[0] = q2_u32x4{pr[0], pr[1], pr[2], pr[3]};
@@ -328,41 +373,23 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
       if ((idx & 15) >= M) ss[idx] = 0.f;
     __syncthreads();
 
-    // this wave's blocks: bl = wv, wv + 4, ...
-    const int mine = (nb - wv + GEMV_WAVES - 1) / GEMV_WAVES;
-    uint32_t wq[GEMV_PF][DW];
-    float dq[GEMV_PF], zq[GEMV_PF];
 #pragma unroll
-    for (int p = 0; p < GEMV_PF; ++p) {
-      if (p < mine) load_wblock<FMT>(a, n, cb0 + wv + GEMV_WAVES * p, g, wq[p], dq[p], zq[p]);
-    }
-    for (int q = 0; q < mine; ++q) {
-      const int bl = wv + GEMV_WAVES * q;
-      q2_u32x4 bf[4];
-      decode_block<FMT>(wq[0], bf);
-      const float dcur = dq[0], zcur = zq[0];
-      // rotate the prefetch window and fetch block q + GEMV_PF
+    for (int q = 0; q < GEMV_QMAX; ++q) {
+      if (q < mine) {
+        const int bl = wv + GEMV_WAVES * q;
+        q2_u32x4 bf[4];
+        decode_block<FMT>(wq[q], bf, kc);
+        const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[bl * 16 + 4 * g]);
+        q2_f32x4 tmp = block_cinit<FMT>(s4, zq[q]);
 #pragma unroll
-      for (int p = 0; p + 1 < GEMV_PF; ++p) {
+        for (int t = 0; t < 4; ++t) {
+          q2_u32x4 av = *reinterpret_cast<const q2_u32x4*>(&xs[crow * rs + bl * 64 + 16 * g + 4 * t]);
+          if (c >= M) av = q2_u32x4{0u, 0u, 0u, 0u};
+          tmp = mfma(av, bf[t], tmp);
+        }
 #pragma unroll
-        for (int d = 0; d < DW; ++d) wq[p][d] = wq[p + 1][d];
-        dq[p] = dq[p + 1];
-        zq[p] = zq[p + 1];
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(dq[q], tmp[e], acc[e]);
       }
-      if (q + GEMV_PF < mine)
-        load_wblock<FMT>(a, n, cb0 + wv + GEMV_WAVES * (q + GEMV_PF), g, wq[GEMV_PF - 1], dq[GEMV_PF - 1],
-                         zq[GEMV_PF - 1]);
-
-      const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[bl * 16 + 4 * g]);
-      q2_f32x4 tmp = block_cinit<FMT>(s4, zcur);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        q2_u32x4 av = q2_u32x4{0u, 0u, 0u, 0u};
-        if (c < M) av = *reinterpret_cast<const q2_u32x4*>(&xs[c * rs + bl * 64 + 16 * g + 4 * t]);
-        tmp = mfma(av, bf[t], tmp);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(dcur, tmp[e], acc[e]);
     }
     __syncthreads();
   }
@@ -384,7 +411,9 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
       const int ks = (3 * a.r + 31) / 32;
       for (int t = 0; t < ks; ++t) {
         const int q0 = 32 * t + 8 * g;
-        s = mfma(lr_afrag(a.lr_t, c, a.M, a.r, q0), lr_bfrag(a.lr_b, n, a.N, a.r, q0), s);
+        q2_u32x4 aq = lr_afrag(a.lr_t, crow, a.r, q0, lr_vec != 0);
+        if (c >= M) aq = q2_u32x4{0u, 0u, 0u, 0u};
+        s = mfma(aq, lr_bfrag(a.lr_b, nc, a.r, q0, lr_vec != 0), s);
       }
     }
     if (n < a.N) {
@@ -400,60 +429,81 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
 // ============================================================================
 // x A^T for the low-rank branch: bf16 limbs [M, 2r] = (hi | lo)
 // ============================================================================
-__global__ __launch_bounds__(256) void lowrank_t_kernel(const uint16_t* x, const uint16_t* A, uint16_t* tl,
-                                                        int64_t M, int64_t K, int r) {
-  __shared__ __align__(16) q2_f32x4 red[4][4][64];
+constexpr int LR_WAVES = 16;
+constexpr int LR_UNROLL = 2;     // k-steps whose loads are issued together
+
+__global__ __launch_bounds__(LR_WAVES * 64) void lowrank_t_kernel(const uint16_t* x, const uint16_t* A, uint16_t* tl,
+                                                                  int64_t M, int64_t K, int r) {
+  __shared__ __align__(16) q2_f32x4 red[LR_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int64_t m = (int64_t)blockIdx.x * 16 + c;          // A-operand row of this lane
+  int64_t m = (int64_t)blockIdx.x * 16 + c;                // A-operand row of this lane
+  m = m < M ? m : M - 1;
   const int col0 = blockIdx.y * 64;
+  const int ntl = (r - col0 + 15) / 16 < 4 ? (r - col0 + 15) / 16 : 4;   // live 16-column tiles
   const int64_t KS = K / 32;
   q2_f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+  int colc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = col0 + 16 * j + c;
+    colc[j] = col < r ? col : r - 1;
+  }
 
-  for (int64_t s = wv; s < KS; s += 4) {
-    const int64_t k0 = s * 32 + 8 * g;
-    q2_u32x4 av = q2_u32x4{0u, 0u, 0u, 0u};
-    if (m < M) av = *reinterpret_cast<const q2_u32x4*>(x + m * K + k0);
+  for (int64_t s0 = wv; s0 < KS; s0 += (int64_t)LR_WAVES * LR_UNROLL) {
+    q2_u32x4 av[LR_UNROLL], bv[LR_UNROLL][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = col0 + 16 * j + c;
-      q2_u32x4 bh = q2_u32x4{0u, 0u, 0u, 0u}, bl = q2_u32x4{0u, 0u, 0u, 0u};
-      if (col < r) {
-        const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(A + (int64_t)col * K + k0);
+    for (int u = 0; u < LR_UNROLL; ++u) {
+      int64_t s = s0 + (int64_t)LR_WAVES * u;
+      s = s < KS ? s : KS - 1;
+      const int64_t k0 = s * 32 + 8 * g;
+      av[u] = *reinterpret_cast<const q2_u32x4*>(x + m * K + k0);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          uint16_t h0, l0, h1, l1;
-          f16_split_bf16((uint16_t)(v[d] & 0xFFFFu), h0, l0);
-          f16_split_bf16((uint16_t)(v[d] >> 16), h1, l1);
-          bh[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          bl[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      for (int j = 0; j < 4; ++j)
+        if (j < ntl) bv[u][j] = *reinterpret_cast<const q2_u32x4*>(A + (int64_t)colc[j] * K + k0);
+    }
+#pragma unroll
+    for (int u = 0; u < LR_UNROLL; ++u) {
+      if (s0 + (int64_t)LR_WAVES * u < KS) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (j < ntl) {
+            q2_u32x4 bh, bl;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              uint16_t h0, l0, h1, l1;
+              f16_split_bf16((uint16_t)(bv[u][j][d] & 0xFFFFu), h0, l0);
+              f16_split_bf16((uint16_t)(bv[u][j][d] >> 16), h1, l1);
+              bh[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+              bl[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            acc[j] = mfma(av[u], bh, acc[j]);
+            acc[j] = mfma(av[u], bl, acc[j]);
+          }
         }
       }
-      acc[j] = mfma(av, bh, acc[j]);
-      acc[j] = mfma(av, bl, acc[j]);
     }
   }
+  for (int j = 0; j < 4; ++j) {
+    if (j >= ntl) break;
+    red[wv][lane] = acc[j];
+    __syncthreads();
+    if (wv == 0) {
+      q2_f32x4 sm = red[0][lane];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) red[wv][j][lane] = acc[j];
-  __syncthreads();
-  if (wv == 0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      q2_f32x4 s = red[0][j][lane];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) {
-        const q2_f32x4 o = red[w][j][lane];
-        s = q2_f32x4{s[0] + o[0], s[1] + o[1], s[2] + o[2], s[3] + o[3]};
+      for (int w = 1; w < LR_WAVES; ++w) {
+        const q2_f32x4 o = red[w][lane];
+        sm = q2_f32x4{sm[0] + o[0], sm[1] + o[1], sm[2] + o[2], sm[3] + o[3]};
       }
-      const int col = col0 + 16 * j + c;           // C layout: column = lane % 16
+      const int col = col0 + 16 * j + c;            // C layout: column = lane % 16
       if (col < r) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t row = (int64_t)blockIdx.x * 16 + 4 * g + e;
           if (row < M) {
-            const float t = s[e];
+            const float t = sm[e];
             const uint16_t hi = f32_to_bf16_rn(t);
             const uint16_t lo = f32_to_bf16_rn(t - bf16_to_f32(hi));
             tl[row * 2 * r + col] = hi;
@@ -462,19 +512,25 @@ __global__ __launch_bounds__(256) void lowrank_t_kernel(const uint16_t* x, const
         }
       }
     }
+    __syncthreads();
   }
 }
 
 // ============================================================================
 // launchers
 // ============================================================================
+static int lowrank_vec(const LinearArgs& a) {
+  return (a.r > 0 && a.r % 8 == 0 && (reinterpret_cast<uintptr_t>(a.lr_b) % 16) == 0) ? 1 : 0;
+}
+
 template <int FMT, int BM, int BN>
 static hipError_t run_gemm(const LinearArgs& a, hipStream_t stream) {
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t tiles_n = (a.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN>), dim3((unsigned)tiles), dim3(256), 0, stream, a, (int)tiles_m);
+  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN>), dim3((unsigned)tiles), dim3(256), 0, stream, a, (int)tiles_m,
+                     lowrank_vec(a));
   return hipGetLastError();
 }
 
@@ -483,6 +539,7 @@ static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   const int64_t KB = a.K / BLOCK_K;
   const int M = (int)a.M;
   int64_t cb = GEMV_X_BUDGET / (M * 256 + 16 + 64);
+  if (cb > (int64_t)GEMV_WAVES * GEMV_QMAX) cb = (int64_t)GEMV_WAVES * GEMV_QMAX;
   if (cb > KB) cb = KB;
   if (cb < 1) cb = 1;
   size_t bytes = (size_t)M * (cb * 64 + 4) * 4 + (size_t)cb * 16 * 4;
@@ -490,7 +547,8 @@ static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   if (bytes < red) bytes = red;
   const int64_t grid = (a.N + 15) / 16;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemv_kernel<FMT>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a, (int)cb);
+  hipLaunchKernelGGL((gemv_kernel<FMT>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a, (int)cb,
+                     lowrank_vec(a));
   return hipGetLastError();
 }
 
@@ -517,7 +575,8 @@ hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* tl, 
   const int64_t gx = (M + 15) / 16;
   const int gy = (r + 63) / 64;
   if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lowrank_t_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream, x, A, tl, M, K, r);
+  hipLaunchKernelGGL(lowrank_t_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(LR_WAVES * 64), 0, stream, x, A, tl, M,
+                     K, r);
   return hipGetLastError();
 }
 
