@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true", help="profiling mode: run warmup + steps eagerly and "
+                    "print only the wall time (no graph, no per-call events)")
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
                     "gemm_m1536, gemv_m1, lowrank_r32, q4_m128")
     args = ap.parse_args()
@@ -181,6 +183,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.eager:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(json.dumps({"eager_ms_per_step": 1e3 * (time.perf_counter() - t0) / args.steps,
+                          "calls": [c[4] for c in calls]}))
+        return
 
     # Timed region: the K steps are captured once into a HIP graph and replayed,
     # so the host's per-call launch cost does not leave the GPU idle.

@@ -20,7 +20,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libq2.so")
+# Q2_LIB names another build of the same library (for A/B measurements).
+LIB_PATH = os.environ.get("Q2_LIB") or os.path.join(_HERE, "libq2.so")
 
 Q2_OK, Q2_ERR_ARG, Q2_ERR_SHAPE, Q2_ERR_ALIGN, Q2_ERR_CODE, Q2_ERR_SCALE, Q2_ERR_DEVICE, Q2_ERR_HIP, \
     Q2_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7, -8

@@ -20,8 +20,11 @@ LIB = os.path.join(PKG, "libq2.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no packed fp32 instructions anywhere in the device code.
+# -amdgpu-mfma-vgpr-form: keep matrix-core results in VGPRs, where the
+# per-block rescale reads them, instead of accumulation registers.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", INCLUDE, "-I", CSRC]
 
 
@@ -36,23 +39,23 @@ def _compile(src):
     return obj, out
 
 
-def build(verbose=True):
+def build(verbose=True, out=LIB, srcs=None):
     os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = srcs or sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(_compile, srcs))
     for _, out in results:
         if out.strip() and verbose:
             print(out, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
-    return LIB
+        print(f"built {out}", file=sys.stderr)
+    return out
 
 
 if __name__ == "__main__":

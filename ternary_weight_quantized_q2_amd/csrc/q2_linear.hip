@@ -68,11 +68,16 @@ __device__ __forceinline__ void decode_block(const uint32_t (&w)[WFmt<FMT>::LANE
   }
 }
 
-// Accumulator start value of a block: Q2 -1.25 * S, 4-bit -(1 + z/16) * S.
+// Accumulator start value of a block from the staged, pre-scaled block sum
+// s4 (-1.25 S for 2-bit, -S for 4-bit): 2-bit -1.25 S, 4-bit -(1 + z/16) S.
 template <int FMT>
 __device__ __forceinline__ q2_f32x4 block_cinit(q2_f32x4 s4, float zp) {
-  const float k = (FMT == 0) ? -1.25f : -(1.f + zp * 0.0625f);
-  return q2_f32x4{k * s4[0], k * s4[1], k * s4[2], k * s4[3]};
+  if constexpr (FMT == 0) {
+    return s4;
+  } else {
+    const float k = 1.f + zp * 0.0625f;
+    return q2_f32x4{k * s4[0], k * s4[1], k * s4[2], k * s4[3]};
+  }
 }
 
 template <int FMT>
@@ -89,10 +94,16 @@ __device__ __forceinline__ void load_x16(const uint16_t* x, int64_t row, int64_t
   nx[4] = v1[0]; nx[5] = v1[1]; nx[6] = v1[2]; nx[7] = v1[3];
 }
 
+// Sum over 8 consecutive lanes with DPP moves (no LDS traffic); the total is
+// exact in the lane with (lane & 7) == 0, in a fixed order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float sum8_lanes(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x104>(v);   // row_shl:4 (lane i reads lane i + 4)
   return v;
 }
 
@@ -204,7 +215,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       dst[0] = q2_u32x4{pr[0], pr[1], pr[2], pr[3]};
       dst[1] = q2_u32x4{pr[4], pr[5], pr[6], pr[7]};
       const float sm = sum8_lanes(bf16_sum16(xr[q]));
-      if (part == 0) ss[buf][row] = sm;
+      if (part == 0) ss[buf][row] = sm * ((FMT == 0) ? -1.25f : -1.f);
     }
   };
   auto w_load = [&](uint32_t (&w)[NT][DW], float (&d)[NT], float (&z)[NT], int64_t blk) {
@@ -231,21 +242,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       zc[j] = z[j];
     }
     w_load(w, d, z, next_blk);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
+    // Tile i's MFMAs are issued before tile i-1's rescale so the FMAs run in
+    // the matrix core's shadow; two temporaries keep everything in VGPRs.
+    q2_f32x4 t0[NT], t1[NT];
+    auto tile = [&](int i, q2_f32x4 (&tmp)[NT]) {
       const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[buf][16 * i + 4 * g]);
-      q2_f32x4 tmp[NT];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const q2_u32x4 av = *reinterpret_cast<const q2_u32x4*>(&xs[buf][(16 * i + c) * XSTRIDE + 16 * g + 4 * t]);
 #pragma unroll
         for (int j = 0; j < NT; ++j) tmp[j] = mfma(av, bf[j][t], t == 0 ? block_cinit<FMT>(s4, zc[j]) : tmp[j]);
       }
+    };
+    auto rescale = [&](int i, const q2_f32x4 (&tmp)[NT]) {
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(dc[j], tmp[j][e], acc[i][j][e]);
+    };
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i & 1) {
+        tile(i, t1);
+        rescale(i - 1, t0);
+      } else {
+        tile(i, t0);
+        if (i > 0) rescale(i - 1, t1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if ((MT - 1) & 1) rescale(MT - 1, t1);
+    else rescale(MT - 1, t0);
   };
 
   if (KB > 0) {
@@ -320,10 +347,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 // GEMV, M <= 16
 // ============================================================================
 constexpr int GEMV_WAVES = 8;
-constexpr int GEMV_QMAX = 12;                     // weight blocks per wave per chunk, all in flight at once
-constexpr int GEMV_X_BUDGET = 64 * 1024;          // LDS bytes for staged activations
+constexpr int GEMV_XQ = 4;                        // 16-activation staging chunks per thread per chunk of K
+constexpr int GEMV_X_ROWBLOCKS = 256;             // (row, block) pairs staged per chunk: 64 KB of LDS
 
-template <int FMT>
+template <int FMT, int QMAX>
 __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int cb, int lr_vec) {
   constexpr int DW = WFmt<FMT>::LANE_DW;
   extern __shared__ __align__(16) uint32_t smem[];
@@ -335,46 +362,73 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int64_t n = (int64_t)blockIdx.x * 16 + c;        // weight row of this lane's MFMA column
-  const int64_t nc = n < a.N ? n : a.N - 1;
+  const int64_t nc = n < a.N ? n : a.N - 1;              // rows past N recompute row N-1, never stored
   const int64_t K = a.K, KB = K / BLOCK_K;
-  const int crow = c < M ? c : M - 1;
+  const int crow = c < M ? c : M - 1;                    // activation rows past M duplicate row M-1
   const DecodeConsts kc = (FMT == 0) ? q2_consts() : q4_consts();
+  const uint8_t* wbase = a.w + nc * ((FMT == 0) ? K / 4 : K / 2) + g * DW * 4;
+  const uint16_t* sbase = a.s + nc * KB;
+  const uint16_t* zbase = (FMT == 1) ? a.z + nc * KB : nullptr;
 
   q2_f32x4 acc = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t cb0 = 0; cb0 < KB; cb0 += cb) {
     const int nb = (int)((KB - cb0) < cb ? (KB - cb0) : cb);
     const int mine = (nb - wv + GEMV_WAVES - 1) / GEMV_WAVES;   // blocks wv, wv + 8, ... of this chunk
-    // every weight load of this wave goes out first
-    uint32_t wq[GEMV_QMAX][DW];
-    float dq[GEMV_QMAX], zq[GEMV_QMAX];
+    const int nchunks = M * nb * 8;
+    // activation loads first, so that staging waits on them only
+    uint32_t nx[GEMV_XQ][8];
 #pragma unroll
-    for (int q = 0; q < GEMV_QMAX; ++q) {
+    for (int u = 0; u < GEMV_XQ; ++u) {
+      int idx = tid + u * GEMV_WAVES * 64;
+      idx = idx < nchunks ? idx : nchunks - 1;
+      const int row = idx / (nb * 8);
+      const int rem = idx - row * nb * 8;
+      load_x16(a.x, row, K, (cb0 + (rem >> 3)) * BLOCK_K + (rem & 7) * 16, nx[u]);
+    }
+    // then every weight load of this wave's share of the chunk
+    uint32_t wq[QMAX][DW];
+    float dq[QMAX], zq[QMAX];
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
       int bl = wv + GEMV_WAVES * q;
       bl = bl < nb ? bl : nb - 1;
-      load_wblock<FMT>(a, nc, cb0 + bl, g, wq[q], dq[q], zq[q]);
+      const uint32_t blk = (uint32_t)(cb0 + bl);
+      const uint8_t* p = wbase + (uint64_t)blk * WFmt<FMT>::BLOCK_BYTES;
+      if constexpr (DW == 2) {
+        const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(p);
+        wq[q][0] = v[0]; wq[q][1] = v[1];
+      } else {
+        const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(p);
+        wq[q][0] = v[0]; wq[q][1] = v[1]; wq[q][2] = v[2]; wq[q][3] = v[3];
+      }
+      dq[q] = f16_to_f32(sbase[blk]);
+      zq[q] = (FMT == 1) ? f16_to_f32(zbase[blk]) : 0.f;
     }
-    // stage this chunk of activations while the weights are in flight
-    const int nchunks = M * nb * 8;
-    for (int idx = tid; idx < nchunks; idx += GEMV_WAVES * 64) {
+    // stage the activations in the decoder's pair order, with pre-scaled block sums
+#pragma unroll
+    for (int u = 0; u < GEMV_XQ; ++u) {
+      const int idx = tid + u * GEMV_WAVES * 64;
+      if (u * GEMV_WAVES * 64 >= nchunks) break;          // uniform: no chunk left for any thread
       const int row = idx / (nb * 8);
       const int rem = idx - row * nb * 8;
       const int bl = rem >> 3, prt = rem & 7;
-      uint32_t nx[8], pr[8];
-      load_x16(a.x, row, K, (cb0 + bl) * BLOCK_K + prt * 16, nx);
-      stage_pairs<FMT>(nx, pr);
-      q2_u32x4* dst = reinterpret_cast<q2_u32x4*>(&xs[row * rs + bl * 64 + prt * 8]);
-      dst[0] = q2_u32x4{pr[0], pr[1], pr[2], pr[3]};
-      dst[1] = q2_u32x4{pr[4], pr[5], pr[6], pr[7]};
-      const float sm = sum8_lanes(bf16_sum16(nx));
-      if (prt == 0) ss[bl * 16 + row] = sm;
+      uint32_t pr[8];
+      stage_pairs<FMT>(nx[u], pr);
+      const float sm = sum8_lanes(bf16_sum16(nx[u]));
+      if (idx < nchunks) {
+        q2_u32x4* dst = reinterpret_cast<q2_u32x4*>(&xs[row * rs + bl * 64 + prt * 8]);
+        dst[0] = q2_u32x4{pr[0], pr[1], pr[2], pr[3]};
+        dst[1] = q2_u32x4{pr[4], pr[5], pr[6], pr[7]};
+        if (prt == 0) ss[bl * 16 + row] = sm * ((FMT == 0) ? -1.25f : -1.f);
+      }
     }
     for (int idx = tid; idx < nb * 16; idx += GEMV_WAVES * 64)
       if ((idx & 15) >= M) ss[idx] = 0.f;
     __syncthreads();
 
 #pragma unroll
-    for (int q = 0; q < GEMV_QMAX; ++q) {
+    for (int q = 0; q < QMAX; ++q) {
       if (q < mine) {
         const int bl = wv + GEMV_WAVES * q;
         q2_u32x4 bf[4];
@@ -382,11 +436,8 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
         const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[bl * 16 + 4 * g]);
         q2_f32x4 tmp = block_cinit<FMT>(s4, zq[q]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          q2_u32x4 av = *reinterpret_cast<const q2_u32x4*>(&xs[crow * rs + bl * 64 + 16 * g + 4 * t]);
-          if (c >= M) av = q2_u32x4{0u, 0u, 0u, 0u};
-          tmp = mfma(av, bf[t], tmp);
-        }
+        for (int t = 0; t < 4; ++t)
+          tmp = mfma(*reinterpret_cast<const q2_u32x4*>(&xs[crow * rs + bl * 64 + 16 * g + 4 * t]), bf[t], tmp);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(dq[q], tmp[e], acc[e]);
       }
@@ -411,9 +462,7 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
       const int ks = (3 * a.r + 31) / 32;
       for (int t = 0; t < ks; ++t) {
         const int q0 = 32 * t + 8 * g;
-        q2_u32x4 aq = lr_afrag(a.lr_t, crow, a.r, q0, lr_vec != 0);
-        if (c >= M) aq = q2_u32x4{0u, 0u, 0u, 0u};
-        s = mfma(aq, lr_bfrag(a.lr_b, nc, a.r, q0, lr_vec != 0), s);
+        s = mfma(lr_afrag(a.lr_t, crow, a.r, q0, lr_vec != 0), lr_bfrag(a.lr_b, nc, a.r, q0, lr_vec != 0), s);
       }
     }
     if (n < a.N) {
@@ -538,8 +587,11 @@ template <int FMT>
 static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   const int64_t KB = a.K / BLOCK_K;
   const int M = (int)a.M;
-  int64_t cb = GEMV_X_BUDGET / (M * 256 + 16 + 64);
-  if (cb > (int64_t)GEMV_WAVES * GEMV_QMAX) cb = (int64_t)GEMV_WAVES * GEMV_QMAX;
+  // blocks staged per chunk: at most 256 (row, block) pairs of activations, and
+  // at most QMAX blocks per wave
+  const int qmax = KB <= (int64_t)GEMV_WAVES * 4 ? 4 : 12;
+  int64_t cb = GEMV_X_ROWBLOCKS / M;
+  if (cb > (int64_t)GEMV_WAVES * qmax) cb = (int64_t)GEMV_WAVES * qmax;
   if (cb > KB) cb = KB;
   if (cb < 1) cb = 1;
   size_t bytes = (size_t)M * (cb * 64 + 4) * 4 + (size_t)cb * 16 * 4;
@@ -547,8 +599,12 @@ static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   if (bytes < red) bytes = red;
   const int64_t grid = (a.N + 15) / 16;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemv_kernel<FMT>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a, (int)cb,
-                     lowrank_vec(a));
+  if (qmax == 4)
+    hipLaunchKernelGGL((gemv_kernel<FMT, 4>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
+                       (int)cb, lowrank_vec(a));
+  else
+    hipLaunchKernelGGL((gemv_kernel<FMT, 12>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
+                       (int)cb, lowrank_vec(a));
   return hipGetLastError();
 }
 
