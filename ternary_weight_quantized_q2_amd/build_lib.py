@@ -44,9 +44,9 @@ def build(verbose=True, out=LIB, srcs=None):
     srcs = srcs or sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(_compile, srcs))
-    for _, out in results:
-        if out.strip() and verbose:
-            print(out, file=sys.stderr)
+    for _, log in results:
+        if log.strip() and verbose:
+            print(log, file=sys.stderr)
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
     r = subprocess.run(cmd, capture_output=True, text=True)
