@@ -22,6 +22,9 @@
 #include "q2_internal.h"
 
 namespace q2dev {
+#ifndef SCHED_FENCE
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#endif
 
 template <int FMT> struct WFmt;
 template <> struct WFmt<0> {           // Q2_0: 32 bytes of codes per row and block
@@ -242,17 +245,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       zc[j] = z[j];
     }
     w_load(w, d, z, next_blk);
-    // Tile i's MFMAs are issued before tile i-1's rescale so the FMAs run in
+    // A fragments of tile i+1 are read from LDS while tile i's MFMAs run;
+    // tile i's MFMAs are issued before tile i-1's rescale so the FMAs run in
     // the matrix core's shadow; two temporaries keep everything in VGPRs.
     q2_f32x4 t0[NT], t1[NT];
-    auto tile = [&](int i, q2_f32x4 (&tmp)[NT]) {
-      const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[buf][16 * i + 4 * g]);
+    q2_u32x4 a0[4], a1[4];
+    q2_f32x4 s0, s1;
+    auto rd = [&](int i, q2_u32x4 (&av)[4], q2_f32x4& s4) {
+      s4 = *reinterpret_cast<const q2_f32x4*>(&ss[buf][16 * i + 4 * g]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const q2_u32x4 av = *reinterpret_cast<const q2_u32x4*>(&xs[buf][(16 * i + c) * XSTRIDE + 16 * g + 4 * t]);
+      for (int t = 0; t < 4; ++t)
+        av[t] = *reinterpret_cast<const q2_u32x4*>(&xs[buf][(16 * i + c) * XSTRIDE + 16 * g + 4 * t]);
+    };
+    auto tile = [&](const q2_u32x4 (&av)[4], q2_f32x4 s4, q2_f32x4 (&tmp)[NT]) {
 #pragma unroll
-        for (int j = 0; j < NT; ++j) tmp[j] = mfma(av, bf[j][t], t == 0 ? block_cinit<FMT>(s4, zc[j]) : tmp[j]);
-      }
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) tmp[j] = mfma(av[t], bf[j][t], t == 0 ? block_cinit<FMT>(s4, zc[j]) : tmp[j]);
     };
     auto rescale = [&](int i, const q2_f32x4 (&tmp)[NT]) {
 #pragma unroll
@@ -260,16 +269,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(dc[j], tmp[j][e], acc[i][j][e]);
     };
+    rd(0, a0, s0);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       if (i & 1) {
-        tile(i, t1);
+        if (i + 1 < MT) rd(i + 1, a0, s0);
+        tile(a1, s1, t1);
         rescale(i - 1, t0);
       } else {
-        tile(i, t0);
+        if (i + 1 < MT) rd(i + 1, a1, s1);
+        tile(a0, s0, t0);
         if (i > 0) rescale(i - 1, t1);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      SCHED_FENCE();
     }
     if ((MT - 1) & 1) rescale(MT - 1, t1);
     else rescale(MT - 1, t0);
@@ -346,8 +358,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 // ============================================================================
 // GEMV, M <= 16
 // ============================================================================
-constexpr int GEMV_WAVES = 8;
-constexpr int GEMV_XQ = 4;                        // 16-activation staging chunks per thread per chunk of K
+#ifndef Q2_GEMV_WAVES
+#define Q2_GEMV_WAVES 8
+#endif
+constexpr int GEMV_WAVES = Q2_GEMV_WAVES;
+constexpr int GEMV_XQ = 2048 / (GEMV_WAVES * 64);   // 16-activation staging chunks per thread per chunk of K
 constexpr int GEMV_X_ROWBLOCKS = 256;             // (row, block) pairs staged per chunk: 64 KB of LDS
 
 template <int FMT, int QMAX>
@@ -380,11 +395,12 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
     uint32_t nx[GEMV_XQ][8];
 #pragma unroll
     for (int u = 0; u < GEMV_XQ; ++u) {
-      int idx = tid + u * GEMV_WAVES * 64;
-      idx = idx < nchunks ? idx : nchunks - 1;
-      const int row = idx / (nb * 8);
-      const int rem = idx - row * nb * 8;
-      load_x16(a.x, row, K, (cb0 + (rem >> 3)) * BLOCK_K + (rem & 7) * 16, nx[u]);
+      const int idx = tid + u * GEMV_WAVES * 64;
+      if (idx < nchunks) {                       // masked lanes issue no memory traffic
+        const int row = idx / (nb * 8);
+        const int rem = idx - row * nb * 8;
+        load_x16(a.x, row, K, (cb0 + (rem >> 3)) * BLOCK_K + (rem & 7) * 16, nx[u]);
+      }
     }
     // then every weight load of this wave's share of the chunk
     uint32_t wq[QMAX][DW];
@@ -589,7 +605,7 @@ static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   const int M = (int)a.M;
   // blocks staged per chunk: at most 256 (row, block) pairs of activations, and
   // at most QMAX blocks per wave
-  const int qmax = KB <= (int64_t)GEMV_WAVES * 4 ? 4 : 12;
+  const int qmax = KB <= (int64_t)GEMV_WAVES * 4 ? 4 : (KB <= (int64_t)GEMV_WAVES * 8 ? 8 : 12);
   int64_t cb = GEMV_X_ROWBLOCKS / M;
   if (cb > (int64_t)GEMV_WAVES * qmax) cb = (int64_t)GEMV_WAVES * qmax;
   if (cb > KB) cb = KB;
@@ -601,6 +617,9 @@ static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (qmax == 4)
     hipLaunchKernelGGL((gemv_kernel<FMT, 4>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
+                       (int)cb, lowrank_vec(a));
+  else if (qmax == 8)
+    hipLaunchKernelGGL((gemv_kernel<FMT, 8>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
                        (int)cb, lowrank_vec(a));
   else
     hipLaunchKernelGGL((gemv_kernel<FMT, 12>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
