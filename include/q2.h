@@ -110,7 +110,7 @@ size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r);
  * 4, 32 and 64 appear there and in "Two and four steps").
  *   A_f16      u16 [r, K] f16                                   (in)
  *   B_f16      u16 [N, r] f16                                   (in)
- *   r          rank, >= 0; r == 0 is exactly q2_linear
+ *   r          rank, 0 <= r <= 65535; r == 0 is exactly q2_linear
  *   workspace  device scratch of >= q2_lowrank_workspace_bytes(M, r) bytes,
  *              256-byte aligned, owned by the caller; overwritten.
  * x A^T is computed once per call (into the workspace) and B (x A^T) is

@@ -176,7 +176,7 @@ int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint1
   int st = check_sizes(M, N, K);
   if (st) return st;
   if (r < 0) return fail(Q2_ERR_ARG, "negative rank r=%lld", (long long)r);
-  if (r > (1 << 20)) return fail(Q2_ERR_ARG, "rank r=%lld too large", (long long)r);
+  if (r > 65535) return fail(Q2_ERR_ARG, "rank r=%lld too large (at most 65535)", (long long)r);
   if (r == 0) return q2_linear(x_bf16, packed, scales_f16, y, M, N, K, stream);
   if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
       (st = check_ptr(packed, N > 0 && K > 0, 16, "packed")) ||

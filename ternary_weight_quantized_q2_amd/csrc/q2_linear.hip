@@ -169,7 +169,12 @@ __device__ __forceinline__ q2_u32x4 lr_bfrag(const uint16_t* B, int64_t n, int r
 // ============================================================================
 constexpr int XSTRIDE = 68;   // dwords per staged row-block: 64 pair dwords + 4 pad (bank spread)
 
-template <int FMT, int BM, int BN>
+// With LR, the workgroup's rows of the low-rank limbs x A^T and its columns of B
+// (split into bf16 hi and lo) are copied into LDS in the prologue, so the
+// epilogue's extra MFMA steps never wait on global memory (r <= LR_RMAX, r % 8 == 0).
+constexpr int LR_RMAX = 64;
+
+template <int FMT, int BM, int BN, bool LR>
 __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, int lr_vec) {
   constexpr int MT = BM / 16;            // 16-row tiles per wave
   constexpr int NT = BN / 64;            // 16-column tiles per wave (4 waves along N)
@@ -179,6 +184,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 
   __shared__ __align__(16) uint32_t xs[2][BM * XSTRIDE];
   __shared__ __align__(16) float ss[2][BM];
+  constexpr int LRM = LR ? BM : 1, LRN = LR ? BN : 1;
+  __shared__ __align__(16) uint16_t lt[LRM][2 * LR_RMAX];
+  __shared__ __align__(16) uint16_t lbh[LRN][LR_RMAX], lbl[LRN][LR_RMAX];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -287,6 +295,36 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
     else rescale(MT - 1, t0);
   };
 
+  if constexpr (LR) {
+    // copy the limbs of this tile's rows and the hi/lo split of its B columns
+    const int r = a.r;
+    const int tch = 2 * r / 8, bch = r / 8;               // 16-byte chunks per row
+    for (int idx = tid; idx < BM * tch; idx += 256) {
+      const int row = idx / tch, ch = idx - row * tch;
+      int64_t gr = m0 + row;
+      gr = gr < M ? gr : M - 1;
+      *reinterpret_cast<q2_u32x4*>(&lt[row][ch * 8]) = *reinterpret_cast<const q2_u32x4*>(a.lr_t + gr * 2 * r + ch * 8);
+    }
+    for (int idx = tid; idx < BN * bch; idx += 256) {
+      const int col = idx / bch, ch = idx - col * bch;
+      int64_t gn = (int64_t)tn * BN + col;
+      gn = gn < a.N ? gn : a.N - 1;
+      const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(a.lr_b + gn * r + ch * 8);
+      q2_u32x4 hv, lv;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint16_t h0, l0, h1, l1;
+        f16_split_bf16((uint16_t)(v[d] & 0xFFFFu), h0, l0);
+        f16_split_bf16((uint16_t)(v[d] >> 16), h1, l1);
+        hv[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lv[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      *reinterpret_cast<q2_u32x4*>(&lbh[col][ch * 8]) = hv;
+      *reinterpret_cast<q2_u32x4*>(&lbl[col][ch * 8]) = lv;
+    }
+    if (KB == 0) __syncthreads();
+  }
+
   if (KB > 0) {
     uint32_t xA[CPT][8], xB[CPT][8];
     uint32_t wA[NT][DW], wB[NT][DW];
@@ -321,7 +359,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][e] *= fin;
 
-  if (a.r > 0) {
+  if (LR) {
+    const int r = a.r;
+    const int ks = (3 * r + 31) / 32;
+    for (int t = 0; t < ks; ++t) {
+      const int q0 = 32 * t + 8 * g;
+      const bool live = q0 < 3 * r;
+      const int part = q0 / r, jj = q0 - part * r;
+      q2_u32x4 bq[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int col = wv * (BN / 4) + 16 * j + c;
+        bq[j] = live ? *reinterpret_cast<const q2_u32x4*>(part == 1 ? &lbl[col][jj] : &lbh[col][jj])
+                     : q2_u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const q2_u32x4 aq = live ? *reinterpret_cast<const q2_u32x4*>(&lt[16 * i + c][(part == 2 ? r : 0) + jj])
+                                 : q2_u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
+      }
+    }
+  } else if (a.r > 0) {
     const int ks = (3 * a.r + 31) / 32;
     for (int t = 0; t < ks; ++t) {
       const int q0 = 32 * t + 8 * g;
@@ -363,33 +423,59 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 #endif
 constexpr int GEMV_WAVES = Q2_GEMV_WAVES;
 constexpr int GEMV_XQ = 2048 / (GEMV_WAVES * 64);   // 16-activation staging chunks per thread per chunk of K
-constexpr int GEMV_X_ROWBLOCKS = 256;             // (row, block) pairs staged per chunk: 64 KB of LDS
+constexpr int GEMV_X_BYTES = 40 * 1024;          // LDS for staged activations and block sums per chunk
 
+// A unit (16 weight rows x 4 consecutive 128-blocks) is loaded with quad-coalesced
+// accesses: lane l reads the 32 bytes of block (l & 3) of row (l >> 2), so four
+// consecutive lanes cover one row's 128 contiguous bytes.  It is then
+// transposed through a per-wave LDS tile into the matrix-core layout, where
+// lane (c, g) needs dwords 2g, 2g+1 of each block of row c.
 template <int FMT, int QMAX>
 __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int cb, int lr_vec) {
-  constexpr int DW = WFmt<FMT>::LANE_DW;
+  constexpr int DW = WFmt<FMT>::LANE_DW;          // dwords per lane per block in the MFMA layout
+  constexpr int BBYTES = WFmt<FMT>::BLOCK_BYTES;  // 32 (2-bit) or 64 (4-bit)
+  constexpr int UDW = 16 * 4 * BBYTES / 4;        // dwords per unit
   extern __shared__ __align__(16) uint32_t smem[];
   const int M = (int)a.M;
-  const int rs = cb * 64 + 4;                     // dwords per staged row
+  const int rs = cb * 64 + 4;                     // dwords per staged activation row
   uint32_t* xs = smem;
-  float* ss = reinterpret_cast<float*>(smem + M * rs);   // [cb][16]
+  float* ss = reinterpret_cast<float*>(smem + M * rs);   // [cb][16] pre-scaled block sums
+  uint32_t* ws = smem + M * rs + cb * 16;                // per wave: one unit of codes, then its scales
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int64_t n = (int64_t)blockIdx.x * 16 + c;        // weight row of this lane's MFMA column
-  const int64_t nc = n < a.N ? n : a.N - 1;              // rows past N recompute row N-1, never stored
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n = n0 + c;                              // weight row of this lane's MFMA column
   const int64_t K = a.K, KB = K / BLOCK_K;
   const int crow = c < M ? c : M - 1;                    // activation rows past M duplicate row M-1
   const DecodeConsts kc = (FMT == 0) ? q2_consts() : q4_consts();
-  const uint8_t* wbase = a.w + nc * ((FMT == 0) ? K / 4 : K / 2) + g * DW * 4;
-  const uint16_t* sbase = a.s + nc * KB;
-  const uint16_t* zbase = (FMT == 1) ? a.z + nc * KB : nullptr;
+  // loader layout
+  const int lrow = lane >> 2, lblk = lane & 3;
+  int64_t ln = n0 + lrow;
+  ln = ln < a.N ? ln : a.N - 1;                          // rows past N reload row N-1, never stored
+  const uint8_t* wrow = a.w + ln * ((FMT == 0) ? K / 4 : K / 2) + lblk * BBYTES;
+  const uint16_t* srow = a.s + ln * KB + lblk;
+  const uint16_t* zrow = (FMT == 1) ? a.z + ln * KB + lblk : nullptr;
+  uint32_t* wt = ws + wv * (UDW + 64);                  // this wave's transpose tile
 
   q2_f32x4 acc = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.r > 0 && wv == GEMV_WAVES - 1) {
+    // The last wave adds the low-rank term first, divided by the final scale
+    // factor (a power of two, so exactly), while the other waves stream codes.
+    const int64_t nc = n < a.N ? n : a.N - 1;
+    const int ks = (3 * a.r + 31) / 32;
+    for (int t = 0; t < ks; ++t) {
+      const int q0 = 32 * t + 8 * g;
+      acc = mfma(lr_afrag(a.lr_t, crow, a.r, q0, lr_vec != 0), lr_bfrag(a.lr_b, nc, a.r, q0, lr_vec != 0), acc);
+    }
+    const float inv = (FMT == 0) ? 0.25f : 0.0625f;
+    acc = q2_f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  }
 
   for (int64_t cb0 = 0; cb0 < KB; cb0 += cb) {
     const int nb = (int)((KB - cb0) < cb ? (KB - cb0) : cb);
-    const int mine = (nb - wv + GEMV_WAVES - 1) / GEMV_WAVES;   // blocks wv, wv + 8, ... of this chunk
+    const int nunits = (nb + 3) / 4;
+    const int mine = (nunits - wv + GEMV_WAVES - 1) / GEMV_WAVES;   // units wv, wv + WAVES, ...
     const int nchunks = M * nb * 8;
     // activation loads first, so that staging waits on them only
     uint32_t nx[GEMV_XQ][8];
@@ -402,24 +488,21 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
         load_x16(a.x, row, K, (cb0 + (rem >> 3)) * BLOCK_K + (rem & 7) * 16, nx[u]);
       }
     }
-    // then every weight load of this wave's share of the chunk
-    uint32_t wq[QMAX][DW];
-    float dq[QMAX], zq[QMAX];
+    // then every weight unit of this wave's share of the chunk, coalesced
+    q2_u32x4 wq[QMAX][BBYTES / 16];
+    uint32_t sq[QMAX], zq[QMAX];
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
-      int bl = wv + GEMV_WAVES * q;
-      bl = bl < nb ? bl : nb - 1;
-      const uint32_t blk = (uint32_t)(cb0 + bl);
-      const uint8_t* p = wbase + (uint64_t)blk * WFmt<FMT>::BLOCK_BYTES;
-      if constexpr (DW == 2) {
-        const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(p);
-        wq[q][0] = v[0]; wq[q][1] = v[1];
-      } else {
-        const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(p);
-        wq[q][0] = v[0]; wq[q][1] = v[1]; wq[q][2] = v[2]; wq[q][3] = v[3];
-      }
-      dq[q] = f16_to_f32(sbase[blk]);
-      zq[q] = (FMT == 1) ? f16_to_f32(zbase[blk]) : 0.f;
+      int unit = wv + GEMV_WAVES * q;
+      unit = unit < nunits ? unit : nunits - 1;
+      int blk = unit * 4 + lblk;
+      blk = blk < nb ? blk : nb - 1;                   // a partial last unit re-reads a valid block
+      const int64_t gb = cb0 + blk;
+      const q2_u32x4* p = reinterpret_cast<const q2_u32x4*>(wrow + (gb - lblk) * BBYTES);
+#pragma unroll
+      for (int h = 0; h < BBYTES / 16; ++h) wq[q][h] = p[h];
+      sq[q] = srow[gb - lblk];
+      zq[q] = (FMT == 1) ? zrow[gb - lblk] : 0u;
     }
     // stage the activations in the decoder's pair order, with pre-scaled block sums
 #pragma unroll
@@ -446,16 +529,45 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
       if (q < mine) {
-        const int bl = wv + GEMV_WAVES * q;
-        q2_u32x4 bf[4];
-        decode_block<FMT>(wq[q], bf, kc);
-        const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[bl * 16 + 4 * g]);
-        q2_f32x4 tmp = block_cinit<FMT>(s4, zq[q]);
+        const int unit = wv + GEMV_WAVES * q;
+        // transpose through the wave's own LDS tile: codes [row][blk][dwords],
+        // then scales and zero points [row][blk] as u16 (one wave, in order)
+        uint32_t* t = wt;
+        {
+          q2_u32x4* dst = reinterpret_cast<q2_u32x4*>(t + (lrow * 4 + lblk) * (BBYTES / 4));
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          tmp = mfma(*reinterpret_cast<const q2_u32x4*>(&xs[crow * rs + bl * 64 + 16 * g + 4 * t]), bf[t], tmp);
+          for (int h = 0; h < BBYTES / 16; ++h) dst[h] = wq[q][h];
+          uint16_t* stw = reinterpret_cast<uint16_t*>(t + UDW);
+          stw[lrow * 4 + lblk] = (uint16_t)sq[q];
+          if (FMT == 1) stw[64 + lrow * 4 + lblk] = (uint16_t)zq[q];
+        }
+        const uint16_t* st = reinterpret_cast<const uint16_t*>(t + UDW);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(dq[q], tmp[e], acc[e]);
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const int bl = unit * 4 + b4;
+          if (bl < nb) {
+            uint32_t w[DW];
+            if constexpr (DW == 2) {
+              const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(t + (c * 4 + b4) * 8 + 2 * g);
+              w[0] = v[0]; w[1] = v[1];
+            } else {
+              const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(t + (c * 4 + b4) * 16 + 4 * g);
+              w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+            }
+            const float dsc = f16_to_f32(st[c * 4 + b4]);
+            const float zp = (FMT == 1) ? f16_to_f32(st[64 + c * 4 + b4]) : 0.f;
+            q2_u32x4 bf[4];
+            decode_block<FMT>(w, bf, kc);
+            const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[bl * 16 + 4 * g]);
+            q2_f32x4 tmp = block_cinit<FMT>(s4, zp);
+#pragma unroll
+            for (int tk = 0; tk < 4; ++tk)
+              tmp = mfma(*reinterpret_cast<const q2_u32x4*>(&xs[crow * rs + bl * 64 + 16 * g + 4 * tk]), bf[tk], tmp);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(dsc, tmp[e], acc[e]);
+          }
+        }
+        __builtin_amdgcn_wave_barrier();              // tile reads done before the next unit's writes
       }
     }
     __syncthreads();
@@ -474,13 +586,6 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
     }
     const float fin = (FMT == 0) ? 4.f : 16.f;
     s = q2_f32x4{s[0] * fin, s[1] * fin, s[2] * fin, s[3] * fin};
-    if (a.r > 0) {
-      const int ks = (3 * a.r + 31) / 32;
-      for (int t = 0; t < ks; ++t) {
-        const int q0 = 32 * t + 8 * g;
-        s = mfma(lr_afrag(a.lr_t, crow, a.r, q0, lr_vec != 0), lr_bfrag(a.lr_b, nc, a.r, q0, lr_vec != 0), s);
-      }
-    }
     if (n < a.N) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -494,9 +599,12 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
 // ============================================================================
 // x A^T for the low-rank branch: bf16 limbs [M, 2r] = (hi | lo)
 // ============================================================================
-constexpr int LR_WAVES = 16;
-constexpr int LR_UNROLL = 2;     // k-steps whose loads are issued together
+constexpr int LR_WAVES = 8;
+constexpr int LR_UNROLL = 12;    // k-steps per wave whose loads are issued together
 
+// A workgroup owns 16 rows of x and 16 columns of A (one MFMA tile); its waves
+// split K in 32-wide steps, issue all their loads first, and are reduced in a
+// fixed order.  A (f16) is split exactly into bf16 hi + lo, two MFMAs per step.
 __global__ __launch_bounds__(LR_WAVES * 64) void lowrank_t_kernel(const uint16_t* x, const uint16_t* A, uint16_t* tl,
                                                                   int64_t M, int64_t K, int r) {
   __shared__ __align__(16) q2_f32x4 red[LR_WAVES][64];
@@ -504,80 +612,60 @@ __global__ __launch_bounds__(LR_WAVES * 64) void lowrank_t_kernel(const uint16_t
   const int c = lane & 15, g = lane >> 4;
   int64_t m = (int64_t)blockIdx.x * 16 + c;                // A-operand row of this lane
   m = m < M ? m : M - 1;
-  const int col0 = blockIdx.y * 64;
-  const int ntl = (r - col0 + 15) / 16 < 4 ? (r - col0 + 15) / 16 : 4;   // live 16-column tiles
+  int col = blockIdx.y * 16 + c;                           // B-operand column (row of A)
+  col = col < r ? col : r - 1;
   const int64_t KS = K / 32;
-  q2_f32x4 acc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
-  int colc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = col0 + 16 * j + c;
-    colc[j] = col < r ? col : r - 1;
-  }
-
+  q2_f32x4 acc = q2_f32x4{0.f, 0.f, 0.f, 0.f};
   for (int64_t s0 = wv; s0 < KS; s0 += (int64_t)LR_WAVES * LR_UNROLL) {
-    q2_u32x4 av[LR_UNROLL], bv[LR_UNROLL][4];
+    q2_u32x4 av[LR_UNROLL], bv[LR_UNROLL];
 #pragma unroll
     for (int u = 0; u < LR_UNROLL; ++u) {
       int64_t s = s0 + (int64_t)LR_WAVES * u;
       s = s < KS ? s : KS - 1;
       const int64_t k0 = s * 32 + 8 * g;
       av[u] = *reinterpret_cast<const q2_u32x4*>(x + m * K + k0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < ntl) bv[u][j] = *reinterpret_cast<const q2_u32x4*>(A + (int64_t)colc[j] * K + k0);
+      bv[u] = *reinterpret_cast<const q2_u32x4*>(A + (int64_t)col * K + k0);
     }
 #pragma unroll
     for (int u = 0; u < LR_UNROLL; ++u) {
       if (s0 + (int64_t)LR_WAVES * u < KS) {
+        q2_u32x4 bh, bl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (j < ntl) {
-            q2_u32x4 bh, bl;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              uint16_t h0, l0, h1, l1;
-              f16_split_bf16((uint16_t)(bv[u][j][d] & 0xFFFFu), h0, l0);
-              f16_split_bf16((uint16_t)(bv[u][j][d] >> 16), h1, l1);
-              bh[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-              bl[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-            }
-            acc[j] = mfma(av[u], bh, acc[j]);
-            acc[j] = mfma(av[u], bl, acc[j]);
-          }
+        for (int d = 0; d < 4; ++d) {
+          uint16_t h0, l0, h1, l1;
+          f16_split_bf16((uint16_t)(bv[u][d] & 0xFFFFu), h0, l0);
+          f16_split_bf16((uint16_t)(bv[u][d] >> 16), h1, l1);
+          bh[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          bl[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
+        acc = mfma(av[u], bh, acc);
+        acc = mfma(av[u], bl, acc);
       }
     }
   }
-  for (int j = 0; j < 4; ++j) {
-    if (j >= ntl) break;
-    red[wv][lane] = acc[j];
-    __syncthreads();
-    if (wv == 0) {
-      q2_f32x4 sm = red[0][lane];
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    q2_f32x4 sm = red[0][lane];
 #pragma unroll
-      for (int w = 1; w < LR_WAVES; ++w) {
-        const q2_f32x4 o = red[w][lane];
-        sm = q2_f32x4{sm[0] + o[0], sm[1] + o[1], sm[2] + o[2], sm[3] + o[3]};
-      }
-      const int col = col0 + 16 * j + c;            // C layout: column = lane % 16
-      if (col < r) {
+    for (int w = 1; w < LR_WAVES; ++w) {
+      const q2_f32x4 o = red[w][lane];
+      sm = q2_f32x4{sm[0] + o[0], sm[1] + o[1], sm[2] + o[2], sm[3] + o[3]};
+    }
+    const int oc = blockIdx.y * 16 + c;                    // C layout: column = lane % 16
+    if (oc < r) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t row = (int64_t)blockIdx.x * 16 + 4 * g + e;
-          if (row < M) {
-            const float t = sm[e];
-            const uint16_t hi = f32_to_bf16_rn(t);
-            const uint16_t lo = f32_to_bf16_rn(t - bf16_to_f32(hi));
-            tl[row * 2 * r + col] = hi;
-            tl[row * 2 * r + r + col] = lo;
-          }
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = (int64_t)blockIdx.x * 16 + 4 * g + e;
+        if (row < M) {
+          const float t = sm[e];
+          const uint16_t hi = f32_to_bf16_rn(t);
+          const uint16_t lo = f32_to_bf16_rn(t - bf16_to_f32(hi));
+          tl[row * 2 * r + oc] = hi;
+          tl[row * 2 * r + r + oc] = lo;
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -594,8 +682,26 @@ static hipError_t run_gemm(const LinearArgs& a, hipStream_t stream) {
   const int64_t tiles_n = (a.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN>), dim3((unsigned)tiles), dim3(256), 0, stream, a, (int)tiles_m,
-                     lowrank_vec(a));
+  const int vec = lowrank_vec(a);
+  if (FMT == 0 && vec && a.r <= LR_RMAX)
+    hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, true>), dim3((unsigned)tiles), dim3(256), 0, stream, a, (int)tiles_m,
+                       vec);
+  else
+    hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, false>), dim3((unsigned)tiles), dim3(256), 0, stream, a,
+                       (int)tiles_m, vec);
+  return hipGetLastError();
+}
+
+template <int FMT, int QMAX>
+static hipError_t launch_gemv(const LinearArgs& a, int64_t cb, hipStream_t stream) {
+  constexpr int UDW = 16 * 4 * WFmt<FMT>::BLOCK_BYTES / 4;
+  size_t bytes = (size_t)a.M * (cb * 64 + 4) * 4 + (size_t)cb * 16 * 4 + (size_t)GEMV_WAVES * (UDW + 64) * 4;
+  const size_t red = (size_t)GEMV_WAVES * 64 * 16;
+  if (bytes < red) bytes = red;
+  const int64_t grid = (a.N + 15) / 16;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemv_kernel<FMT, QMAX>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
+                     (int)cb, lowrank_vec(a));
   return hipGetLastError();
 }
 
@@ -603,28 +709,17 @@ template <int FMT>
 static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   const int64_t KB = a.K / BLOCK_K;
   const int M = (int)a.M;
-  // blocks staged per chunk: at most 256 (row, block) pairs of activations, and
-  // at most QMAX blocks per wave
-  const int qmax = KB <= (int64_t)GEMV_WAVES * 4 ? 4 : (KB <= (int64_t)GEMV_WAVES * 8 ? 8 : 12);
-  int64_t cb = GEMV_X_ROWBLOCKS / M;
-  if (cb > (int64_t)GEMV_WAVES * qmax) cb = (int64_t)GEMV_WAVES * qmax;
+  // Blocks staged per chunk: activations within GEMV_X_BYTES of LDS, and at
+  // most QMAX four-block units per wave.
+  const int64_t units = (KB + 3) / 4;
+  const int qmax = units <= GEMV_WAVES ? 1 : (units <= 2 * GEMV_WAVES ? 2 : 3);
+  int64_t cb = GEMV_X_BYTES / (M * 256 + 64);
+  if (cb > (int64_t)GEMV_WAVES * qmax * 4) cb = (int64_t)GEMV_WAVES * qmax * 4;
   if (cb > KB) cb = KB;
   if (cb < 1) cb = 1;
-  size_t bytes = (size_t)M * (cb * 64 + 4) * 4 + (size_t)cb * 16 * 4;
-  const size_t red = (size_t)GEMV_WAVES * 64 * 16;
-  if (bytes < red) bytes = red;
-  const int64_t grid = (a.N + 15) / 16;
-  if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (qmax == 4)
-    hipLaunchKernelGGL((gemv_kernel<FMT, 4>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
-                       (int)cb, lowrank_vec(a));
-  else if (qmax == 8)
-    hipLaunchKernelGGL((gemv_kernel<FMT, 8>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
-                       (int)cb, lowrank_vec(a));
-  else
-    hipLaunchKernelGGL((gemv_kernel<FMT, 12>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
-                       (int)cb, lowrank_vec(a));
-  return hipGetLastError();
+  if (qmax == 1) return launch_gemv<FMT, 1>(a, cb, stream);
+  if (qmax == 2) return launch_gemv<FMT, 2>(a, cb, stream);
+  return launch_gemv<FMT, 3>(a, cb, stream);
 }
 
 template <int FMT>
@@ -648,7 +743,7 @@ hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, hipStream
 hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* tl, int64_t M, int64_t K, int r,
                             hipStream_t stream) {
   const int64_t gx = (M + 15) / 16;
-  const int gy = (r + 63) / 64;
+  const int gy = (r + 15) / 16;
   if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(lowrank_t_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(LR_WAVES * 64), 0, stream, x, A, tl, M,
                      K, r);
