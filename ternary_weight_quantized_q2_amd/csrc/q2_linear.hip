@@ -22,9 +22,6 @@
 #include "q2_internal.h"
 
 namespace q2dev {
-#ifndef SCHED_FENCE
-#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-#endif
 
 template <int FMT> struct WFmt;
 template <> struct WFmt<0> {           // Q2_0: 32 bytes of codes per row and block
@@ -289,7 +286,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
         tile(a0, s0, t0);
         if (i > 0) rescale(i - 1, t1);
       }
-      SCHED_FENCE();
     }
     if ((MT - 1) & 1) rescale(MT - 1, t1);
     else rescale(MT - 1, t0);
