@@ -90,7 +90,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="profiling mode: run warmup + steps eagerly and "
                     "print only the wall time (no graph, no per-call events)")
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
-                    "gemm_m1536, gemv_m1, lowrank_r32, q4_m128")
+                    "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -166,6 +166,11 @@ def main():
                       lambda xq=xq, P=P, S=S, Z=Z, yq=yq: q2.q4_linear(xq, P, S, Z, yq),
                       f"M={I.Q4_M} K={k} N={n}"))
 
+    if "copy_ref" in args.only.split(","):
+        # calibration for the HBM counters: a plain copy of known size (256 MiB read + 256 MiB written)
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        calls.append(("copy_ref", 0.0, float(src.numel()), lambda: dst.copy_(src), "copy 256 MiB"))
     if args.only:
         keep = set(args.only.split(","))
         calls = [c for c in calls if c[0] in keep]

@@ -292,31 +292,58 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
   };
 
   if constexpr (LR) {
-    // copy the limbs of this tile's rows and the hi/lo split of its B columns
+    // Copy the limbs of this tile's rows and the hi/lo split of its B columns:
+    // every load is issued first, then stored (r <= LR_RMAX so at most
+    // BM*16 and BN*8 16-byte chunks, i.e. CPT*2 and NT*2 per thread).
     const int r = a.r;
     const int tch = 2 * r / 8, bch = r / 8;               // 16-byte chunks per row
-    for (int idx = tid; idx < BM * tch; idx += 256) {
-      const int row = idx / tch, ch = idx - row * tch;
-      int64_t gr = m0 + row;
-      gr = gr < M ? gr : M - 1;
-      *reinterpret_cast<q2_u32x4*>(&lt[row][ch * 8]) = *reinterpret_cast<const q2_u32x4*>(a.lr_t + gr * 2 * r + ch * 8);
-    }
-    for (int idx = tid; idx < BN * bch; idx += 256) {
-      const int col = idx / bch, ch = idx - col * bch;
-      int64_t gn = (int64_t)tn * BN + col;
-      gn = gn < a.N ? gn : a.N - 1;
-      const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(a.lr_b + gn * r + ch * 8);
-      q2_u32x4 hv, lv;
+    constexpr int TQ = BM * (2 * LR_RMAX / 8) / 256, BQ = BN * (LR_RMAX / 8) / 256;
+    q2_u32x4 tv[TQ], bv[BQ];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint16_t h0, l0, h1, l1;
-        f16_split_bf16((uint16_t)(v[d] & 0xFFFFu), h0, l0);
-        f16_split_bf16((uint16_t)(v[d] >> 16), h1, l1);
-        hv[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lv[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    for (int u = 0; u < TQ; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < BM * tch) {
+        const int row = idx / tch, ch = idx - row * tch;
+        int64_t gr = m0 + row;
+        gr = gr < M ? gr : M - 1;
+        tv[u] = *reinterpret_cast<const q2_u32x4*>(a.lr_t + gr * 2 * r + ch * 8);
       }
-      *reinterpret_cast<q2_u32x4*>(&lbh[col][ch * 8]) = hv;
-      *reinterpret_cast<q2_u32x4*>(&lbl[col][ch * 8]) = lv;
+    }
+#pragma unroll
+    for (int u = 0; u < BQ; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < BN * bch) {
+        const int col = idx / bch, ch = idx - col * bch;
+        int64_t gn = (int64_t)tn * BN + col;
+        gn = gn < a.N ? gn : a.N - 1;
+        bv[u] = *reinterpret_cast<const q2_u32x4*>(a.lr_b + gn * r + ch * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TQ; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < BM * tch) {
+        const int row = idx / tch, ch = idx - row * tch;
+        *reinterpret_cast<q2_u32x4*>(&lt[row][ch * 8]) = tv[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < BQ; ++u) {
+      const int idx = tid + 256 * u;
+      if (idx < BN * bch) {
+        const int col = idx / bch, ch = idx - col * bch;
+        q2_u32x4 hv, lv;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint16_t h0, l0, h1, l1;
+          f16_split_bf16((uint16_t)(bv[u][d] & 0xFFFFu), h0, l0);
+          f16_split_bf16((uint16_t)(bv[u][d] >> 16), h1, l1);
+          hv[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          lv[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        *reinterpret_cast<q2_u32x4*>(&lbh[col][ch * 8]) = hv;
+        *reinterpret_cast<q2_u32x4*>(&lbl[col][ch * 8]) = lv;
+      }
     }
     if (KB == 0) __syncthreads();
   }
@@ -415,10 +442,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 // GEMV, M <= 16
 // ============================================================================
 #ifndef Q2_GEMV_WAVES
-#define Q2_GEMV_WAVES 8
+#define Q2_GEMV_WAVES 4
 #endif
 constexpr int GEMV_WAVES = Q2_GEMV_WAVES;
-constexpr int GEMV_XQ = 2048 / (GEMV_WAVES * 64);   // 16-activation staging chunks per thread per chunk of K
+constexpr int GEMV_XQ = 2;                        // 16-activation staging chunks per thread per pass
 constexpr int GEMV_X_BYTES = 40 * 1024;          // LDS for staged activations and block sums per chunk
 
 // A unit (16 weight rows x 4 consecutive 128-blocks) is loaded with quad-coalesced
@@ -473,18 +500,41 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
     const int nunits = (nb + 3) / 4;
     const int mine = (nunits - wv + GEMV_WAVES - 1) / GEMV_WAVES;   // units wv, wv + WAVES, ...
     const int nchunks = M * nb * 8;
-    // activation loads first, so that staging waits on them only
+    // activation loads of the first staging pass go out first, so that
+    // staging waits on them only; then every weight unit of this wave
+    constexpr int XP = GEMV_WAVES * 64 * GEMV_XQ;          // chunks per staging pass
     uint32_t nx[GEMV_XQ][8];
+    auto x_issue = [&](int base) {
 #pragma unroll
-    for (int u = 0; u < GEMV_XQ; ++u) {
-      const int idx = tid + u * GEMV_WAVES * 64;
-      if (idx < nchunks) {                       // masked lanes issue no memory traffic
+      for (int u = 0; u < GEMV_XQ; ++u) {
+        const int idx = base + tid + u * GEMV_WAVES * 64;
+        if (idx < nchunks) {                     // masked lanes issue no memory traffic
+          const int row = idx / (nb * 8);
+          const int rem = idx - row * nb * 8;
+          load_x16(a.x, row, K, (cb0 + (rem >> 3)) * BLOCK_K + (rem & 7) * 16, nx[u]);
+        }
+      }
+    };
+    auto x_stage = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < GEMV_XQ; ++u) {
+        const int idx = base + tid + u * GEMV_WAVES * 64;
+        if (base + u * GEMV_WAVES * 64 >= nchunks) break;   // uniform: no chunk left for any thread
         const int row = idx / (nb * 8);
         const int rem = idx - row * nb * 8;
-        load_x16(a.x, row, K, (cb0 + (rem >> 3)) * BLOCK_K + (rem & 7) * 16, nx[u]);
+        const int bl = rem >> 3, prt = rem & 7;
+        uint32_t pr[8];
+        stage_pairs<FMT>(nx[u], pr);
+        const float sm = sum8_lanes(bf16_sum16(nx[u]));
+        if (idx < nchunks) {
+          q2_u32x4* dst = reinterpret_cast<q2_u32x4*>(&xs[row * rs + bl * 64 + prt * 8]);
+          dst[0] = q2_u32x4{pr[0], pr[1], pr[2], pr[3]};
+          dst[1] = q2_u32x4{pr[4], pr[5], pr[6], pr[7]};
+          if (prt == 0) ss[bl * 16 + row] = sm * ((FMT == 0) ? -1.25f : -1.f);
+        }
       }
-    }
-    // then every weight unit of this wave's share of the chunk, coalesced
+    };
+    x_issue(0);
     q2_u32x4 wq[QMAX][BBYTES / 16];
     uint32_t sq[QMAX], zq[QMAX];
 #pragma unroll
@@ -500,23 +550,10 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
       sq[q] = srow[gb - lblk];
       zq[q] = (FMT == 1) ? zrow[gb - lblk] : 0u;
     }
-    // stage the activations in the decoder's pair order, with pre-scaled block sums
-#pragma unroll
-    for (int u = 0; u < GEMV_XQ; ++u) {
-      const int idx = tid + u * GEMV_WAVES * 64;
-      if (u * GEMV_WAVES * 64 >= nchunks) break;          // uniform: no chunk left for any thread
-      const int row = idx / (nb * 8);
-      const int rem = idx - row * nb * 8;
-      const int bl = rem >> 3, prt = rem & 7;
-      uint32_t pr[8];
-      stage_pairs<FMT>(nx[u], pr);
-      const float sm = sum8_lanes(bf16_sum16(nx[u]));
-      if (idx < nchunks) {
-        q2_u32x4* dst = reinterpret_cast<q2_u32x4*>(&xs[row * rs + bl * 64 + prt * 8]);
-        dst[0] = q2_u32x4{pr[0], pr[1], pr[2], pr[3]};
-        dst[1] = q2_u32x4{pr[4], pr[5], pr[6], pr[7]};
-        if (prt == 0) ss[bl * 16 + row] = sm * ((FMT == 0) ? -1.25f : -1.f);
-      }
+    x_stage(0);
+    for (int base = XP; base < nchunks; base += XP) {
+      x_issue(base);
+      x_stage(base);
     }
     for (int idx = tid; idx < nb * 16; idx += GEMV_WAVES * 64)
       if ((idx & 15) >= M) ss[idx] = 0.f;
@@ -708,14 +745,15 @@ static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   // Blocks staged per chunk: activations within GEMV_X_BYTES of LDS, and at
   // most QMAX four-block units per wave.
   const int64_t units = (KB + 3) / 4;
-  const int qmax = units <= GEMV_WAVES ? 1 : (units <= 2 * GEMV_WAVES ? 2 : 3);
+  const int qmax = units <= GEMV_WAVES ? 1 : units <= 2 * GEMV_WAVES ? 2 : units <= 3 * GEMV_WAVES ? 3 : 6;
   int64_t cb = GEMV_X_BYTES / (M * 256 + 64);
   if (cb > (int64_t)GEMV_WAVES * qmax * 4) cb = (int64_t)GEMV_WAVES * qmax * 4;
   if (cb > KB) cb = KB;
   if (cb < 1) cb = 1;
   if (qmax == 1) return launch_gemv<FMT, 1>(a, cb, stream);
   if (qmax == 2) return launch_gemv<FMT, 2>(a, cb, stream);
-  return launch_gemv<FMT, 3>(a, cb, stream);
+  if (qmax == 3) return launch_gemv<FMT, 3>(a, cb, stream);
+  return launch_gemv<FMT, 6>(a, cb, stream);
 }
 
 template <int FMT>
