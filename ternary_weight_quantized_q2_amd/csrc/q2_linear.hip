@@ -182,8 +182,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
   __shared__ __align__(16) uint32_t xs[2][BM * XSTRIDE];
   __shared__ __align__(16) float ss[2][BM];
   constexpr int LRM = LR ? BM : 1, LRN = LR ? BN : 1;
-  __shared__ __align__(16) uint16_t lt[LRM][2 * LR_RMAX];
-  __shared__ __align__(16) uint16_t lbh[LRN][LR_RMAX], lbl[LRN][LR_RMAX];
+  __shared__ __align__(16) uint16_t lt[LRM * 2 * LR_RMAX];   // limbs of the tile's rows, row stride 2r
+  __shared__ __align__(16) uint16_t lb[LRN * LR_RMAX];       // B (f16) of the tile's columns, row stride r
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -292,60 +292,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
   };
 
   if constexpr (LR) {
-    // Copy the limbs of this tile's rows and the hi/lo split of its B columns:
-    // every load is issued first, then stored (r <= LR_RMAX so at most
-    // BM*16 and BN*8 16-byte chunks, i.e. CPT*2 and NT*2 per thread).
+    // Copy the limbs of this tile's rows and its columns of B into LDS with
+    // direct global-to-LDS loads: asynchronous, no registers, waited for only
+    // before the epilogue.  Both copies are whole 64-lane instructions because
+    // r % 8 == 0 makes BM*2r/8 and BN*r/8 multiples of 64 for these tiles.
     const int r = a.r;
     const int tch = 2 * r / 8, bch = r / 8;               // 16-byte chunks per row
-    constexpr int TQ = BM * (2 * LR_RMAX / 8) / 256, BQ = BN * (LR_RMAX / 8) / 256;
-    q2_u32x4 tv[TQ], bv[BQ];
-#pragma unroll
-    for (int u = 0; u < TQ; ++u) {
-      const int idx = tid + 256 * u;
-      if (idx < BM * tch) {
-        const int row = idx / tch, ch = idx - row * tch;
-        int64_t gr = m0 + row;
-        gr = gr < M ? gr : M - 1;
-        tv[u] = *reinterpret_cast<const q2_u32x4*>(a.lr_t + gr * 2 * r + ch * 8);
-      }
+    for (int base = wv * 64; base < BM * tch; base += 256) {
+      const int idx = base + lane;
+      const int row = idx / tch, ch = idx - row * tch;
+      int64_t gr = m0 + row;
+      gr = gr < M ? gr : M - 1;
+      __builtin_amdgcn_global_load_lds(a.lr_t + gr * 2 * r + ch * 8,
+                                       (__attribute__((address_space(3))) void*)(lt + base * 8), 16, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < BQ; ++u) {
-      const int idx = tid + 256 * u;
-      if (idx < BN * bch) {
-        const int col = idx / bch, ch = idx - col * bch;
-        int64_t gn = (int64_t)tn * BN + col;
-        gn = gn < a.N ? gn : a.N - 1;
-        bv[u] = *reinterpret_cast<const q2_u32x4*>(a.lr_b + gn * r + ch * 8);
-      }
+    for (int base = wv * 64; base < BN * bch; base += 256) {
+      const int idx = base + lane;
+      const int col = idx / bch, ch = idx - col * bch;
+      int64_t gn = (int64_t)tn * BN + col;
+      gn = gn < a.N ? gn : a.N - 1;
+      __builtin_amdgcn_global_load_lds(a.lr_b + gn * r + ch * 8,
+                                       (__attribute__((address_space(3))) void*)(lb + base * 8), 16, 0, 0);
     }
-#pragma unroll
-    for (int u = 0; u < TQ; ++u) {
-      const int idx = tid + 256 * u;
-      if (idx < BM * tch) {
-        const int row = idx / tch, ch = idx - row * tch;
-        *reinterpret_cast<q2_u32x4*>(&lt[row][ch * 8]) = tv[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < BQ; ++u) {
-      const int idx = tid + 256 * u;
-      if (idx < BN * bch) {
-        const int col = idx / bch, ch = idx - col * bch;
-        q2_u32x4 hv, lv;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          uint16_t h0, l0, h1, l1;
-          f16_split_bf16((uint16_t)(bv[u][d] & 0xFFFFu), h0, l0);
-          f16_split_bf16((uint16_t)(bv[u][d] >> 16), h1, l1);
-          hv[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          lv[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        }
-        *reinterpret_cast<q2_u32x4*>(&lbh[col][ch * 8]) = hv;
-        *reinterpret_cast<q2_u32x4*>(&lbl[col][ch * 8]) = lv;
-      }
-    }
-    if (KB == 0) __syncthreads();
   }
 
   if (KB > 0) {
@@ -383,6 +351,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       for (int e = 0; e < 4; ++e) acc[i][j][e] *= fin;
 
   if (LR) {
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's global-to-LDS copies have landed
+    __syncthreads();                   // and every other wave's
     const int r = a.r;
     const int ks = (3 * r + 31) / 32;
     for (int t = 0; t < ks; ++t) {
@@ -393,12 +363,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const int col = wv * (BN / 4) + 16 * j + c;
-        bq[j] = live ? *reinterpret_cast<const q2_u32x4*>(part == 1 ? &lbl[col][jj] : &lbh[col][jj])
-                     : q2_u32x4{0u, 0u, 0u, 0u};
+        q2_u32x4 v = q2_u32x4{0u, 0u, 0u, 0u};
+        if (live) {
+          const q2_u32x4 raw = *reinterpret_cast<const q2_u32x4*>(&lb[col * r + jj]);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            uint16_t h0, l0, h1, l1;
+            f16_split_bf16((uint16_t)(raw[d] & 0xFFFFu), h0, l0);
+            f16_split_bf16((uint16_t)(raw[d] >> 16), h1, l1);
+            v[d] = (part == 1) ? ((uint32_t)l0 | ((uint32_t)l1 << 16)) : ((uint32_t)h0 | ((uint32_t)h1 << 16));
+          }
+        }
+        bq[j] = v;
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const q2_u32x4 aq = live ? *reinterpret_cast<const q2_u32x4*>(&lt[16 * i + c][(part == 2 ? r : 0) + jj])
+        const q2_u32x4 aq = live ? *reinterpret_cast<const q2_u32x4*>(&lt[(16 * i + c) * 2 * r + (part == 2 ? r : 0) + jj])
                                  : q2_u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
@@ -441,10 +421,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 // ============================================================================
 // GEMV, M <= 16
 // ============================================================================
-#ifndef Q2_GEMV_WAVES
-#define Q2_GEMV_WAVES 4
-#endif
-constexpr int GEMV_WAVES = Q2_GEMV_WAVES;
 constexpr int GEMV_XQ = 2;                        // 16-activation staging chunks per thread per pass
 constexpr int GEMV_X_BYTES = 40 * 1024;          // LDS for staged activations and block sums per chunk
 
@@ -453,7 +429,7 @@ constexpr int GEMV_X_BYTES = 40 * 1024;          // LDS for staged activations a
 // consecutive lanes cover one row's 128 contiguous bytes.  It is then
 // transposed through a per-wave LDS tile into the matrix-core layout, where
 // lane (c, g) needs dwords 2g, 2g+1 of each block of row c.
-template <int FMT, int QMAX>
+template <int FMT, int QMAX, int GEMV_WAVES>
 __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int cb, int lr_vec) {
   constexpr int DW = WFmt<FMT>::LANE_DW;          // dwords per lane per block in the MFMA layout
   constexpr int BBYTES = WFmt<FMT>::BLOCK_BYTES;  // 32 (2-bit) or 64 (4-bit)
@@ -725,35 +701,44 @@ static hipError_t run_gemm(const LinearArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int FMT, int QMAX>
+template <int FMT, int QMAX, int WAVES>
 static hipError_t launch_gemv(const LinearArgs& a, int64_t cb, hipStream_t stream) {
   constexpr int UDW = 16 * 4 * WFmt<FMT>::BLOCK_BYTES / 4;
-  size_t bytes = (size_t)a.M * (cb * 64 + 4) * 4 + (size_t)cb * 16 * 4 + (size_t)GEMV_WAVES * (UDW + 64) * 4;
-  const size_t red = (size_t)GEMV_WAVES * 64 * 16;
+  size_t bytes = (size_t)a.M * (cb * 64 + 4) * 4 + (size_t)cb * 16 * 4 + (size_t)WAVES * (UDW + 64) * 4;
+  const size_t red = (size_t)WAVES * 64 * 16;
   if (bytes < red) bytes = red;
   const int64_t grid = (a.N + 15) / 16;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemv_kernel<FMT, QMAX>), dim3((unsigned)grid), dim3(GEMV_WAVES * 64), bytes, stream, a,
+  hipLaunchKernelGGL((gemv_kernel<FMT, QMAX, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), bytes, stream, a,
                      (int)cb, lowrank_vec(a));
   return hipGetLastError();
 }
 
-template <int FMT>
-static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
+template <int FMT, int WAVES>
+static hipError_t run_gemv_w(const LinearArgs& a, hipStream_t stream) {
   const int64_t KB = a.K / BLOCK_K;
   const int M = (int)a.M;
   // Blocks staged per chunk: activations within GEMV_X_BYTES of LDS, and at
   // most QMAX four-block units per wave.
   const int64_t units = (KB + 3) / 4;
-  const int qmax = units <= GEMV_WAVES ? 1 : units <= 2 * GEMV_WAVES ? 2 : units <= 3 * GEMV_WAVES ? 3 : 6;
+  const int qmax = units <= WAVES ? 1 : units <= 2 * WAVES ? 2 : units <= 3 * WAVES ? 3 : 6;
   int64_t cb = GEMV_X_BYTES / (M * 256 + 64);
-  if (cb > (int64_t)GEMV_WAVES * qmax * 4) cb = (int64_t)GEMV_WAVES * qmax * 4;
+  if (cb > (int64_t)WAVES * qmax * 4) cb = (int64_t)WAVES * qmax * 4;
   if (cb > KB) cb = KB;
   if (cb < 1) cb = 1;
-  if (qmax == 1) return launch_gemv<FMT, 1>(a, cb, stream);
-  if (qmax == 2) return launch_gemv<FMT, 2>(a, cb, stream);
-  if (qmax == 3) return launch_gemv<FMT, 3>(a, cb, stream);
-  return launch_gemv<FMT, 6>(a, cb, stream);
+  if (qmax == 1) return launch_gemv<FMT, 1, WAVES>(a, cb, stream);
+  if (qmax == 2) return launch_gemv<FMT, 2, WAVES>(a, cb, stream);
+  if (qmax == 3) return launch_gemv<FMT, 3, WAVES>(a, cb, stream);
+  return launch_gemv<FMT, 6, WAVES>(a, cb, stream);
+}
+
+// Eight waves per workgroup while the grid fits in one dispatch round at two
+// workgroups per CU, four waves (four workgroups per CU) beyond that.
+template <int FMT>
+static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
+  const int64_t grid = (a.N + 15) / 16;
+  if (grid <= 384) return run_gemv_w<FMT, 8>(a, stream);
+  return run_gemv_w<FMT, 4>(a, stream);
 }
 
 template <int FMT>
