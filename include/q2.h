@@ -14,7 +14,8 @@
  * a plain pointer offset (same page, section "The GPU driver...").
  *
  * Conventions shared by every entry point:
- *  - Sizes are int64.  M, N, K, r >= 0; K must be a multiple of 128.  A call
+ *  - Sizes are int64.  M, N, K, r >= 0; K must be a multiple of 128, and at
+ *    most 2^24 for the linear entry points (Q2_ERR_SHAPE otherwise).  A call
  *    with M == 0 or N == 0 does nothing and returns Q2_OK; K == 0 writes
  *    zeros (an empty sum).  Pointers to buffers of zero bytes may be NULL.
  *  - All array pointers are device pointers; all arrays are dense row-major.

@@ -48,6 +48,13 @@ int check_sizes(int64_t M, int64_t N, int64_t K) {
   return Q2_OK;
 }
 
+// The linear kernels address one tile's activation rows and weight columns
+// with 32-bit offsets; K up to 2^24 keeps them in range for every tile shape.
+int check_linear_k(int64_t K) {
+  if (K > ((int64_t)1 << 24)) return fail(Q2_ERR_SHAPE, "K=%lld exceeds 16777216", (long long)K);
+  return Q2_OK;
+}
+
 std::atomic<int> g_arch_ok[64];
 
 int check_device() {
@@ -159,7 +166,7 @@ int q2_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K, uin
 int q2_linear(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16, float* y, int64_t M,
               int64_t N, int64_t K, hipStream_t stream) {
   int st = check_sizes(M, N, K);
-  if (st) return st;
+  if (st || (st = check_linear_k(K))) return st;
   if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
       (st = check_ptr(packed, N > 0 && K > 0, 16, "packed")) ||
       (st = check_ptr(scales_f16, N > 0 && K > 0, 2, "scales_f16")) ||
@@ -174,7 +181,7 @@ int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint1
                       const uint16_t* A_f16, const uint16_t* B_f16, int64_t r, float* y, int64_t M, int64_t N,
                       int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int st = check_sizes(M, N, K);
-  if (st) return st;
+  if (st || (st = check_linear_k(K))) return st;
   if (r < 0) return fail(Q2_ERR_ARG, "negative rank r=%lld", (long long)r);
   if (r > 65535) return fail(Q2_ERR_ARG, "rank r=%lld too large (at most 65535)", (long long)r);
   if (r == 0) return q2_linear(x_bf16, packed, scales_f16, y, M, N, K, stream);
@@ -200,7 +207,7 @@ int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint1
 int q4_linear(const uint16_t* x_bf16, const uint8_t* packed4, const uint16_t* scale_f16, const uint16_t* zero_f16,
               float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   int st = check_sizes(M, N, K);
-  if (st) return st;
+  if (st || (st = check_linear_k(K))) return st;
   if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
       (st = check_ptr(packed4, N > 0 && K > 0, 16, "packed4")) ||
       (st = check_ptr(scale_f16, N > 0 && K > 0, 2, "scale_f16")) ||

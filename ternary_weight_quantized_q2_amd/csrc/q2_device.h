@@ -98,6 +98,69 @@ __device__ __forceinline__ q2_u32x4 q4_bfrag(uint32_t w, DecodeConsts k) {
   return q2_u32x4{q4_pair<0>(w, k), q4_pair<1>(w, k), q4_pair<2>(w, k), q4_pair<3>(w, k)};
 }
 
+// ---- consecutive pairs -------------------------------------------------------
+// The GEMM reads its activation fragments as 8 consecutive x straight from
+// shared memory, so there a weight dword must hold two consecutive codes.
+// For 2-bit codes one byte permute copies the byte of four codes into bits
+// 8-15 of both 16-bit halves, and a packed 16-bit shift (different amount per
+// half) brings code 2p to the low half's bits 5-6 and code 2p+1 to the high
+// half's: 2.5 VALU ops per pair.  For 4-bit codes the even and odd nibbles are
+// separated once per dword, a byte permute pairs nibble 2p (low half) with
+// nibble 2p+1 (high half) and one shift-or lands both in bits 3-6.
+struct NatConsts {
+  uint32_t mask, one, sh01, sh23;
+};
+__device__ __forceinline__ NatConsts q2_nat_consts() {
+  NatConsts k;
+  asm("v_mov_b32 %0, 0x00600060" : "=v"(k.mask));
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(k.one));
+  asm("v_mov_b32 %0, 0x00050003" : "=v"(k.sh01));   // low half >> 3, high half >> 5
+  asm("v_mov_b32 %0, 0x00090007" : "=v"(k.sh23));   // low half >> 7, high half >> 9
+  return k;
+}
+__device__ __forceinline__ NatConsts q4_nat_consts() {
+  NatConsts k;
+  asm("v_mov_b32 %0, 0x0f0f0f0f" : "=v"(k.mask));
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(k.one));
+  k.sh01 = k.sh23 = 0;
+  return k;
+}
+
+// Independent shifts of the two 16-bit halves of v (amounts in the halves of sh).
+__device__ __forceinline__ uint32_t pk_shr16(uint32_t v, uint32_t sh) {
+  uint32_t r;
+  asm("v_pk_lshrrev_b16 %0, %1, %2" : "=v"(r) : "v"(sh), "v"(v));
+  return r;
+}
+
+// Byte B of w in bits 8-15 of both halves, zeros elsewhere (selector 0x0C = 0).
+template <int B>
+__device__ __forceinline__ uint32_t byte_to_halves(uint32_t w) {
+  return __builtin_amdgcn_perm(w, w, 0x000C000Cu | (B << 8) | (B << 24));
+}
+
+// B operand from 16-bit half H of a 2-bit codes dword (codes 8H .. 8H+7): dword
+// p holds bf16(1 + c/4) of codes 8H + 2p (low half) and 8H + 2p + 1 (high half).
+template <int H>
+__device__ __forceinline__ q2_u32x4 q2_bfrag_nat(uint32_t w, const NatConsts& k) {
+  const uint32_t u0 = byte_to_halves<2 * H>(w), u1 = byte_to_halves<2 * H + 1>(w);
+  return q2_u32x4{and_or(pk_shr16(u0, k.sh01), k.mask, k.one), and_or(pk_shr16(u0, k.sh23), k.mask, k.one),
+                  and_or(pk_shr16(u1, k.sh01), k.mask, k.one), and_or(pk_shr16(u1, k.sh23), k.mask, k.one)};
+}
+
+// B operand from a 4-bit codes dword (8 nibbles): dword p holds bf16(1 + q/16)
+// of nibbles 2p (low half) and 2p + 1 (high half).
+__device__ __forceinline__ q2_u32x4 q4_bfrag_nat(uint32_t w, const NatConsts& k) {
+  const uint32_t e = w & k.mask, o = (w >> 4) & k.mask;
+  q2_u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t t = __builtin_amdgcn_perm(o, e, 0x0C000C00u | (uint32_t)p | ((uint32_t)(p + 4) << 16));
+    r[p] = (t << 3) | k.one;
+  }
+  return r;
+}
+
 // ---- activation pair order -------------------------------------------------
 // nx[h] = (x[2h], x[2h+1]) for 16 consecutive x.  2-bit order: out[j] =
 // (x[j], x[j+8]) for j = 0..7.

@@ -164,72 +164,209 @@ __device__ __forceinline__ q2_u32x4 lr_bfrag(const uint16_t* B, int64_t n, int r
 // ============================================================================
 // GEMM, M > 16
 // ============================================================================
-constexpr int XSTRIDE = 68;   // dwords per staged row-block: 64 pair dwords + 4 pad (bank spread)
-
 // With LR, the workgroup's rows of the low-rank limbs x A^T and its columns of B
-// (split into bf16 hi and lo) are copied into LDS in the prologue, so the
-// epilogue's extra MFMA steps never wait on global memory (r <= LR_RMAX, r % 8 == 0).
+// are copied into LDS in the prologue, so the epilogue's extra MFMA steps never
+// wait on global memory (r <= LR_RMAX, r % 8 == 0).
 constexpr int LR_RMAX = 64;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all its LDS operations are done, then meet the other waves.  Unlike
+// __syncthreads this does not drain every outstanding load, so the
+// global-to-LDS copies of later blocks stay in flight across the barrier.
+// Vector-memory loads complete in issue order, so "at most N outstanding"
+// means everything issued before the last N has landed.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));   // vmcnt(N) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int FMT>
+__device__ __forceinline__ void decode_block_nat(const uint32_t (&w)[WFmt<FMT>::LANE_DW], q2_u32x4 (&bf)[4],
+                                                 const NatConsts& k) {
+  if constexpr (FMT == 0) {
+    bf[0] = q2_bfrag_nat<0>(w[0], k);
+    bf[1] = q2_bfrag_nat<1>(w[0], k);
+    bf[2] = q2_bfrag_nat<0>(w[1], k);
+    bf[3] = q2_bfrag_nat<1>(w[1], k);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) bf[t] = q4_bfrag_nat(w[t], k);
+  }
+}
+
+// A workgroup owns a BM x BN output tile; its four waves split it along N
+// (BM x BN/4 each), so every wave decodes only its own weight columns and the
+// activation tile in LDS is shared by all four.
+//
+// K-slot assignment of the 16x16x32 MFMA: in K step t of a 128-block, lane
+// group g covers k = 32g + 8t .. 32g + 8t + 7.  The activation fragment is then
+// one 16-byte chunk of a row (chunk 4g + t), and the lane's weight codes for
+// the whole block are 8 contiguous bytes (2-bit) or 16 (4-bit).
+//
+// Every operand moves HBM -> LDS with direct global-to-LDS copies (no
+// registers, no VALU): activations into a ring of XS block buffers, weight
+// codes, scales and zero points into a ring of 3.  Since the main loop issues
+// no other vector-memory loads, the only waits are the explicit ones in
+// stage_barrier.  Activation chunk q of row r is stored at position
+// q ^ (r & 15), so the 16 lanes of a fragment read (same chunk, 16 consecutive
+// rows) hit 16 different bank groups; weight units are swizzled the same way.
+// A scale or zero point is copied as the 4-byte word that holds it (aligned
+// down; the word never leaves the 16-byte granule of the value), so the copies
+// need no alignment beyond the element's.
+//
+// Per block the accumulator of each 16x16 tile starts at -1.25 * S (2-bit) or
+// -(1 + z/16) * S (4-bit), S the block's row sums of x.  S of block b+1 is
+// computed during block b with matrix-core steps against a constant B operand
+// (-1.25 resp. -1 in every element), split over the waves by 16-row tile, and
+// handed over in LDS.
 template <int FMT, int BM, int BN, bool LR>
 __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, int lr_vec) {
   constexpr int MT = BM / 16;            // 16-row tiles per wave
   constexpr int NT = BN / 64;            // 16-column tiles per wave (4 waves along N)
-  constexpr int CPT = BM / 32;           // 16-element staging chunks per thread per block
   constexpr int DW = WFmt<FMT>::LANE_DW;
-  static_assert(BM % 32 == 0 && BN % 64 == 0, "tile shape");
+  constexpr int BBYTES = WFmt<FMT>::BLOCK_BYTES;
+  constexpr int XS = LR ? 3 : 4;         // activation ring: b, b+1 (row sums), in-flight
+  constexpr int WS = 3;                  // weight ring: b, b+1, b+2
+  constexpr int XSTAGE = BM * 256;       // bytes per activation block
+  constexpr int CODE_BYTES = BN * BBYTES;
+  constexpr int WSTAGE = CODE_BYTES + ((FMT == 0) ? 1024 : 2048);   // codes + 256 scale [+ 256 zero] words
+  constexpr int XU = BM / 16;            // activation copies (16 B) per thread per block
+  constexpr int CU = (FMT == 0) ? BN / 32 : BN / 64;   // code copies per thread per block (4 B / 16 B)
+  constexpr int WU = CU + ((FMT == 0) ? 1 : 2);        // all weight copies per thread per block
+  static_assert(BM % 16 == 0 && BN % 64 == 0 && BN <= 256, "tile shape");
 
-  __shared__ __align__(16) uint32_t xs[2][BM * XSTRIDE];
-  __shared__ __align__(16) float ss[2][BM];
-  constexpr int LRM = LR ? BM : 1, LRN = LR ? BN : 1;
-  __shared__ __align__(16) uint16_t lt[LRM * 2 * LR_RMAX];   // limbs of the tile's rows, row stride 2r
-  __shared__ __align__(16) uint16_t lb[LRN * LR_RMAX];       // B (f16) of the tile's columns, row stride r
+  // One shared array carved by hand.  (With several LDS objects the compiler
+  // tracks the copies per object and drains them before every read of that
+  // object; the ordering here is explicit in stage_barrier instead.)
+  constexpr int LRM = LR ? BM : 0, LRN = LR ? BN : 0;
+  constexpr int OFF_W = XS * XSTAGE;
+  constexpr int OFF_S = OFF_W + WS * WSTAGE;
+  constexpr int OFF_LT = OFF_S + 2 * BM * 4;
+  constexpr int OFF_LB = OFF_LT + LRM * 2 * LR_RMAX * 2;
+  constexpr int SMEM = OFF_LB + LRN * LR_RMAX * 2;
+  __shared__ __align__(16) uint8_t smem[SMEM];
+  uint8_t* const xs = smem;
+  uint8_t* const wsm = smem + OFF_W;
+  float (*const ss)[BM] = reinterpret_cast<float (*)[BM]>(smem + OFF_S);
+  uint16_t* const lt = reinterpret_cast<uint16_t*>(smem + OFF_LT);   // limbs of the tile's rows, row stride 2r
+  uint16_t* const lb = reinterpret_cast<uint16_t*>(smem + OFF_LB);   // B (f16) of the tile's columns, row stride r
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int64_t m0 = (int64_t)tm * BM;
-  const int64_t nw = (int64_t)tn * BN + wv * (BN / 4);   // first row of W for this wave
-  const int64_t M = a.M, K = a.K, KB = K / BLOCK_K;
-  const DecodeConsts kc = (FMT == 0) ? q2_consts() : q4_consts();
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t nw = n0 + wv * (BN / 4);   // first row of W for this wave
+  const int64_t M = a.M, N = a.N, K = a.K, KB = K / BLOCK_K;
+  const int64_t row_bytes = (FMT == 0) ? K / 4 : K / 2;
+  const NatConsts kc = (FMT == 0) ? q2_nat_consts() : q4_nat_consts();
 
-  const int part = tid & 7;
-  const int row0 = tid >> 3;
-  int64_t xrow[CPT];
+  // ---- copy sources (byte offsets from the tile's block base; K <= 2^24 keeps
+  // them in 32 bits).  They are widened to 64 bits at the copy: with a 32-bit
+  // offset operand the host compilation pass drops the kernel's launch stub.
+  uint32_t xoff[XU];
 #pragma unroll
-  for (int q = 0; q < CPT; ++q) {
-    const int64_t r = m0 + row0 + 32 * q;
-    xrow[q] = r < M ? r : M - 1;
+  for (int u = 0; u < XU; ++u) {
+    const int pos = (u * 4 + wv) * 64 + lane;      // 16-byte chunk position in the stage
+    const int row = pos >> 4;
+    const int q = (pos & 15) ^ (row & 15);
+    const int64_t gr = (m0 + row < M) ? row : M - 1 - m0;
+    xoff[u] = (uint32_t)(gr * K * 2 + q * 16);
   }
-  int64_t wrow[NT];
+  uint32_t woff[CU];
+#pragma unroll
+  for (int v = 0; v < CU; ++v) {
+    const int pos = (v * 4 + wv) * 64 + lane;
+    int col, unit;
+    if constexpr (FMT == 0) {                      // 4-byte copies, 8 per column; 8-byte units swizzled
+      col = pos >> 3;
+      const int up = (pos & 7) >> 1;
+      unit = ((up ^ ((col >> 2) & 3)) << 3) | ((pos & 1) << 2);
+    } else {                                       // 16-byte copies, 4 per column, swizzled
+      col = pos >> 2;
+      unit = ((pos & 3) ^ ((col >> 1) & 3)) << 4;
+    }
+    const int64_t gc = (n0 + col < N) ? col : N - 1 - n0;
+    woff[v] = (uint32_t)(gc * row_bytes + unit);
+  }
+  // Scale / zero-point word of column wv*64 + lane of the tile (clamped).
+  int64_t sgc = wv * 64 + lane;
+  sgc = sgc < BN ? sgc : BN - 1;
+  sgc = (n0 + sgc < N) ? n0 + sgc : N - 1;
+  const int64_t s_idx = sgc * KB;                  // element index of the column's block-0 scale
+
+  // ---- read side: lane offsets within a stage
+  int aoff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) aoff[t] = c * 256 + (((4 * g + t) ^ c) << 4);
+  const int coff = (FMT == 0) ? c * 32 + ((g ^ ((c >> 2) & 3)) << 3) : c * 64 + ((g ^ ((c >> 1) & 3)) << 4);
+  // Which half of its word holds the scale (zero point) of this lane's column j at block 0.
+  uint32_t shalf = 0, zhalf = 0;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const int64_t r = nw + 16 * j + c;
-    wrow[j] = r < a.N ? r : a.N - 1;
+    int64_t r = nw + 16 * j + c;
+    r = r < N ? r : N - 1;
+    shalf |= (uint32_t)((((uintptr_t)(a.s + r * KB)) >> 1) & 1) << j;
+    if constexpr (FMT == 1) zhalf |= (uint32_t)((((uintptr_t)(a.z + r * KB)) >> 1) & 1) << j;
   }
 
-  auto x_load = [&](uint32_t (&xr)[CPT][8], int64_t blk) {
+  // Blocks past the end re-copy the last block into a buffer nobody reads, so
+  // every wave issues the same number of copies per block and the vmcnt
+  // arithmetic of stage_barrier stays exact.
+  auto x_issue = [&](int64_t blk, int stage) {
     blk = blk < KB ? blk : KB - 1;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + m0 * K + blk * BLOCK_K);
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) load_x16(a.x, xrow[q], K, blk * BLOCK_K + part * 16, xr[q]);
+    for (int u = 0; u < XU; ++u)
+      __builtin_amdgcn_global_load_lds(base + (uint64_t)xoff[u], (lds_void*)(smem + stage * XSTAGE + (u * 4 + wv) * 1024),
+                                       16, 0, 0);
   };
-  auto x_store = [&](const uint32_t (&xr)[CPT][8], int buf) {
+  auto w_issue = [&](int64_t blk, int stage) {
+    blk = blk < KB ? blk : KB - 1;
+    const uint8_t* base = a.w + n0 * row_bytes + blk * BBYTES;
+    const int dst = OFF_W + stage * WSTAGE;   // LDS copies must name the shared array itself
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int row = row0 + 32 * q;
-      uint32_t pr[8];
-      stage_pairs<FMT>(xr[q], pr);
-      q2_u32x4* dst = reinterpret_cast<q2_u32x4*>(&xs[buf][row * XSTRIDE + part * 8]);
-      dst[0] = q2_u32x4{pr[0], pr[1], pr[2], pr[3]};
-      dst[1] = q2_u32x4{pr[4], pr[5], pr[6], pr[7]};
-      const float sm = sum8_lanes(bf16_sum16(xr[q]));
-      if (part == 0) ss[buf][row] = sm * ((FMT == 0) ? -1.25f : -1.f);
+    for (int v = 0; v < CU; ++v) {
+      if constexpr (FMT == 0)
+        __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v], (lds_void*)(smem + dst + (v * 4 + wv) * 256), 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v], (lds_void*)(smem + dst + (v * 4 + wv) * 1024), 16, 0, 0);
+    }
+    // Byte offset of the aligned word holding element s_idx + blk (may start 2 bytes before it).
+    const int64_t si = 2 * (s_idx + blk);
+    const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.s);
+    __builtin_amdgcn_global_load_lds(sp + (si - (int64_t)(((uintptr_t)sp + si) & 3)),
+                                     (lds_void*)(smem + dst + CODE_BYTES + wv * 256), 4, 0, 0);
+    if constexpr (FMT == 1) {
+      const uint8_t* zp = reinterpret_cast<const uint8_t*>(a.z);
+      __builtin_amdgcn_global_load_lds(zp + (si - (int64_t)(((uintptr_t)zp + si) & 3)),
+                                       (lds_void*)(smem + dst + CODE_BYTES + 1024 + wv * 256), 4, 0, 0);
     }
   };
-  auto w_load = [&](uint32_t (&w)[NT][DW], float (&d)[NT], float (&z)[NT], int64_t blk) {
-    blk = blk < KB ? blk : KB - 1;
+  auto afrag = [&](const uint8_t* st, int i, int t) -> q2_u32x4 {
+    return *reinterpret_cast<const q2_u32x4*>(st + i * 4096 + aoff[t]);
+  };
+
+  // Row sums of the block in stage `st` for this wave's 16-row tiles (i = wv, wv + 4, ...).
+  const uint32_t sone = (FMT == 0) ? 0xBFA0BFA0u : 0xBF80BF80u;   // bf16 -1.25 / -1 pairs
+  const q2_u32x4 sones = q2_u32x4{sone, sone, sone, sone};
+  auto s_compute = [&](const uint8_t* st, int buf) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) load_wblock<FMT>(a, wrow[j], blk, g, w[j], d[j], z[j]);
+    for (int ii = 0; ii < (MT + 3) / 4; ++ii) {
+      const int i = wv + 4 * ii;
+      if (i < MT) {
+        q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s4 = mfma(afrag(st, i, t), sones, s4);
+        if (c == 0) *reinterpret_cast<q2_f32x4*>(&ss[buf][16 * i + 4 * g]) = s4;
+      }
+    }
   };
 
   q2_f32x4 acc[MT][NT];
@@ -238,18 +375,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One block: decode this wave's weights, refill their registers with the
-  // block two ahead, then run the MFMAs over the staged activations.
-  auto compute = [&](int buf, uint32_t (&w)[NT][DW], float (&d)[NT], float (&z)[NT], int64_t next_blk) {
+  // One block: decode this wave's weights from LDS, then run the MFMAs.
+  auto compute = [&](const uint8_t* st, const uint8_t* wst, const float* sb, int64_t blk) {
     q2_u32x4 bf[NT][4];
     float dc[NT], zc[NT];
+    const uint32_t par = (uint32_t)(blk & 1) ? 0xFFu : 0u;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      decode_block<FMT>(w[j], bf[j], kc);
-      dc[j] = d[j];
-      zc[j] = z[j];
+      const int col0 = wv * (BN / 4) + 16 * j;
+      uint32_t w[DW];
+      if constexpr (FMT == 0) {
+        const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(wst + col0 * 32 + coff);
+        w[0] = v[0]; w[1] = v[1];
+      } else {
+        const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(wst + col0 * 64 + coff);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+      }
+      decode_block_nat<FMT>(w, bf[j], kc);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(wst + CODE_BYTES + (col0 + c) * 4);
+      dc[j] = f16_to_f32((uint16_t)(sw >> ((((shalf ^ par) >> j) & 1) * 16)));
+      if constexpr (FMT == 1) {
+        const uint32_t zw = *reinterpret_cast<const uint32_t*>(wst + CODE_BYTES + 1024 + (col0 + c) * 4);
+        zc[j] = f16_to_f32((uint16_t)(zw >> ((((zhalf ^ par) >> j) & 1) * 16)));
+      } else {
+        zc[j] = 0.f;
+      }
     }
-    w_load(w, d, z, next_blk);
     // A fragments of tile i+1 are read from LDS while tile i's MFMAs run;
     // tile i's MFMAs are issued before tile i-1's rescale so the FMAs run in
     // the matrix core's shadow; two temporaries keep everything in VGPRs.
@@ -257,10 +408,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
     q2_u32x4 a0[4], a1[4];
     q2_f32x4 s0, s1;
     auto rd = [&](int i, q2_u32x4 (&av)[4], q2_f32x4& s4) {
-      s4 = *reinterpret_cast<const q2_f32x4*>(&ss[buf][16 * i + 4 * g]);
+      s4 = *reinterpret_cast<const q2_f32x4*>(&sb[16 * i + 4 * g]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        av[t] = *reinterpret_cast<const q2_u32x4*>(&xs[buf][(16 * i + c) * XSTRIDE + 16 * g + 4 * t]);
+      for (int t = 0; t < 4; ++t) av[t] = afrag(st, i, t);
     };
     auto tile = [&](const q2_u32x4 (&av)[4], q2_f32x4 s4, q2_f32x4 (&tmp)[NT]) {
 #pragma unroll
@@ -292,9 +442,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
   };
 
   if constexpr (LR) {
-    // Copy the limbs of this tile's rows and its columns of B into LDS with
-    // direct global-to-LDS loads: asynchronous, no registers, waited for only
-    // before the epilogue.  Both copies are whole 64-lane instructions because
+    // Copy the limbs of this tile's rows and its columns of B into LDS.  These
+    // are the oldest copies of the wave, so the first stage_barrier already
+    // covers them.  Both copies are whole 64-lane instructions because
     // r % 8 == 0 makes BM*2r/8 and BN*r/8 multiples of 64 for these tiles.
     const int r = a.r;
     const int tch = 2 * r / 8, bch = r / 8;               // 16-byte chunks per row
@@ -303,44 +453,53 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       const int row = idx / tch, ch = idx - row * tch;
       int64_t gr = m0 + row;
       gr = gr < M ? gr : M - 1;
-      __builtin_amdgcn_global_load_lds(a.lr_t + gr * 2 * r + ch * 8,
-                                       (__attribute__((address_space(3))) void*)(lt + base * 8), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.lr_t + gr * 2 * r + ch * 8, (lds_void*)(smem + OFF_LT + base * 16), 16, 0,
+                                       0);
     }
     for (int base = wv * 64; base < BN * bch; base += 256) {
       const int idx = base + lane;
       const int col = idx / bch, ch = idx - col * bch;
-      int64_t gn = (int64_t)tn * BN + col;
-      gn = gn < a.N ? gn : a.N - 1;
-      __builtin_amdgcn_global_load_lds(a.lr_b + gn * r + ch * 8,
-                                       (__attribute__((address_space(3))) void*)(lb + base * 8), 16, 0, 0);
+      int64_t gn = n0 + col;
+      gn = gn < N ? gn : N - 1;
+      __builtin_amdgcn_global_load_lds(a.lr_b + gn * r + ch * 8, (lds_void*)(smem + OFF_LB + base * 16), 16, 0,
+                                       0);
     }
   }
 
   if (KB > 0) {
-    uint32_t xA[CPT][8], xB[CPT][8];
-    uint32_t wA[NT][DW], wB[NT][DW];
-    float dA[NT], dB[NT], zA[NT], zB[NT];
-    x_load(xA, 0);
-    w_load(wA, dA, zA, 0);
-    x_load(xB, 1);
-    w_load(wB, dB, zB, 1);
-    x_store(xA, 0);
-    x_load(xA, 2);
-    __syncthreads();
-    // Steady state at block b: LDS[b&1] holds X(b); the other X registers
-    // hold X(b+1) (to be staged after this block) and X(b+2) (in flight).
-    for (int64_t b = 0; b < KB; b += 2) {
-      compute(0, wA, dA, zA, b + 2);
-      if (b + 1 < KB) x_store(xB, 1);
-      x_load(xB, b + 3);
-      __syncthreads();
-      if (b + 1 >= KB) break;
-      compute(1, wB, dB, zB, b + 3);
-      if (b + 2 < KB) x_store(xA, 0);
-      x_load(xA, b + 4);
-      __syncthreads();
+    // At the top of block b: activations b and b+1 and the weights of b have
+    // landed and the row sums of b are in ss[b & 1].  With XS = 4 the
+    // activations of b+1 were issued two blocks ago (one block's copies came
+    // after them), with XS = 3 one block ago (only that block's weight copies
+    // came after them).
+    x_issue(0, 0);
+    w_issue(0, 0);
+    x_issue(1, 1);
+    w_issue(1, 1);
+    if constexpr (XS == 4) {
+      x_issue(2, 2);
+      stage_barrier<2 * XU + 2 * WU>();
+    } else {
+      stage_barrier<XU + 2 * WU>();
+    }
+    s_compute(xs, 0);
+    int sx = 0, sw = 0;                  // stages of block b
+    for (int64_t b = 0; b < KB; ++b) {
+      if constexpr (XS == 4) stage_barrier<XU + WU>();
+      else stage_barrier<WU>();
+      const int sxn = (sx + XS - 1 >= XS) ? sx - 1 : sx + XS - 1;     // (b + XS - 1) % XS
+      const int swn = (sw + 2 >= WS) ? sw - 1 : sw + 2;               // (b + 2) % 3
+      x_issue(b + XS - 1, sxn);
+      w_issue(b + 2, swn);
+      compute(xs + sx * XSTAGE, wsm + sw * WSTAGE, ss[b & 1], b);
+      const int sx1 = (sx + 1 == XS) ? 0 : sx + 1;
+      if (b + 1 < KB) s_compute(xs + sx1 * XSTAGE, (int)((b + 1) & 1));
+      sx = sx1;
+      sw = (sw + 1 == WS) ? 0 : sw + 1;
     }
   }
+  // No copy may still be writing this workgroup's LDS when it ends.
+  __builtin_amdgcn_s_waitcnt(0);
 
   const float fin = (FMT == 0) ? 4.f : 16.f;
 #pragma unroll
@@ -351,8 +510,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       for (int e = 0; e < 4; ++e) acc[i][j][e] *= fin;
 
   if (LR) {
-    __builtin_amdgcn_s_waitcnt(0);     // this wave's global-to-LDS copies have landed
-    __syncthreads();                   // and every other wave's
+    __syncthreads();                   // every wave's copies of the low-rank operands have landed
     const int r = a.r;
     const int ks = (3 * r + 31) / 32;
     for (int t = 0; t < ks; ++t) {
@@ -390,7 +548,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       const int q0 = 32 * t + 8 * g;
       q2_u32x4 bq[NT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) bq[j] = lr_bfrag(a.lr_b, wrow[j], a.r, q0, lr_vec != 0);
+      for (int j = 0; j < NT; ++j) {
+        int64_t n = nw + 16 * j + c;
+        n = n < N ? n : N - 1;
+        bq[j] = lr_bfrag(a.lr_b, n, a.r, q0, lr_vec != 0);
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         int64_t mr = m0 + 16 * i + c;
@@ -407,11 +569,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int64_t n = nw + 16 * j + c;
-      if (n < a.N) {
+      if (n < N) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (m < M) a.y[m * a.N + n] = acc[i][j][e];
+          if (m < M) a.y[m * N + n] = acc[i][j][e];
         }
       }
     }
@@ -692,12 +854,16 @@ static hipError_t run_gemm(const LinearArgs& a, hipStream_t stream) {
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   const int vec = lowrank_vec(a);
-  if (FMT == 0 && vec && a.r <= LR_RMAX)
-    hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, true>), dim3((unsigned)tiles), dim3(256), 0, stream, a, (int)tiles_m,
-                       vec);
-  else
-    hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, false>), dim3((unsigned)tiles), dim3(256), 0, stream, a,
-                       (int)tiles_m, vec);
+  // The low-rank branch only exists for Q2_0 weights.
+  if constexpr (FMT == 0) {
+    if (vec && a.r <= LR_RMAX) {
+      hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, true>), dim3((unsigned)tiles), dim3(256), 0, stream, a,
+                         (int)tiles_m, vec);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<FMT, BM, BN, false>), dim3((unsigned)tiles), dim3(256), 0, stream, a, (int)tiles_m,
+                     vec);
   return hipGetLastError();
 }
 
@@ -746,6 +912,10 @@ static hipError_t run_gemm_auto(const LinearArgs& a, hipStream_t stream) {
   // Prefer the largest tile that still gives a few waves of workgroups over
   // the 256 compute units.
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  // 48 x 192 tiles run two workgroups (eight waves) per CU; with the low-rank
+  // operands staged in LDS the tile no longer fits twice, so that case keeps 96 x 192.
+  const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
+  if (!lr_lds && a.M >= 48 && tiles(48, 192) >= 512) return run_gemm<FMT, 48, 192>(a, stream);
   if (a.M >= 96 && tiles(96, 192) >= 256) return run_gemm<FMT, 96, 192>(a, stream);
   if (a.M >= 64 && tiles(64, 128) >= 256) return run_gemm<FMT, 64, 128>(a, stream);
   if (tiles(32, 128) >= 256) return run_gemm<FMT, 32, 128>(a, stream);

@@ -68,6 +68,12 @@ def test_linear_argument_errors(lib):
     assert lib.q4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 5, 64, None) == q2.Q2_ERR_SHAPE
     assert lib.q4_linear(FAKE, FAKE, FAKE, None, FAKE, 3, 5, 128, None) == q2.Q2_ERR_ARG
     assert lib.q2_dequant(FAKE, FAKE, FAKE, 4, 130, None) == q2.Q2_ERR_SHAPE
+    # K beyond 2^24 is refused by every linear entry point (checked before any HIP call)
+    big = (1 << 24) + 128
+    assert L(FAKE, FAKE, FAKE, FAKE, 4, 8, big, None) == q2.Q2_ERR_SHAPE and b"16777216" in lib.q2_last_error()
+    assert lib.q4_linear(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, big, None) == q2.Q2_ERR_SHAPE
+    assert lib.q2_linear_lowrank(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 8, big, FAKE, 1 << 20,
+                                 None) == q2.Q2_ERR_SHAPE
     assert lib.q2_dequant(None, None, None, 0, 128, None) == q2.Q2_OK
 
 

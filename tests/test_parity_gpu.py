@@ -163,6 +163,42 @@ def test_linear_ragged(path, m, n, k):
     assert_close(y, O.q2_linear(xb, p_ref, s_ref), f"{path} M={m} N={n} K={k}")
 
 
+# One case per GEMM tile configuration (48x192, 96x192, 64x128, 32x128, 32x64),
+# each ragged in M and N so the clamped rows and columns are exercised.
+TILE_CASES = [(203, 24700, 384), (500, 8500, 256), (250, 8100, 256), (40, 16300, 256), (20, 300, 256)]
+
+
+@pytest.mark.parametrize("m,n,k", TILE_CASES)
+def test_linear_tile_configs(m, n, k):
+    p_dev, s_dev, p_ref, s_ref = q2_weights(16, n, k)
+    xb, x = acts(16, m, k)
+    y = q2.q2_linear(x, p_dev, s_dev).cpu().numpy()
+    assert_close(y, O.q2_linear(xb, p_ref, s_ref), f"M={m} N={n} K={k}")
+    p4, s4, z4, xb4, x4, P, S, Z = q4_case(19, m, k, n)
+    y4 = q2.q4_linear(x4, P, S, Z).cpu().numpy()
+    assert_close(y4, O.q4_linear(xb4, p4, s4, z4), f"q4 M={m} N={n} K={k}")
+
+
+def _offset_f16(t):
+    """The same values in a buffer whose first element sits 2 bytes past a 4-byte boundary."""
+    flat = torch.empty(t.numel() + 1, dtype=torch.float16, device=t.device)
+    v = flat[1:].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 4 == 2
+    return v
+
+
+@pytest.mark.parametrize("m,n,k", [(203, 24700, 384), (130, 700, 1280), (5, 77, 384)])
+def test_scales_at_odd_halfword(m, n, k):
+    p_dev, s_dev, p_ref, s_ref = q2_weights(17, n, k)
+    xb, x = acts(17, m, k)
+    y = q2.q2_linear(x, p_dev, _offset_f16(s_dev)).cpu().numpy()
+    assert_close(y, O.q2_linear(xb, p_ref, s_ref), f"odd scales M={m} N={n} K={k}")
+    p4, s4, z4, xb4, x4, P, S, Z = q4_case(18, m, k, n)
+    y4 = q2.q4_linear(x4, P, _offset_f16(S), _offset_f16(Z)).cpu().numpy()
+    assert_close(y4, O.q4_linear(xb4, p4, s4, z4), f"odd q4 scales M={m} N={n} K={k}")
+
+
 def test_linear_empty_and_k_zero():
     n = 40
     x = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
