@@ -142,7 +142,7 @@ def main():
             p, s = copies[state["i"] % len(copies)]
             state["i"] += 1
             q2.q2_linear(x1, p, s, y)
-        calls.append(("gemv_m1", 2.0 * n * k, wbytes, fn, f"M=1 K={k} N={n} x{ncopies} copies"))
+        calls.append(("gemv_m1", 2.0 * n * k, wbytes, fn, f"M=1 K={k} N={n} x{ncopies} copies", ncopies))
     # low-rank branch, rank 32
     lr = I.LOWRANK
     r = 32
@@ -167,23 +167,21 @@ def main():
                       f"M={I.Q4_M} K={k} N={n}"))
 
     if "copy_ref" in args.only.split(","):
-        # calibration for the HBM counters: a plain copy of known size (256 MiB read + 256 MiB written)
-        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).fill_(1)
+        # calibration for the HBM counters: a plain streaming kernel of known size
+        # (256 MiB read + 256 MiB written)
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        calls.append(("copy_ref", 0.0, float(src.numel()), lambda: dst.copy_(src), "copy 256 MiB"))
+        calls.append(("copy_ref", 0.0, float(src.numel() * 4), lambda: torch.neg(src, out=dst),
+                      "elementwise neg, 256 MiB read + 256 MiB written"))
     if args.only:
         keep = set(args.only.split(","))
         calls = [c for c in calls if c[0] in keep]
         if not calls:
             sys.exit(f"--only {args.only}: no such call family")
 
-    def step(events=None):
-        for ci, c in enumerate(calls):
-            if events is not None:
-                events[ci][0].record()
+    def step():
+        for c in calls:
             c[3]()
-            if events is not None:
-                events[ci][1].record()
 
     for _ in range(args.warmup):
         step()
@@ -211,24 +209,33 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
     step_flops = sum(c[1] for c in calls)
 
-    # Per-call durations: the same calls again, each bracketed by HIP events on
-    # torch's current stream (the stream the library launches on).  A GPU spin
-    # queued first lets the host enqueue the whole step before the GPU reaches
-    # it, so each event pair brackets back-to-back GPU execution only.
-    per = [[] for _ in calls]
-    for _ in range(args.steps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
-        torch.cuda._sleep(5_000_000)
-        step(ev)
+    # Per-call durations: for each call, `steps` back-to-back launches captured
+    # in a graph of their own, bracketed by HIP events recorded on torch's
+    # current stream (the stream the library launches on); the average launch
+    # duration includes the gap between consecutive kernels.
+    # A streamed (M = 1) call runs at least once per weight copy, so every
+    # launch reads weights that are not cache resident.
+    per = []
+    for c in calls:
+        reps = max(args.steps, c[5] if len(c) > 5 else 1)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                c[3]()
+        g.replay()
         torch.cuda.synchronize()
-        for ci, (e0, e1) in enumerate(ev):
-            per[ci].append(e0.elapsed_time(e1) * 1e-3)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        del g
 
     parts = {}
     fam_time, fam_flops, fam_bytes = {}, {}, {}
-    for c, ts in zip(calls, per):
-        fam, flops, wbytes, _, label = c
-        t = float(np.mean(ts))
+    for c, t in zip(calls, per):
+        fam, flops, wbytes, _, label = c[:5]
         d = {"us": round(t * 1e6, 3), "tflops": round(flops / t / 1e12, 3),
              "weight_gbs": round(wbytes / t / 1e9, 2)}
         d["frac"] = round((wbytes / t / 1e9) / PEAK_HBM_GBS, 4) if fam == "gemv_m1" else \

@@ -186,6 +186,12 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Chunk swizzle of an activation row: chunk q of row r sits at position
+// q ^ row_swz(r), row_swz a bit rotation of r mod 16.  Plain q ^ (r & 15) is
+// conflict-free for 16 lanes in isolation but measured at two thirds of the
+// LDS read rate of the rotated form for the 64-lane fragment reads.
+__device__ __forceinline__ int row_swz(int r) { return ((r >> 2) & 3) | ((r & 3) << 2); }
+
 template <int FMT>
 __device__ __forceinline__ void decode_block_nat(const uint32_t (&w)[WFmt<FMT>::LANE_DW], q2_u32x4 (&bf)[4],
                                                  const NatConsts& k) {
@@ -213,9 +219,8 @@ __device__ __forceinline__ void decode_block_nat(const uint32_t (&w)[WFmt<FMT>::
 // registers, no VALU): activations into a ring of XS block buffers, weight
 // codes, scales and zero points into a ring of 3.  Since the main loop issues
 // no other vector-memory loads, the only waits are the explicit ones in
-// stage_barrier.  Activation chunk q of row r is stored at position
-// q ^ (r & 15), so the 16 lanes of a fragment read (same chunk, 16 consecutive
-// rows) hit 16 different bank groups; weight units are swizzled the same way.
+// stage_barrier.  Activation chunks are XOR-swizzled per row (row_swz) so
+// fragment reads run at the full LDS rate; weight units are swizzled too.
 // A scale or zero point is copied as the 4-byte word that holds it (aligned
 // down; the word never leaves the 16-byte granule of the value), so the copies
 // need no alignment beyond the element's.
@@ -234,10 +239,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
   constexpr int XS = LR ? 3 : 4;         // activation ring: b, b+1 (row sums), in-flight
   constexpr int WS = 3;                  // weight ring: b, b+1, b+2
   constexpr int XSTAGE = BM * 256;       // bytes per activation block
-  constexpr int CODE_BYTES = BN * BBYTES;
+  constexpr int CU = (FMT == 0) ? (BN * 2 + 255) / 256 : BN / 64;   // 16-byte code copies per thread per block
+  constexpr int CODE_BYTES = CU * 4096;  // code chunk slots of a weight stage (2-bit: padded past BN * 32)
   constexpr int WSTAGE = CODE_BYTES + ((FMT == 0) ? 1024 : 2048);   // codes + 256 scale [+ 256 zero] words
   constexpr int XU = BM / 16;            // activation copies (16 B) per thread per block
-  constexpr int CU = (FMT == 0) ? BN / 32 : BN / 64;   // code copies per thread per block (4 B / 16 B)
   constexpr int WU = CU + ((FMT == 0) ? 1 : 2);        // all weight copies per thread per block
   static_assert(BM % 16 == 0 && BN % 64 == 0 && BN <= 256, "tile shape");
 
@@ -275,7 +280,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
   for (int u = 0; u < XU; ++u) {
     const int pos = (u * 4 + wv) * 64 + lane;      // 16-byte chunk position in the stage
     const int row = pos >> 4;
-    const int q = (pos & 15) ^ (row & 15);
+    const int q = (pos & 15) ^ row_swz(row);
     const int64_t gr = (m0 + row < M) ? row : M - 1 - m0;
     xoff[u] = (uint32_t)(gr * K * 2 + q * 16);
   }
@@ -284,11 +289,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
   for (int v = 0; v < CU; ++v) {
     const int pos = (v * 4 + wv) * 64 + lane;
     int col, unit;
-    if constexpr (FMT == 0) {                      // 4-byte copies, 8 per column; 8-byte units swizzled
-      col = pos >> 3;
-      const int up = (pos & 7) >> 1;
-      unit = ((up ^ ((col >> 2) & 3)) << 3) | ((pos & 1) << 2);
-    } else {                                       // 16-byte copies, 4 per column, swizzled
+    if constexpr (FMT == 0) {                      // 2 chunks per column (slots past 2 BN: padding)
+      col = pos >> 1;
+      col = col < BN ? col : BN - 1;
+      unit = ((pos & 1) ^ ((col >> 2) & 1)) << 4;
+    } else {                                       // 4 chunks per column
       col = pos >> 2;
       unit = ((pos & 3) ^ ((col >> 1) & 3)) << 4;
     }
@@ -304,8 +309,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
   // ---- read side: lane offsets within a stage
   int aoff[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) aoff[t] = c * 256 + (((4 * g + t) ^ c) << 4);
-  const int coff = (FMT == 0) ? c * 32 + ((g ^ ((c >> 2) & 3)) << 3) : c * 64 + ((g ^ ((c >> 1) & 3)) << 4);
+  for (int t = 0; t < 4; ++t) aoff[t] = c * 256 + (((4 * g + t) ^ row_swz(c)) << 4);
+  const int coff = (FMT == 0) ? c * 32 + ((((g >> 1) ^ ((c >> 2) & 1)) << 4) | ((g & 1) << 3))
+                              : c * 64 + ((g ^ ((c >> 1) & 3)) << 4);
   // Which half of its word holds the scale (zero point) of this lane's column j at block 0.
   uint32_t shalf = 0, zhalf = 0;
 #pragma unroll
@@ -332,12 +338,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
     const uint8_t* base = a.w + n0 * row_bytes + blk * BBYTES;
     const int dst = OFF_W + stage * WSTAGE;   // LDS copies must name the shared array itself
 #pragma unroll
-    for (int v = 0; v < CU; ++v) {
-      if constexpr (FMT == 0)
-        __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v], (lds_void*)(smem + dst + (v * 4 + wv) * 256), 4, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v], (lds_void*)(smem + dst + (v * 4 + wv) * 1024), 16, 0, 0);
-    }
+    for (int v = 0; v < CU; ++v)
+      __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v], (lds_void*)(smem + dst + (v * 4 + wv) * 1024), 16, 0,
+                                       0);
     // Byte offset of the aligned word holding element s_idx + blk (may start 2 bytes before it).
     const int64_t si = 2 * (s_idx + blk);
     const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.s);
@@ -491,9 +494,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       const int swn = (sw + 2 >= WS) ? sw - 1 : sw + 2;               // (b + 2) % 3
       x_issue(b + XS - 1, sxn);
       w_issue(b + 2, swn);
-      compute(xs + sx * XSTAGE, wsm + sw * WSTAGE, ss[b & 1], b);
+      // Row sums of b+1 first: their LDS reads and dependent MFMAs overlap the decode of b.
       const int sx1 = (sx + 1 == XS) ? 0 : sx + 1;
       if (b + 1 < KB) s_compute(xs + sx1 * XSTAGE, (int)((b + 1) & 1));
+      compute(xs + sx * XSTAGE, wsm + sw * WSTAGE, ss[b & 1], b);
       sx = sx1;
       sw = (sw + 1 == WS) ? 0 : sw + 1;
     }
