@@ -585,6 +585,356 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 }
 
 // ============================================================================
+// GEMM at 96 x 192 with eight waves: the two waves of a SIMD split the K blocks
+// ============================================================================
+// Wave w owns the 96 x 48 output columns (w & 3) and the K blocks of parity
+// w >> 2, so the two waves sharing a SIMD (w and w + 4) compute the same output
+// tile from alternate blocks: per SIMD and block there is one wave's decode
+// and rescale (as with a single 96-row wave) but two waves to hide latency.
+// Their partial accumulators are summed once, through LDS, at the end (the
+// block-scaled sum is linear in the blocks).  One iteration covers a pair of
+// blocks: the pair's copies were issued during the previous iteration into the
+// other half of a two-pair ring; the row sums of both blocks are computed at
+// the top of the iteration (twelve 16-row tasks, three per SIMD) and published
+// through LDS before the main MFMAs.
+template <int FMT, bool LR>
+__global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles_m) {
+  constexpr int BM = 96, BN = 192, MT = 6, NT = 3;
+  constexpr int DW = WFmt<FMT>::LANE_DW;
+  constexpr int BBYTES = WFmt<FMT>::BLOCK_BYTES;
+  constexpr int XSTAGE = BM * 256;                           // one activation block
+  constexpr int CODE_SLOT = (FMT == 0) ? 512 * 16 : 768 * 16; // one block's codes (2-bit: 384 chunks padded to 512)
+  constexpr int WSTAGE = CODE_SLOT + ((FMT == 0) ? 1024 : 2048);
+  constexpr int XU = 6;                                      // activation copies per thread per pair
+  constexpr int CU = (FMT == 0) ? 2 : 3;                     // code copies per thread per pair
+  constexpr int OFF_W = 4 * XSTAGE;
+  constexpr int OFF_S = OFF_W + 4 * WSTAGE;
+  constexpr int SMEM = OFF_S + 4 * BM * 4;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(3 * XSTAGE >= 4 * 96 * 48 * 4, "reduction buffer");
+  __shared__ __align__(16) uint8_t smem[SMEM];
+  float (*const ss)[2][BM] = reinterpret_cast<float (*)[2][BM]>(smem + OFF_S);   // [slot][block of pair][row]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wv & 3, par = wv >> 2;
+  const int c = lane & 15, g = lane >> 4;
+  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t nw = n0 + wn * (BN / 4);
+  const int64_t M = a.M, N = a.N, K = a.K, KB = K / BLOCK_K;
+  const int64_t row_bytes = (FMT == 0) ? K / 4 : K / 2;
+  const NatConsts kc = (FMT == 0) ? q2_nat_consts() : q4_nat_consts();
+
+  // ---- copy sources.  Activation copy u of wave wv fills, in block u / 3 of
+  // the pair, the 64 chunk positions starting at ((u % 3) * 8 + wv) * 64.
+  uint32_t xoff[3];                       // copies u and u + 3 (the pair's two blocks) share an offset
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int pos = (u * 8 + wv) * 64 + lane;
+    const int row = pos >> 4;
+    const int q = (pos & 15) ^ row_swz(row);
+    const int64_t gr = (m0 + row < M) ? row : M - 1 - m0;
+    xoff[u] = (uint32_t)(gr * K * 2 + q * 16);
+  }
+  // Code copy v of wave wv: chunk index ci = (v * 8 + wv) * 64 + lane of the
+  // pair, block ci / CPB, chunk ci % CPB of that block.
+  constexpr int CPB = CODE_SLOT / 16;                          // chunk slots per block
+  uint32_t woff[CU];
+#pragma unroll
+  for (int v = 0; v < CU; ++v) {
+    const int ci = (v * 8 + wv) * 64 + lane;
+    const int pos = ci % CPB;
+    int col, unit;
+    if constexpr (FMT == 0) {
+      col = pos >> 1;
+      col = col < BN ? col : BN - 1;
+      unit = ((pos & 1) ^ ((col >> 2) & 1)) << 4;
+    } else {
+      col = pos >> 2;
+      unit = ((pos & 3) ^ ((col >> 1) & 3)) << 4;
+    }
+    const int64_t gc = (n0 + col < N) ? col : N - 1 - n0;
+    woff[v] = (uint32_t)(gc * row_bytes + unit);
+  }
+  // Scale / zero word: wave wv covers block (wv >> 2) of the pair, columns (wv & 3) * 64 + lane.
+  int64_t sgc = (wv & 3) * 64 + lane;
+  sgc = sgc < BN ? sgc : BN - 1;
+  sgc = (n0 + sgc < N) ? n0 + sgc : N - 1;
+  const int64_t s_idx = sgc * KB;
+
+  // ---- read side
+  int aoff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) aoff[t] = c * 256 + (((4 * g + t) ^ row_swz(c)) << 4);
+  const int coff = (FMT == 0) ? c * 32 + ((((g >> 1) ^ ((c >> 2) & 1)) << 4) | ((g & 1) << 3))
+                              : c * 64 + ((g ^ ((c >> 1) & 3)) << 4);
+  uint32_t shalf = 0, zhalf = 0;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    int64_t r = nw + 16 * j + c;
+    r = r < N ? r : N - 1;
+    shalf |= (uint32_t)((((uintptr_t)(a.s + r * KB)) >> 1) & 1) << j;
+    if constexpr (FMT == 1) zhalf |= (uint32_t)((((uintptr_t)(a.z + r * KB)) >> 1) & 1) << j;
+  }
+
+  // Copies of the pair starting at block b2 (blocks past the end re-copy the last one).
+  auto issue_pair = [&](int64_t b2, int slot) {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      int64_t blk = b2 + u / 3;
+      blk = blk < KB ? blk : KB - 1;
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + m0 * K + blk * BLOCK_K);
+      __builtin_amdgcn_global_load_lds(base + (uint64_t)xoff[u % 3],
+                                       (lds_void*)(smem + (2 * slot + u / 3) * XSTAGE + ((u % 3) * 8 + wv) * 1024),
+                                       16, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < CU; ++v) {
+      const int ci0 = (v * 8 + wv) * 64;                       // uniform
+      const int q = ci0 / CPB;
+      int64_t blk = b2 + q;
+      blk = blk < KB ? blk : KB - 1;
+      const uint8_t* base = a.w + n0 * row_bytes + blk * BBYTES;
+      __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v],
+                                       (lds_void*)(smem + OFF_W + (2 * slot + q) * WSTAGE + (ci0 - q * CPB) * 16),
+                                       16, 0, 0);
+    }
+    {
+      int64_t blk = b2 + (wv >> 2);
+      blk = blk < KB ? blk : KB - 1;
+      const int64_t si = 2 * (s_idx + blk);
+      const int dst = OFF_W + (2 * slot + (wv >> 2)) * WSTAGE + CODE_SLOT + (wv & 3) * 256;
+      const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.s);
+      __builtin_amdgcn_global_load_lds(sp + (si - (int64_t)(((uintptr_t)sp + si) & 3)), (lds_void*)(smem + dst), 4, 0,
+                                       0);
+      if constexpr (FMT == 1) {
+        const uint8_t* zp = reinterpret_cast<const uint8_t*>(a.z);
+        __builtin_amdgcn_global_load_lds(zp + (si - (int64_t)(((uintptr_t)zp + si) & 3)),
+                                         (lds_void*)(smem + dst + 1024), 4, 0, 0);
+      }
+    }
+  };
+  // Low-rank operands into the two activation stages starting at stage st0.
+  auto issue_lr = [&](int st0) {
+    const int r = a.r;
+    const int tch = 2 * r / 8, bch = r / 8;
+    for (int base = wv * 64; base < BM * tch; base += 512) {
+      const int idx = base + lane;
+      const int row = idx / tch, ch = idx - row * tch;
+      int64_t gr = m0 + row;
+      gr = gr < M ? gr : M - 1;
+      __builtin_amdgcn_global_load_lds(a.lr_t + gr * 2 * r + ch * 8, (lds_void*)(smem + st0 * XSTAGE + base * 16), 16,
+                                       0, 0);
+    }
+    for (int base = wv * 64; base < BN * bch; base += 512) {
+      const int idx = base + lane;
+      const int col = idx / bch, ch = idx - col * bch;
+      int64_t gn = n0 + col;
+      gn = gn < N ? gn : N - 1;
+      __builtin_amdgcn_global_load_lds(a.lr_b + gn * r + ch * 8, (lds_void*)(smem + (st0 + 1) * XSTAGE + base * 16),
+                                       16, 0, 0);
+    }
+  };
+  auto afrag = [&](const uint8_t* st, int i, int t) -> q2_u32x4 {
+    return *reinterpret_cast<const q2_u32x4*>(st + i * 4096 + aoff[t]);
+  };
+
+  const uint32_t sone = (FMT == 0) ? 0xBFA0BFA0u : 0xBF80BF80u;   // bf16 -1.25 / -1 pairs
+  const q2_u32x4 sones = q2_u32x4{sone, sone, sone, sone};
+
+  q2_f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Decode of one block's weights for this wave's columns (from its weight stage).
+  auto decode = [&](const uint8_t* wst, int64_t blk, q2_u32x4 (&bf)[NT][4], float (&dc)[NT], float (&zc)[NT]) {
+    const uint32_t pmask = (uint32_t)(blk & 1) ? 0xFFu : 0u;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int col0 = wn * (BN / 4) + 16 * j;
+      uint32_t w[DW];
+      if constexpr (FMT == 0) {
+        const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(wst + col0 * 32 + coff);
+        w[0] = v[0]; w[1] = v[1];
+      } else {
+        const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(wst + col0 * 64 + coff);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+      }
+      decode_block_nat<FMT>(w, bf[j], kc);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + (col0 + c) * 4);
+      dc[j] = f16_to_f32((uint16_t)(sw >> ((((shalf ^ pmask) >> j) & 1) * 16)));
+      if constexpr (FMT == 1) {
+        const uint32_t zw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + 1024 + (col0 + c) * 4);
+        zc[j] = f16_to_f32((uint16_t)(zw >> ((((zhalf ^ pmask) >> j) & 1) * 16)));
+      } else {
+        zc[j] = 0.f;
+      }
+    }
+  };
+  // MFMAs of one block over the staged activations `st`, row sums `sb`.
+  // Fragments of tile i+1 are read while tile i's MFMAs run; each tile is
+  // rescaled right after its MFMAs (the SIMD's other wave covers the wait).
+  auto mainblk = [&](const uint8_t* st, const float* sb, const q2_u32x4 (&bf)[NT][4], const float (&dc)[NT],
+                     const float (&zc)[NT]) {
+    q2_u32x4 a0[4], a1[4];
+    q2_f32x4 s0, s1;
+    auto rd = [&](int i, q2_u32x4 (&av)[4], q2_f32x4& s4) {
+      s4 = *reinterpret_cast<const q2_f32x4*>(&sb[16 * i + 4 * g]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) av[t] = afrag(st, i, t);
+    };
+    auto tile = [&](int i, const q2_u32x4 (&av)[4], q2_f32x4 s4) {
+      q2_f32x4 tmp[NT];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          tmp[j] = mfma(av[t], bf[j][t], t == 0 ? block_cinit<FMT>(s4, zc[j]) : tmp[j]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(dc[j], tmp[j][e], acc[i][j][e]);
+    };
+    rd(0, a0, s0);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i & 1) {
+        if (i + 1 < MT) rd(i + 1, a0, s0);
+        tile(i, a1, s1);
+      } else {
+        if (i + 1 < MT) rd(i + 1, a1, s1);
+        tile(i, a0, s0);
+      }
+    }
+  };
+
+  // Iteration ip covers the pair (2ip, 2ip+1) in ring slot ip & 1:
+  //   B1 (the pair has landed): copies of the next pair go out; row sums of
+  //      both blocks (twelve 16-row tasks); each wave decodes its block;
+  //   B2 (row sums visible): each wave runs the MFMAs of its block.
+  // (Skewing the parities by half an iteration, so that one wave of a SIMD
+  // decodes while the other multiplies, keeps the decoded operands live across
+  // the loop and does not fit the 256 registers of a two-wave SIMD.)
+  int lr_st0 = 2;                         // activation stages holding the low-rank operands
+  if (KB > 0) {
+    issue_pair(0, 0);
+    for (int64_t ip = 0; 2 * ip < KB; ++ip) {
+      const int slot = (int)(ip & 1);
+      stage_barrier<0>();                 // B1: this pair has landed; every wave is done with the previous one
+      if (2 * ip + 2 < KB) {
+        issue_pair(2 * ip + 2, slot ^ 1);
+      } else if constexpr (LR) {
+        lr_st0 = 2 * (slot ^ 1);
+        issue_lr(lr_st0);
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {    // row sums: tasks wv and wv + 8 of twelve
+        const int task = wv + 8 * k2;
+        const int q = task >= 6 ? 1 : 0, it = task - 6 * q;
+        if (task < 12 && 2 * ip + q < KB) {
+          const uint8_t* st = smem + (2 * slot + q) * XSTAGE;
+          q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) s4 = mfma(afrag(st, it, t), sones, s4);
+          if (c == 0) *reinterpret_cast<q2_f32x4*>(&ss[slot][q][16 * it + 4 * g]) = s4;
+        }
+      }
+      const int64_t bp = 2 * ip + par;
+      q2_u32x4 bf[NT][4];
+      float dc[NT], zc[NT];
+      decode(smem + OFF_W + (2 * slot + par) * WSTAGE, bp, bf, dc, zc);
+      stage_barrier<63>();                // B2: row sums visible (no wait on the copies in flight)
+      if (bp < KB) mainblk(smem + (2 * slot + par) * XSTAGE, ss[slot][par], bf, dc, zc);
+    }
+  } else if constexpr (LR) {
+    issue_lr(lr_st0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);          // every copy of this wave has landed
+  __syncthreads();
+
+  const float fin = (FMT == 0) ? 4.f : 16.f;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] *= fin;
+
+  if constexpr (LR) {
+    // Parity-1 waves add the branch to their partial sums.
+    if (par == 1) {
+      const uint16_t* lt = reinterpret_cast<const uint16_t*>(smem + lr_st0 * XSTAGE);
+      const uint16_t* lb = reinterpret_cast<const uint16_t*>(smem + (lr_st0 + 1) * XSTAGE);
+      const int r = a.r;
+      const int ks = (3 * r + 31) / 32;
+      for (int t = 0; t < ks; ++t) {
+        const int q0 = 32 * t + 8 * g;
+        const bool lv = q0 < 3 * r;
+        const int part = q0 / r, jj = q0 - part * r;
+        q2_u32x4 bq[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int col = wn * (BN / 4) + 16 * j + c;
+          q2_u32x4 v = q2_u32x4{0u, 0u, 0u, 0u};
+          if (lv) {
+            const q2_u32x4 raw = *reinterpret_cast<const q2_u32x4*>(&lb[col * r + jj]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              uint16_t h0, l0, h1, l1;
+              f16_split_bf16((uint16_t)(raw[d] & 0xFFFFu), h0, l0);
+              f16_split_bf16((uint16_t)(raw[d] >> 16), h1, l1);
+              v[d] = (part == 1) ? ((uint32_t)l0 | ((uint32_t)l1 << 16)) : ((uint32_t)h0 | ((uint32_t)h1 << 16));
+            }
+          }
+          bq[j] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const q2_u32x4 aq =
+              lv ? *reinterpret_cast<const q2_u32x4*>(&lt[(16 * i + c) * 2 * r + (part == 2 ? r : 0) + jj])
+                 : q2_u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
+        }
+      }
+    }
+  }
+  // Every wave is done reading activations and low-rank operands: the reduction
+  // buffer may overwrite them.
+  __syncthreads();
+
+  // Parity-1 partial sums -> LDS -> added by the parity-0 wave of the same columns.
+  float* red = reinterpret_cast<float*>(smem) + wn * (MT * NT * 4 * 64);
+  if (par == 1) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((i * NT + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+  }
+  __syncthreads();
+  if (par == 0) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int64_t n = nw + 16 * j + c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[i][j][e] + red[((i * NT + j) * 4 + e) * 64 + lane];
+          const int64_t m = m0 + 16 * i + 4 * g + e;
+          if (m < M && n < N) a.y[m * N + n] = v;
+        }
+      }
+    }
+  }
+}
+
+// ============================================================================
 // GEMV, M <= 16
 // ============================================================================
 constexpr int GEMV_XQ = 2;                        // 16-activation staging chunks per thread per pass
@@ -912,6 +1262,22 @@ static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
 }
 
 template <int FMT>
+static hipError_t run_gemm_kpair(const LinearArgs& a, hipStream_t stream) {
+  const int64_t tiles_m = (a.M + 95) / 96;
+  const int64_t tiles = tiles_m * ((a.N + 191) / 192);
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  if constexpr (FMT == 0) {
+    if (a.r > 0) {
+      hipLaunchKernelGGL((gemm_kpair_kernel<FMT, true>), dim3((unsigned)tiles), dim3(512), 0, stream, a,
+                         (int)tiles_m);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kpair_kernel<FMT, false>), dim3((unsigned)tiles), dim3(512), 0, stream, a, (int)tiles_m);
+  return hipGetLastError();
+}
+
+template <int FMT>
 static hipError_t run_gemm_auto(const LinearArgs& a, hipStream_t stream) {
   // Prefer the largest tile that still gives a few waves of workgroups over
   // the 256 compute units.
@@ -919,6 +1285,11 @@ static hipError_t run_gemm_auto(const LinearArgs& a, hipStream_t stream) {
   // 48 x 192 tiles run two workgroups (eight waves) per CU; with the low-rank
   // operands staged in LDS the tile no longer fits twice, so that case keeps 96 x 192.
   const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
+#ifndef Q2_NO_KPAIR
+  // Eight-wave 96 x 192 tiles when they fill the chip (the low-rank branch only
+  // in its LDS-staged form).
+  if (a.M >= 96 && tiles(96, 192) >= 256 && (a.r == 0 || lr_lds)) return run_gemm_kpair<FMT>(a, stream);
+#endif
   if (!lr_lds && a.M >= 48 && tiles(48, 192) >= 512) return run_gemm<FMT, 48, 192>(a, stream);
   if (a.M >= 96 && tiles(96, 192) >= 256) return run_gemm<FMT, 96, 192>(a, stream);
   if (a.M >= 64 && tiles(64, 128) >= 256) return run_gemm<FMT, 64, 128>(a, stream);

@@ -266,7 +266,9 @@ def lowrank_case(cfg, m, k, n, r):
 
 @pytest.mark.parametrize("m,k,n,r", [(4, 256, 64, 4), (4, 256, 64, 32), (1, 3072, 9216, 32), (17, 384, 100, 5),
                                      (16, 1280, 333, 64), (200, 640, 250, 7), (96, 3072, 192, 64),
-                                     (257, 512, 300, 72), (100, 256, 70, 8), (33, 1280, 190, 16), (1, 128, 5, 1)])
+                                     (257, 512, 300, 72), (100, 256, 70, 8), (33, 1280, 190, 16), (1, 128, 5, 1),
+                                     # eight-wave 96x192 tiles: odd block count, a single block
+                                     (200, 640, 24700, 32), (203, 128, 24700, 8)])
 def test_lowrank_parity(m, k, n, r):
     p_dev, s_dev, p_ref, s_ref, xb, x, a, b, A, B = lowrank_case(50, m, k, n, r)
     y = q2.q2_linear_lowrank(x, p_dev, s_dev, A, B).cpu().numpy()
