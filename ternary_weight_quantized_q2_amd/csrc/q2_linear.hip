@@ -678,19 +678,21 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
     if constexpr (FMT == 1) zhalf |= (uint32_t)((((uintptr_t)(a.z + r * KB)) >> 1) & 1) << j;
   }
 
-  // Copies of the pair starting at block b2 (blocks past the end re-copy the last one).
-  auto issue_pair = [&](int64_t b2, int slot) {
-#pragma unroll
-    for (int u = 0; u < XU; ++u) {
+  // Copies of the pair starting at block b2, one unit at a time: units 0-5
+  // activations, then the codes, the scale words [and zero words].  Blocks
+  // past the end re-copy the last one.
+  constexpr int NU = XU + CU + ((FMT == 0) ? 1 : 2);
+  auto issue_unit = [&](int unit, int64_t b2, int slot) {
+    if (unit < XU) {
+      const int u = unit;
       int64_t blk = b2 + u / 3;
       blk = blk < KB ? blk : KB - 1;
       const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + m0 * K + blk * BLOCK_K);
       __builtin_amdgcn_global_load_lds(base + (uint64_t)xoff[u % 3],
                                        (lds_void*)(smem + (2 * slot + u / 3) * XSTAGE + ((u % 3) * 8 + wv) * 1024),
                                        16, 0, 0);
-    }
-#pragma unroll
-    for (int v = 0; v < CU; ++v) {
+    } else if (unit < XU + CU) {
+      const int v = unit - XU;
       const int ci0 = (v * 8 + wv) * 64;                       // uniform
       const int q = ci0 / CPB;
       int64_t blk = b2 + q;
@@ -699,21 +701,25 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v],
                                        (lds_void*)(smem + OFF_W + (2 * slot + q) * WSTAGE + (ci0 - q * CPB) * 16),
                                        16, 0, 0);
-    }
-    {
+    } else {
       int64_t blk = b2 + (wv >> 2);
       blk = blk < KB ? blk : KB - 1;
       const int64_t si = 2 * (s_idx + blk);
       const int dst = OFF_W + (2 * slot + (wv >> 2)) * WSTAGE + CODE_SLOT + (wv & 3) * 256;
-      const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.s);
-      __builtin_amdgcn_global_load_lds(sp + (si - (int64_t)(((uintptr_t)sp + si) & 3)), (lds_void*)(smem + dst), 4, 0,
-                                       0);
-      if constexpr (FMT == 1) {
+      if (unit == XU + CU) {
+        const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.s);
+        __builtin_amdgcn_global_load_lds(sp + (si - (int64_t)(((uintptr_t)sp + si) & 3)), (lds_void*)(smem + dst), 4,
+                                         0, 0);
+      } else if constexpr (FMT == 1) {
         const uint8_t* zp = reinterpret_cast<const uint8_t*>(a.z);
         __builtin_amdgcn_global_load_lds(zp + (si - (int64_t)(((uintptr_t)zp + si) & 3)),
                                          (lds_void*)(smem + dst + 1024), 4, 0, 0);
       }
     }
+  };
+  auto issue_pair = [&](int64_t b2, int slot) {
+#pragma unroll
+    for (int un = 0; un < NU; ++un) issue_unit(un, b2, slot);
   };
   // Low-rank operands into the two activation stages starting at stage st0.
   auto issue_lr = [&](int st0) {
@@ -777,8 +783,10 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   // MFMAs of one block over the staged activations `st`, row sums `sb`.
   // Fragments of tile i+1 are read while tile i's MFMAs run; each tile is
   // rescaled right after its MFMAs (the SIMD's other wave covers the wait).
+  // The next pair's copies (nb2 >= 0) are issued two units per row tile, so the
+  // vector-memory path works in the background of the MFMAs.
   auto mainblk = [&](const uint8_t* st, const float* sb, const q2_u32x4 (&bf)[NT][4], const float (&dc)[NT],
-                     const float (&zc)[NT]) {
+                     const float (&zc)[NT], int64_t nb2, int nslot) {
     q2_u32x4 a0[4], a1[4];
     q2_f32x4 s0, s1;
     auto rd = [&](int i, q2_u32x4 (&av)[4], q2_f32x4& s4) {
@@ -801,6 +809,15 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
     rd(0, a0, s0);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
+      if (nb2 >= 0) {
+#pragma unroll
+        for (int un = 2 * i; un < 2 * i + 2; ++un)
+          if (un < NU) issue_unit(un, nb2, nslot);
+        if (i == MT - 1) {
+#pragma unroll
+          for (int un = 2 * MT; un < NU; ++un) issue_unit(un, nb2, nslot);
+        }
+      }
       if (i & 1) {
         if (i + 1 < MT) rd(i + 1, a0, s0);
         tile(i, a1, s1);
@@ -812,9 +829,10 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   };
 
   // Iteration ip covers the pair (2ip, 2ip+1) in ring slot ip & 1:
-  //   B1 (the pair has landed): copies of the next pair go out; row sums of
-  //      both blocks (twelve 16-row tasks); each wave decodes its block;
-  //   B2 (row sums visible): each wave runs the MFMAs of its block.
+  //   B1 (the pair has landed): row sums of both blocks (twelve 16-row
+  //      tasks); each wave decodes its block;
+  //   B2 (row sums visible): each wave runs the MFMAs of its block and, spread
+  //      over them, issues its copies of the next pair.
   // (Skewing the parities by half an iteration, so that one wave of a SIMD
   // decodes while the other multiplies, keeps the decoded operands live across
   // the loop and does not fit the 256 registers of a two-wave SIMD.)
@@ -824,11 +842,12 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
     for (int64_t ip = 0; 2 * ip < KB; ++ip) {
       const int slot = (int)(ip & 1);
       stage_barrier<0>();                 // B1: this pair has landed; every wave is done with the previous one
-      if (2 * ip + 2 < KB) {
-        issue_pair(2 * ip + 2, slot ^ 1);
-      } else if constexpr (LR) {
-        lr_st0 = 2 * (slot ^ 1);
-        issue_lr(lr_st0);
+      const int64_t nb2 = (2 * ip + 2 < KB) ? 2 * ip + 2 : -1;   // next pair, copied during the MFMAs
+      if constexpr (LR) {
+        if (nb2 < 0) {
+          lr_st0 = 2 * (slot ^ 1);
+          issue_lr(lr_st0);
+        }
       }
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {    // row sums: tasks wv and wv + 8 of twelve
@@ -847,7 +866,8 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       float dc[NT], zc[NT];
       decode(smem + OFF_W + (2 * slot + par) * WSTAGE, bp, bf, dc, zc);
       stage_barrier<63>();                // B2: row sums visible (no wait on the copies in flight)
-      if (bp < KB) mainblk(smem + (2 * slot + par) * XSTAGE, ss[slot][par], bf, dc, zc);
+      if (bp < KB) mainblk(smem + (2 * slot + par) * XSTAGE, ss[slot][par], bf, dc, zc, nb2, slot ^ 1);
+      else if (nb2 >= 0) issue_pair(nb2, slot ^ 1);
     }
   } else if constexpr (LR) {
     issue_lr(lr_st0);
