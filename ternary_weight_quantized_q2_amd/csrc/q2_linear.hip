@@ -605,7 +605,6 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   constexpr int XSTAGE = BM * 256;                           // one activation block
   constexpr int CODE_SLOT = (FMT == 0) ? 512 * 16 : 768 * 16; // one block's codes (2-bit: 384 chunks padded to 512)
   constexpr int WSTAGE = CODE_SLOT + ((FMT == 0) ? 1024 : 2048);
-  constexpr int XU = 6;                                      // activation copies per thread per pair
   constexpr int CU = (FMT == 0) ? 2 : 3;                     // code copies per thread per pair
   constexpr int OFF_W = 4 * XSTAGE;
   constexpr int OFF_S = OFF_W + 4 * WSTAGE;
@@ -626,17 +625,16 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   const int64_t row_bytes = (FMT == 0) ? K / 4 : K / 2;
   const NatConsts kc = (FMT == 0) ? q2_nat_consts() : q4_nat_consts();
 
-  // ---- copy sources.  Activation copy u of wave wv fills, in block u / 3 of
-  // the pair, the 64 chunk positions starting at ((u % 3) * 8 + wv) * 64.
-  uint32_t xoff[3];                       // copies u and u + 3 (the pair's two blocks) share an offset
-#pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int pos = (u * 8 + wv) * 64 + lane;
-    const int row = pos >> 4;
-    const int q = (pos & 15) ^ row_swz(row);
-    const int64_t gr = (m0 + row < M) ? row : M - 1 - m0;
-    xoff[u] = (uint32_t)(gr * K * 2 + q * 16);
-  }
+  // ---- copy sources.  Activations are copied in 16-row tasks: the pair has
+  // twelve (block q = t / 6, row tile t % 6), wave wv owns tasks wv and, for
+  // wv < 4, wv + 8 -- the same tasks whose row sums it computes, so it can wait
+  // for its own copies alone.  Copy k (0..3) of a task fills rows 4k .. 4k+3
+  // of the tile; lane l covers row 4k + (l >> 4), chunk position l & 15.
+  // M is a multiple of 96 here, so no activation row needs clamping.  The
+  // lane's source offset for copy k is its row offset (a multiple of 256) with
+  // the swizzled chunk in the low byte: row_swz(4k + (l >> 4)) = k | ((l >> 4) << 2).
+  const int xtasks = wv < 4 ? 2 : 1;
+  const uint32_t xsrc = (uint32_t)((lane >> 4) * K * 2) | (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) << 4);
   // Code copy v of wave wv: chunk index ci = (v * 8 + wv) * 64 + lane of the
   // pair, block ci / CPB, chunk ci % CPB of that block.
   constexpr int CPB = CODE_SLOT / 16;                          // chunk slots per block
@@ -678,21 +676,32 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
     if constexpr (FMT == 1) zhalf |= (uint32_t)((((uintptr_t)(a.z + r * KB)) >> 1) & 1) << j;
   }
 
-  // Copies of the pair starting at block b2, one unit at a time: units 0-5
-  // activations, then the codes, the scale words [and zero words].  Blocks
-  // past the end re-copy the last one.
-  constexpr int NU = XU + CU + ((FMT == 0) ? 1 : 2);
+  // Copies of the pair starting at block b2, one unit at a time: units 0-7 the
+  // activation copies of this wave's tasks (4 per task), then the codes, the
+  // scale words [and zero words].  Blocks past the end re-copy the last one.
+  constexpr int XUM = 8;
+  constexpr int NU = XUM + CU + ((FMT == 0) ? 1 : 2);
+  constexpr int NWU = NU - XUM;           // weight copies, issued after the activations
+  auto task_of = [&](int k2, int& q, int& it) {
+    const int task = wv + 8 * k2;
+    q = task >= 6 ? 1 : 0;
+    it = task - 6 * q;
+  };
   auto issue_unit = [&](int unit, int64_t b2, int slot) {
-    if (unit < XU) {
-      const int u = unit;
-      int64_t blk = b2 + u / 3;
-      blk = blk < KB ? blk : KB - 1;
-      const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + m0 * K + blk * BLOCK_K);
-      __builtin_amdgcn_global_load_lds(base + (uint64_t)xoff[u % 3],
-                                       (lds_void*)(smem + (2 * slot + u / 3) * XSTAGE + ((u % 3) * 8 + wv) * 1024),
-                                       16, 0, 0);
-    } else if (unit < XU + CU) {
-      const int v = unit - XU;
+    if (unit < XUM) {
+      const int k2 = unit >> 2, kk = unit & 3;
+      if (k2 < xtasks) {
+        int q, it;
+        task_of(k2, q, it);
+        int64_t blk = b2 + q;
+        blk = blk < KB ? blk : KB - 1;
+        const int r0 = 16 * it + 4 * kk;                         // first tile row of this copy
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + (m0 + r0) * K + blk * BLOCK_K);
+        __builtin_amdgcn_global_load_lds(base + (uint64_t)(xsrc ^ (uint32_t)(kk << 4)),
+                                         (lds_void*)(smem + (2 * slot + q) * XSTAGE + r0 * 256), 16, 0, 0);
+      }
+    } else if (unit < XUM + CU) {
+      const int v = unit - XUM;
       const int ci0 = (v * 8 + wv) * 64;                       // uniform
       const int q = ci0 / CPB;
       int64_t blk = b2 + q;
@@ -706,7 +715,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       blk = blk < KB ? blk : KB - 1;
       const int64_t si = 2 * (s_idx + blk);
       const int dst = OFF_W + (2 * slot + (wv >> 2)) * WSTAGE + CODE_SLOT + (wv & 3) * 256;
-      if (unit == XU + CU) {
+      if (unit == XUM + CU) {
         const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.s);
         __builtin_amdgcn_global_load_lds(sp + (si - (int64_t)(((uintptr_t)sp + si) & 3)), (lds_void*)(smem + dst), 4,
                                          0, 0);
@@ -716,10 +725,6 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
                                          (lds_void*)(smem + dst + 1024), 4, 0, 0);
       }
     }
-  };
-  auto issue_pair = [&](int64_t b2, int slot) {
-#pragma unroll
-    for (int un = 0; un < NU; ++un) issue_unit(un, b2, slot);
   };
   // Low-rank operands into the two activation stages starting at stage st0.
   auto issue_lr = [&](int st0) {
@@ -748,6 +753,23 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
 
   const uint32_t sone = (FMT == 0) ? 0xBFA0BFA0u : 0xBF80BF80u;   // bf16 -1.25 / -1 pairs
   const q2_u32x4 sones = q2_u32x4{sone, sone, sone, sone};
+  // Row sums of this wave's tasks of the pair starting at block b2 (slot `slot`).
+  auto row_sums = [&](int64_t b2, int slot) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      if (k2 < xtasks) {
+        int q, it;
+        task_of(k2, q, it);
+        if (b2 + q < KB) {
+          const uint8_t* st = smem + (2 * slot + q) * XSTAGE;
+          q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) s4 = mfma(afrag(st, it, t), sones, s4);
+          if (c == 0) *reinterpret_cast<q2_f32x4*>(&ss[slot][q][16 * it + 4 * g]) = s4;
+        }
+      }
+    }
+  };
 
   q2_f32x4 acc[MT][NT];
 #pragma unroll
@@ -809,13 +831,13 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
     rd(0, a0, s0);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      if (nb2 >= 0) {
+      if (nb2 >= 0) {                     // tiles 0-3: activation copies, tile 4: weight copies
+        if (i < 4) {
 #pragma unroll
-        for (int un = 2 * i; un < 2 * i + 2; ++un)
-          if (un < NU) issue_unit(un, nb2, nslot);
-        if (i == MT - 1) {
+          for (int un = 2 * i; un < 2 * i + 2; ++un) issue_unit(un, nb2, nslot);
+        } else if (i == 4) {
 #pragma unroll
-          for (int un = 2 * MT; un < NU; ++un) issue_unit(un, nb2, nslot);
+          for (int un = XUM; un < NU; ++un) issue_unit(un, nb2, nslot);
         }
       }
       if (i & 1) {
@@ -827,21 +849,31 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       }
     }
   };
+  // This wave's activation copies of the next pair have landed once only its
+  // NWU weight copies (issued after them) may still be in flight.
+  auto next_row_sums = [&](int64_t nb2, int nslot) {
+    if (nb2 >= 0) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt((NWU & 15) | (7 << 4) | (15 << 8) | ((NWU >> 4) << 14));   // vmcnt(NWU)
+      asm volatile("" ::: "memory");
+      row_sums(nb2, nslot);
+    }
+  };
 
-  // Iteration ip covers the pair (2ip, 2ip+1) in ring slot ip & 1:
-  //   B1 (the pair has landed): row sums of both blocks (twelve 16-row
-  //      tasks); each wave decodes its block;
-  //   B2 (row sums visible): each wave runs the MFMAs of its block and, spread
-  //      over them, issues its copies of the next pair.
-  // (Skewing the parities by half an iteration, so that one wave of a SIMD
-  // decodes while the other multiplies, keeps the decoded operands live across
-  // the loop and does not fit the 256 registers of a two-wave SIMD.)
+  // Iteration ip covers the pair (2ip, 2ip+1) in ring slot ip & 1.  At its
+  // top barrier the pair's copies and row sums are complete; each wave then
+  // decodes its block and runs its MFMAs, issuing its copies of the next pair
+  // along the way, and finally computes the row sums of the tasks it copied
+  // (after its own copies have landed), which the next top barrier publishes.
+  // There is no other barrier, so the two waves of a SIMD drift apart and one
+  // decodes while the other multiplies.
   int lr_st0 = 2;                         // activation stages holding the low-rank operands
   if (KB > 0) {
-    issue_pair(0, 0);
+    for (int un = 0; un < NU; ++un) issue_unit(un, 0, 0);
+    next_row_sums(0, 0);
     for (int64_t ip = 0; 2 * ip < KB; ++ip) {
       const int slot = (int)(ip & 1);
-      stage_barrier<0>();                 // B1: this pair has landed; every wave is done with the previous one
+      stage_barrier<0>();                 // the pair's copies and row sums are complete; the previous pair is done
       const int64_t nb2 = (2 * ip + 2 < KB) ? 2 * ip + 2 : -1;   // next pair, copied during the MFMAs
       if constexpr (LR) {
         if (nb2 < 0) {
@@ -849,25 +881,16 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
           issue_lr(lr_st0);
         }
       }
-#pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {    // row sums: tasks wv and wv + 8 of twelve
-        const int task = wv + 8 * k2;
-        const int q = task >= 6 ? 1 : 0, it = task - 6 * q;
-        if (task < 12 && 2 * ip + q < KB) {
-          const uint8_t* st = smem + (2 * slot + q) * XSTAGE;
-          q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) s4 = mfma(afrag(st, it, t), sones, s4);
-          if (c == 0) *reinterpret_cast<q2_f32x4*>(&ss[slot][q][16 * it + 4 * g]) = s4;
-        }
-      }
       const int64_t bp = 2 * ip + par;
       q2_u32x4 bf[NT][4];
       float dc[NT], zc[NT];
       decode(smem + OFF_W + (2 * slot + par) * WSTAGE, bp, bf, dc, zc);
-      stage_barrier<63>();                // B2: row sums visible (no wait on the copies in flight)
-      if (bp < KB) mainblk(smem + (2 * slot + par) * XSTAGE, ss[slot][par], bf, dc, zc, nb2, slot ^ 1);
-      else if (nb2 >= 0) issue_pair(nb2, slot ^ 1);
+      if (bp < KB) {
+        mainblk(smem + (2 * slot + par) * XSTAGE, ss[slot][par], bf, dc, zc, nb2, slot ^ 1);
+      } else if (nb2 >= 0) {
+        for (int un = 0; un < NU; ++un) issue_unit(un, nb2, slot ^ 1);
+      }
+      next_row_sums(nb2, slot ^ 1);
     }
   } else if constexpr (LR) {
     issue_lr(lr_st0);
@@ -1306,9 +1329,9 @@ static hipError_t run_gemm_auto(const LinearArgs& a, hipStream_t stream) {
   // operands staged in LDS the tile no longer fits twice, so that case keeps 96 x 192.
   const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
 #ifndef Q2_NO_KPAIR
-  // Eight-wave 96 x 192 tiles when they fill the chip (the low-rank branch only
-  // in its LDS-staged form).
-  if (a.M >= 96 && tiles(96, 192) >= 256 && (a.r == 0 || lr_lds)) return run_gemm_kpair<FMT>(a, stream);
+  // Eight-wave 96 x 192 tiles when they fill the chip and M is a whole number
+  // of tiles (the low-rank branch only in its LDS-staged form).
+  if (a.M % 96 == 0 && tiles(96, 192) >= 256 && (a.r == 0 || lr_lds)) return run_gemm_kpair<FMT>(a, stream);
 #endif
   if (!lr_lds && a.M >= 48 && tiles(48, 192) >= 512) return run_gemm<FMT, 48, 192>(a, stream);
   if (a.M >= 96 && tiles(96, 192) >= 256) return run_gemm<FMT, 96, 192>(a, stream);

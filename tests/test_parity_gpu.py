@@ -163,9 +163,11 @@ def test_linear_ragged(path, m, n, k):
     assert_close(y, O.q2_linear(xb, p_ref, s_ref), f"{path} M={m} N={n} K={k}")
 
 
-# One case per GEMM tile configuration (48x192, 96x192, 64x128, 32x128, 32x64),
-# each ragged in M and N so the clamped rows and columns are exercised.
-TILE_CASES = [(203, 24700, 384), (500, 8500, 256), (250, 8100, 256), (40, 16300, 256), (20, 300, 256)]
+# One case per GEMM tile configuration (eight-wave 96x192 with an odd and a
+# single block, 48x192, 96x192, 64x128, 32x128, 32x64), ragged in N and,
+# where the configuration allows, in M.
+TILE_CASES = [(192, 24700, 384), (96, 49300, 128), (203, 24700, 384), (500, 8500, 256), (250, 8100, 256),
+              (40, 16300, 256), (20, 300, 256)]
 
 
 @pytest.mark.parametrize("m,n,k", TILE_CASES)
@@ -268,7 +270,7 @@ def lowrank_case(cfg, m, k, n, r):
                                      (16, 1280, 333, 64), (200, 640, 250, 7), (96, 3072, 192, 64),
                                      (257, 512, 300, 72), (100, 256, 70, 8), (33, 1280, 190, 16), (1, 128, 5, 1),
                                      # eight-wave 96x192 tiles: odd block count, a single block
-                                     (200, 640, 24700, 32), (203, 128, 24700, 8)])
+                                     (192, 640, 24700, 32), (96, 128, 49300, 8), (203, 640, 24700, 16)])
 def test_lowrank_parity(m, k, n, r):
     p_dev, s_dev, p_ref, s_ref, xb, x, a, b, A, B = lowrank_case(50, m, k, n, r)
     y = q2.q2_linear_lowrank(x, p_dev, s_dev, A, B).cpu().numpy()
