@@ -35,12 +35,37 @@ Q4_BYTES_PER_WEIGHT = 0.53125
 ROTATE_BYTES = 1 << 30
 
 
+def _code_only(text):
+    """C/C++/HIP source with comments removed and whitespace collapsed, so the
+    hash below follows the code and not its commentary."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":                       # string or character literal
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_quantized_q2_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -270,7 +295,7 @@ def main():
             "activations": "bf16 N(0,1)",
             "parallelism": "single GPU",
         },
-        "roofline": {"bound": "mfma", "kernel": "gemm_kernel (Q2_0, M=1536)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_kpair_kernel (Q2_0, M=1536)",
                      "achieved": round(gemm_ach, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "roofline_gemv": {"bound": "hbm", "kernel": "gemv_kernel (Q2_0, M=1)", "achieved": round(gemv_ach, 2),

@@ -17,10 +17,13 @@
 // sum x (q - 1) / 4 exactly in real arithmetic; the 4-bit path starts it at
 // -(1 + z/16) * sum(x) and ends at sum x (q - z) / 16.
 //
-// Because a dword's two halves are 16 bits apart, a 2-bit pair holds codes
-// (j, j+8) of the dword's 16 codes and a 4-bit pair holds codes (j, j+4) of
-// its 8 codes.  The activations are stored in shared memory in the same pair
-// order, built once per block by the staging threads.
+// Two pair orders are used.  Strided pairs (GEMV): because a dword's two
+// halves are 16 bits apart, one shift and one and-or make a 2-bit pair of codes
+// (j, j+8) of the dword's 16 codes, or a 4-bit pair of codes (j, j+4) of its 8;
+// the activations are then stored in shared memory in the same pair order by
+// the staging threads.  Consecutive pairs (GEMM): the activation fragments are
+// read from shared memory as copied, so the weight pairs hold codes (2p, 2p+1);
+// building them costs a byte permute and a packed shift more per dword.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -594,9 +594,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 // Their partial accumulators are summed once, through LDS, at the end (the
 // block-scaled sum is linear in the blocks).  One iteration covers a pair of
 // blocks: the pair's copies were issued during the previous iteration into the
-// other half of a two-pair ring; the row sums of both blocks are computed at
-// the top of the iteration (twelve 16-row tasks, three per SIMD) and published
-// through LDS before the main MFMAs.
+// other half of a two-pair ring.  The pair's activations form twelve 16-row
+// tasks; each wave copies its own tasks and, once its copies have landed,
+// computes their row sums on the matrix cores, so the only barrier is the one
+// that starts an iteration.
 template <int FMT, bool LR>
 __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles_m) {
   constexpr int BM = 96, BN = 192, MT = 6, NT = 3;
