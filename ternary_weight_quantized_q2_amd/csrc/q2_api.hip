@@ -90,6 +90,14 @@ int forced_path() {
   return 0;
 }
 
+// Test-only override of the GEMM kernel configuration: Q2_GEMM_TILE=<name>
+// (-1 for an unknown name).
+int forced_cfg() {
+  const char* v = std::getenv("Q2_GEMM_TILE");
+  if (v == nullptr || *v == 0) return 0;
+  return q2dev::gemm_config_id(v);
+}
+
 int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* s, const uint16_t* z, float* y,
                   int64_t M, int64_t N, int64_t K, const uint16_t* lr_t, const uint16_t* lr_b, int64_t r,
                   hipStream_t stream) {
@@ -99,7 +107,9 @@ int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* 
   a.lr_t = lr_t; a.lr_b = lr_b; a.r = (int)r;
   int path = forced_path();
   if (path == 1 && M > 16) path = 0;
-  return hip_status(q2dev::launch_linear(a, fmt, path, stream), fmt == 0 ? "q2 linear launch" : "q4 linear launch");
+  const int cfg = forced_cfg();
+  if (cfg < 0) return fail(Q2_ERR_ARG, "unknown Q2_GEMM_TILE configuration");
+  return hip_status(q2dev::launch_linear(a, fmt, path, cfg, stream), fmt == 0 ? "q2 linear launch" : "q4 linear launch");
 }
 
 }  // namespace

@@ -20,6 +20,7 @@
 // Every summation order is fixed, so results are bitwise reproducible.
 #include "q2_device.h"
 #include "q2_internal.h"
+#include <cstring>
 
 namespace q2dev {
 
@@ -979,6 +980,379 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
 }
 
 // ============================================================================
+// GEMM for few rows: KG groups of four waves split the K blocks
+// ============================================================================
+// Consecutive workgroup ids are dispatched to the eight XCDs in turn.  This
+// hands each XCD a contiguous range of tiles instead; tiles are numbered
+// row-fastest, so the row tiles that read the same weight columns meet in one
+// L2 and the weights come from HBM about once.
+__device__ __forceinline__ int xcd_tile(int b, int tiles) {
+  const int per = tiles >> 3, rem = tiles & 7;
+  const int xcd = b & 7, local = b >> 3;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+}
+
+// With few activation rows a workgroup tile carries little matrix-core work
+// per block, and one wave per SIMD would expose every LDS, matrix-core and
+// barrier latency of a block in turn.  Here a workgroup of KG groups of four
+// waves owns a BM x BN tile (BM = 16 MT, BN = 64 NT); wave w computes the
+// BM x 16 NT columns w & 3 from the blocks KG s + (w >> 2) of each set s of KG
+// consecutive blocks, so a SIMD runs KG independent waves on the same output
+// columns while every block's weights are still decoded once per workgroup.
+// The KG partial sums are added in group order, through LDS, at the end.
+// A ring of NSET sets: the copies of set s + NSET - 1 are issued during set s,
+// spread over its row tiles, so with three sets a copy has two sets' time to
+// land.  Each wave copies whole 16-row activation tiles and computes their row
+// sums once its own copies have landed; one barrier per set publishes them.
+// Rows past M are clamped on the copy side and dropped at the store.
+template <int FMT, int MT, int NT, int KG, int NSET>
+__global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int tiles_m) {
+  constexpr int W = 4 * KG;                                   // waves
+  constexpr int BM = 16 * MT, BN = 64 * NT;
+  constexpr int DW = WFmt<FMT>::LANE_DW;
+  constexpr int BBYTES = WFmt<FMT>::BLOCK_BYTES;
+  constexpr int XSTAGE = BM * 256;                            // one activation block
+  constexpr int CPB = (FMT == 0) ? 2 * BN : 4 * BN;           // 16-byte code chunks per block
+  constexpr int CODE_SLOT = CPB * 16;
+  constexpr int SWORDS = 4 * BN;                              // bytes of scale (zero) words per block
+  constexpr int WSTAGE = CODE_SLOT + ((FMT == 0) ? SWORDS : 2 * SWORDS);
+  constexpr int NST = NSET * KG;                              // block stages of the ring
+  constexpr int OFF_W = NST * XSTAGE;
+  constexpr int OFF_S = OFF_W + NST * WSTAGE;
+  constexpr int SMEM = OFF_S + NST * BM * 4;
+  constexpr int NTASK = KG * MT;                              // 16-row activation tiles per set
+  constexpr int XT = (NTASK + W - 1) / W;                     // tasks per wave (at most)
+  constexpr int XUM = 4 * XT;                                 // activation copy units per wave
+  constexpr int CINS = KG * CPB / 64;                         // 64-chunk code copies per set
+  constexpr int CU = (CINS + W - 1) / W;                      // code copies per wave
+  constexpr int NWU = CU + ((FMT == 0) ? 1 : 2);              // weight copies per wave
+  constexpr int NU = XUM + NWU;
+  constexpr int UPT = (NU + MT - 1) / MT;                     // copy units issued per row tile
+  static_assert(NSET == 2 || NSET == 3, "ring depth");
+  static_assert(XT <= 2, "activation tasks per wave");
+  static_assert(CPB % 64 == 0, "a code copy must not straddle two blocks");
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert((KG - 1) * BM * BN * 4 <= OFF_S, "reduction buffer");
+  __shared__ __align__(16) uint8_t smem[SMEM];
+  float (*const ss)[KG][BM] = reinterpret_cast<float (*)[KG][BM]>(smem + OFF_S);   // [slot][block of set][row]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wv & 3, kg = wv >> 2;
+  const int c = lane & 15, g = lane >> 4;
+  const int tiles_n = (int)((a.N + BN - 1) / BN);
+  const int tile = xcd_tile((int)blockIdx.x, tiles_m * tiles_n);
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t nw = n0 + wn * (BN / 4);
+  const int64_t M = a.M, N = a.N, K = a.K, KB = K / BLOCK_K;
+  const int64_t NS = (KB + KG - 1) / KG;                      // sets
+  const int64_t row_bytes = (FMT == 0) ? K / 4 : K / 2;
+  const NatConsts kc = (FMT == 0) ? q2_nat_consts() : q4_nat_consts();
+
+  // ---- copy sources.  Task t of a set is row tile t % MT of block t / MT;
+  // wave wv owns tasks wv, wv + W, ...  Copy kk (0..3) of a task fills tile
+  // rows 4kk .. 4kk+3; lane l covers row 4kk + (l >> 4), chunk position l & 15,
+  // which holds chunk (l & 15) ^ row_swz(row).  The lane's byte offset from
+  // the tile's block base (row clamped to M - 1) fits 32 bits since BM <= 128
+  // and K <= 2^24.
+  int xtasks = 0;
+#pragma unroll
+  for (int k2 = 0; k2 < XT; ++k2) xtasks += (wv + W * k2 < NTASK) ? 1 : 0;
+  const int set_units = 4 * xtasks + NWU;                     // copies this wave issues per set
+  uint32_t xoff[XT][4];
+#pragma unroll
+  for (int k2 = 0; k2 < XT; ++k2) {
+    const int it = (wv + W * k2) % MT;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int rin = 4 * kk + (lane >> 4);
+      int64_t gr = m0 + 16 * it + rin;
+      gr = gr < M ? gr : M - 1;
+      xoff[k2][kk] = (uint32_t)((gr - m0) * K * 2) | (uint32_t)(((lane & 15) ^ row_swz(rin)) << 4);
+    }
+  }
+  // Code copy v of wave wv: copy index ci = v * W + wv of the set (clamped to
+  // the last one, which is then copied twice with identical bytes), block
+  // ci * 64 / CPB, chunks from (ci * 64) % CPB of that block.
+  uint32_t woff[CU];
+#pragma unroll
+  for (int v = 0; v < CU; ++v) {
+    int ci = v * W + wv;
+    ci = ci < CINS ? ci : CINS - 1;
+    const int pos = (ci * 64) % CPB + lane;
+    int col, unit;
+    if constexpr (FMT == 0) {
+      col = pos >> 1;
+      unit = ((pos & 1) ^ ((col >> 2) & 1)) << 4;
+    } else {
+      col = pos >> 2;
+      unit = ((pos & 3) ^ ((col >> 1) & 3)) << 4;
+    }
+    const int64_t gc = (n0 + col < N) ? col : N - 1 - n0;
+    woff[v] = (uint32_t)(gc * row_bytes + unit);
+  }
+  // Scale / zero words: the waves of group kg cover block kg of the set, wave
+  // wn the columns sq * 64 + lane with sq = min(wn, NT - 1) (waves past NT
+  // repeat the last group's copy, identical bytes to the same place).
+  const int sq = wn < NT ? wn : NT - 1;
+  int64_t sgc = n0 + sq * 64 + lane;
+  sgc = sgc < N ? sgc : N - 1;
+  const int64_t s_idx = sgc * KB;
+
+  // ---- read side
+  int aoff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) aoff[t] = c * 256 + (((4 * g + t) ^ row_swz(c)) << 4);
+  const int coff = (FMT == 0) ? c * 32 + ((((g >> 1) ^ ((c >> 2) & 1)) << 4) | ((g & 1) << 3))
+                              : c * 64 + ((g ^ ((c >> 1) & 3)) << 4);
+  uint32_t shalf = 0, zhalf = 0;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    int64_t r = nw + 16 * j + c;
+    r = r < N ? r : N - 1;
+    shalf |= (uint32_t)((((uintptr_t)(a.s + r * KB)) >> 1) & 1) << j;
+    if constexpr (FMT == 1) zhalf |= (uint32_t)((((uintptr_t)(a.z + r * KB)) >> 1) & 1) << j;
+  }
+
+  // Copies of set `set` into ring slot `slot`, one unit at a time: units
+  // 0 .. XUM-1 the activation copies of this wave's tasks, then the codes, the
+  // scale words [and zero words].  Blocks past the end re-copy the last one.
+  auto issue_unit = [&](int unit, int64_t set, int slot) {
+    const int64_t b0 = KG * set;
+    if (unit < XUM) {
+      const int k2 = unit >> 2, kk = unit & 3;
+      if (k2 < xtasks) {
+        const int task = wv + W * k2;
+        const int q = task / MT, it = task - q * MT;
+        int64_t blk = b0 + q;
+        blk = blk < KB ? blk : KB - 1;
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + m0 * K + blk * BLOCK_K);
+        __builtin_amdgcn_global_load_lds(base + (uint64_t)xoff[k2][kk],
+                                         (lds_void*)(smem + (slot * KG + q) * XSTAGE + (16 * it + 4 * kk) * 256),
+                                         16, 0, 0);
+      }
+    } else if (unit < XUM + CU) {
+      const int v = unit - XUM;
+      int ci = v * W + wv;                                     // uniform
+      ci = ci < CINS ? ci : CINS - 1;
+      const int q = ci * 64 / CPB;
+      int64_t blk = b0 + q;
+      blk = blk < KB ? blk : KB - 1;
+      const uint8_t* base = a.w + n0 * row_bytes + blk * BBYTES;
+      __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v],
+                                       (lds_void*)(smem + OFF_W + (slot * KG + q) * WSTAGE + ((ci * 64) % CPB) * 16),
+                                       16, 0, 0);
+    } else {
+      int64_t blk = b0 + kg;
+      blk = blk < KB ? blk : KB - 1;
+      const int64_t si = 2 * (s_idx + blk);
+      const int dst = OFF_W + (slot * KG + kg) * WSTAGE + CODE_SLOT + sq * 256;
+      if (unit == XUM + CU) {
+        const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.s);
+        __builtin_amdgcn_global_load_lds(sp + (si - (int64_t)(((uintptr_t)sp + si) & 3)), (lds_void*)(smem + dst), 4,
+                                         0, 0);
+      } else if constexpr (FMT == 1) {
+        const uint8_t* zp = reinterpret_cast<const uint8_t*>(a.z);
+        __builtin_amdgcn_global_load_lds(zp + (si - (int64_t)(((uintptr_t)zp + si) & 3)),
+                                         (lds_void*)(smem + dst + SWORDS), 4, 0, 0);
+      }
+    }
+  };
+  auto issue_set = [&](int64_t set, int slot) {
+    for (int un = 0; un < NU; ++un) issue_unit(un, set, slot);
+  };
+  auto afrag = [&](const uint8_t* st, int i, int t) -> q2_u32x4 {
+    return *reinterpret_cast<const q2_u32x4*>(st + i * 4096 + aoff[t]);
+  };
+
+  const uint32_t sone = (FMT == 0) ? 0xBFA0BFA0u : 0xBF80BF80u;   // bf16 -1.25 / -1 pairs
+  const q2_u32x4 sones = q2_u32x4{sone, sone, sone, sone};
+  // Row sums of this wave's tasks of set `set` (slot `slot`).
+  auto row_sums = [&](int64_t set, int slot) {
+#pragma unroll
+    for (int k2 = 0; k2 < XT; ++k2) {
+      if (k2 < xtasks) {
+        const int task = wv + W * k2;
+        const int q = task / MT, it = task - q * MT;
+        if (KG * set + q < KB) {
+          const uint8_t* st = smem + (slot * KG + q) * XSTAGE;
+          q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) s4 = mfma(afrag(st, it, t), sones, s4);
+          if (c == 0) *reinterpret_cast<q2_f32x4*>(&ss[slot][q][16 * it + 4 * g]) = s4;
+        }
+      }
+    }
+  };
+  // Wait until at most n of this wave's copies are in flight (n is uniform and
+  // one of the per-set counts).
+  auto wait_copies = [&](int n) {
+    asm volatile("" ::: "memory");
+    if (n == 0) {
+      __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));
+    } else if (n == NWU) {
+      __builtin_amdgcn_s_waitcnt((NWU & 15) | (7 << 4) | (15 << 8) | ((NWU >> 4) << 14));
+    } else if (n == NWU + 4) {
+      __builtin_amdgcn_s_waitcnt(((NWU + 4) & 15) | (7 << 4) | (15 << 8) | (((NWU + 4) >> 4) << 14));
+    } else {
+      __builtin_amdgcn_s_waitcnt(((NWU + 8) & 15) | (7 << 4) | (15 << 8) | (((NWU + 8) >> 4) << 14));
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  q2_f32x4 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Decode of one block's weights for this wave's columns (from its weight stage).
+  auto decode = [&](const uint8_t* wst, int64_t blk, q2_u32x4 (&bf)[NT][4], float (&dc)[NT], float (&zc)[NT]) {
+    const uint32_t pmask = (uint32_t)(blk & 1) ? 0xFFu : 0u;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int col0 = wn * (BN / 4) + 16 * j;
+      uint32_t w[DW];
+      if constexpr (FMT == 0) {
+        const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(wst + col0 * 32 + coff);
+        w[0] = v[0]; w[1] = v[1];
+      } else {
+        const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(wst + col0 * 64 + coff);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+      }
+      decode_block_nat<FMT>(w, bf[j], kc);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + (col0 + c) * 4);
+      dc[j] = f16_to_f32((uint16_t)(sw >> ((((shalf ^ pmask) >> j) & 1) * 16)));
+      if constexpr (FMT == 1) {
+        const uint32_t zw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + SWORDS + (col0 + c) * 4);
+        zc[j] = f16_to_f32((uint16_t)(zw >> ((((zhalf ^ pmask) >> j) & 1) * 16)));
+      } else {
+        zc[j] = 0.f;
+      }
+    }
+  };
+  // MFMAs of one block over the staged activations `st`, row sums `sb`; the
+  // copies of set `cset` (if >= 0) are issued UPT units per row tile.
+  auto mainblk = [&](const uint8_t* st, const float* sb, const q2_u32x4 (&bf)[NT][4], const float (&dc)[NT],
+                     const float (&zc)[NT], int64_t cset, int cslot) {
+    q2_u32x4 a0[4], a1[4];
+    q2_f32x4 s0, s1;
+    auto rd = [&](int i, q2_u32x4 (&av)[4], q2_f32x4& s4) {
+      s4 = *reinterpret_cast<const q2_f32x4*>(&sb[16 * i + 4 * g]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) av[t] = afrag(st, i, t);
+    };
+    auto tile = [&](int i, const q2_u32x4 (&av)[4], q2_f32x4 s4) {
+      q2_f32x4 tmp[NT];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          tmp[j] = mfma(av[t], bf[j][t], t == 0 ? block_cinit<FMT>(s4, zc[j]) : tmp[j]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(dc[j], tmp[j][e], acc[i][j][e]);
+    };
+    rd(0, a0, s0);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (cset >= 0) {
+#pragma unroll
+        for (int un = UPT * i; un < UPT * i + UPT; ++un)
+          if (un < NU) issue_unit(un, cset, cslot);
+      }
+      if (i & 1) {
+        if (i + 1 < MT) rd(i + 1, a0, s0);
+        tile(i, a1, s1);
+      } else {
+        if (i + 1 < MT) rd(i + 1, a1, s1);
+        tile(i, a0, s0);
+      }
+    }
+  };
+
+  // Set s sits in ring slot s % NSET.  Before the top barrier of set s, every
+  // wave has waited for its own copies of set s and written their row sums;
+  // the barrier publishes them and marks set s - 1 done, so its slot receives
+  // the copies of set s + NSET - 1 during set s.  With NSET = 2 a set's weight
+  // copies are the last ones waited for (vmcnt(0) at its top barrier); with
+  // NSET = 3 each wave has waited for all of set s's copies at the end of set
+  // s - 1, leaving only the copies of set s + 1 in flight.
+  if (KB > 0) {
+    issue_set(0, 0);
+    if constexpr (NSET == 3) {
+      if (NS > 1) issue_set(1, 1);
+      wait_copies(NS > 1 ? set_units : 0);
+    } else {
+      wait_copies(NWU);
+    }
+    row_sums(0, 0);
+    int slot = 0;
+    for (int64_t s = 0; s < NS; ++s) {
+      if constexpr (NSET == 3) stage_barrier<63>();
+      else stage_barrier<0>();
+      const int64_t cset = (s + NSET - 1 < NS) ? s + NSET - 1 : -1;   // the set copied during this one
+      const int cslot = (slot + NSET - 1 >= NSET) ? slot - 1 : slot + NSET - 1;   // (s + NSET - 1) % NSET
+      const int64_t bp = KG * s + kg;
+      if (bp < KB) {
+        q2_u32x4 bf[NT][4];
+        float dc[NT], zc[NT];
+        decode(smem + OFF_W + (slot * KG + kg) * WSTAGE, bp, bf, dc, zc);
+        mainblk(smem + (slot * KG + kg) * XSTAGE, ss[slot][kg], bf, dc, zc, cset, cslot);
+      } else if (cset >= 0) {
+        issue_set(cset, cslot);
+      }
+      const int nslot = (slot + 1 == NSET) ? 0 : slot + 1;
+      if (s + 1 < NS) {
+        // The copies of set s + 1 have landed once only those issued after
+        // them may be in flight: with two sets its own weight copies, with
+        // three the copies of set s + 2 issued during this set.
+        if constexpr (NSET == 3) wait_copies(cset >= 0 ? set_units : 0);
+        else wait_copies(NWU);
+        row_sums(s + 1, nslot);
+      }
+      slot = nslot;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);          // every copy of this wave has landed
+  __syncthreads();                        // and every wave is done reading the stages
+
+  // Partial sums of groups 1 .. KG-1 -> LDS -> added in group order by group 0.
+  float* const red = reinterpret_cast<float*>(smem);
+  constexpr int PART = MT * NT * 4 * 64;  // floats per wave
+  if (kg > 0) {
+    float* const mine = red + ((kg - 1) * 4 + wn) * PART;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine[((i * NT + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+  }
+  __syncthreads();
+  if (kg == 0) {
+    const float fin = (FMT == 0) ? 4.f : 16.f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int64_t n = nw + 16 * j + c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = acc[i][j][e];
+#pragma unroll
+          for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
+          const int64_t m = m0 + 16 * i + 4 * g + e;
+          if (m < M && n < N) a.y[m * N + n] = v * fin;
+        }
+      }
+    }
+  }
+}
+
+// ============================================================================
 // GEMV, M <= 16
 // ============================================================================
 constexpr int GEMV_XQ = 2;                        // 16-activation staging chunks per thread per pass
@@ -1321,31 +1695,97 @@ static hipError_t run_gemm_kpair(const LinearArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int FMT, int MT, int NT, int KG, int NSET>
+static hipError_t run_gemm_kgroup(const LinearArgs& a, hipStream_t stream) {
+  constexpr int BM = 16 * MT, BN = 64 * NT;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles = tiles_m * ((a.N + BN - 1) / BN);
+  if (tiles > 0x7fffffff || a.r > 0) return hipErrorInvalidValue;   // no low-rank epilogue here
+  hipLaunchKernelGGL((gemm_kgroup_kernel<FMT, MT, NT, KG, NSET>), dim3((unsigned)tiles), dim3(256 * KG), 0, stream,
+                     a, (int)tiles_m);
+  return hipGetLastError();
+}
+
+// GEMM kernel configurations.  The automatic choice picks one of them; tests
+// can force any by name (gemm_config_id), so every configuration is exercised
+// whatever shapes the automatic choice gives it.
+static const char* const kGemmCfgNames[] = {"auto",    "kpair",   "w48x192", "w96x192", "w64x128",
+                                            "w32x128", "w32x64",  "kg2x1x4", "kg4x2x2", "kg2x1x2",
+                                            "kg2x2x4", "kg2x2x2", "kg2x1x4r3"};
+enum GemmCfg { CFG_AUTO, CFG_KPAIR, CFG_W48x192, CFG_W96x192, CFG_W64x128, CFG_W32x128, CFG_W32x64, CFG_KG2x1x4,
+               CFG_KG4x2x2, CFG_KG2x1x2, CFG_KG2x2x4, CFG_KG2x2x2, CFG_KG2x1x4R3, CFG_COUNT };
+static_assert(sizeof kGemmCfgNames / sizeof kGemmCfgNames[0] == CFG_COUNT, "configuration names");
+
+int gemm_config_id(const char* name) {
+  for (int i = 0; i < CFG_COUNT; ++i)
+    if (std::strcmp(name, kGemmCfgNames[i]) == 0) return i;
+  return -1;
+}
+
 template <int FMT>
-static hipError_t run_gemm_auto(const LinearArgs& a, hipStream_t stream) {
-  // Prefer the largest tile that still gives a few waves of workgroups over
-  // the 256 compute units.
-  auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  // 48 x 192 tiles run two workgroups (eight waves) per CU; with the low-rank
-  // operands staged in LDS the tile no longer fits twice, so that case keeps 96 x 192.
+static hipError_t run_gemm_cfg(const LinearArgs& a, int cfg, hipStream_t stream) {
   const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
+  switch (cfg) {
+    case CFG_KPAIR:   // whole 96-row tiles; the branch only in its LDS-staged form
+      if (a.M % 96 != 0 || (a.r > 0 && !lr_lds)) return hipErrorInvalidValue;
+      return run_gemm_kpair<FMT>(a, stream);
+    case CFG_W48x192: return run_gemm<FMT, 48, 192>(a, stream);
+    case CFG_W96x192: return run_gemm<FMT, 96, 192>(a, stream);
+    case CFG_W64x128: return run_gemm<FMT, 64, 128>(a, stream);
+    case CFG_W32x128: return run_gemm<FMT, 32, 128>(a, stream);
+    case CFG_W32x64: return run_gemm<FMT, 32, 64>(a, stream);
+    case CFG_KG2x1x4: return run_gemm_kgroup<FMT, 2, 1, 4, 2>(a, stream);
+    case CFG_KG4x2x2: return run_gemm_kgroup<FMT, 4, 2, 2, 2>(a, stream);
+    case CFG_KG2x1x2: return run_gemm_kgroup<FMT, 2, 1, 2, 2>(a, stream);
+    case CFG_KG2x2x4: return run_gemm_kgroup<FMT, 2, 2, 4, 2>(a, stream);
+    case CFG_KG2x2x2: return run_gemm_kgroup<FMT, 2, 2, 2, 2>(a, stream);
+    case CFG_KG2x1x4R3: return run_gemm_kgroup<FMT, 2, 1, 4, 3>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int FMT>
+static int gemm_auto_cfg(const LinearArgs& a) {
+  auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
+  const int64_t KB = a.K / BLOCK_K;
+  // Up to 384 rows without the low-rank branch: K-group tiles, the widest
+  // whose workgroup count still covers a good part of the chip (measured on
+  // the 3072 / 9216 / 12288 and 2560 / 9728 shapes); Q2_0 with long K keeps a
+  // third set in flight.
+  if (a.r == 0 && a.M <= 384) {
+    const int narrow = (FMT == 0 && KB >= 64) ? CFG_KG2x1x4R3 : CFG_KG2x1x4;
+    if (a.M <= 64) return tiles(32, 128) >= 128 ? CFG_KG2x2x4 : narrow;
+    if (a.M <= 128) return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : narrow;
+    if (a.M <= 256) return tiles(32, 128) >= 400 ? (FMT == 0 ? CFG_KG2x2x2 : CFG_KG2x1x2) : CFG_KG2x2x4;
+    if (a.M % 96 == 0 && tiles(96, 192) >= 128) return CFG_KPAIR;
+    return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : CFG_KG2x2x4;
+  }
+  // Otherwise prefer the largest tile that still gives a few waves of
+  // workgroups over the 256 compute units.
 #ifndef Q2_NO_KPAIR
   // Eight-wave 96 x 192 tiles when they fill the chip and M is a whole number
   // of tiles (the low-rank branch only in its LDS-staged form).
-  if (a.M % 96 == 0 && tiles(96, 192) >= 256 && (a.r == 0 || lr_lds)) return run_gemm_kpair<FMT>(a, stream);
+  if (a.M % 96 == 0 && tiles(96, 192) >= 256 && (a.r == 0 || lr_lds)) return CFG_KPAIR;
 #endif
-  if (!lr_lds && a.M >= 48 && tiles(48, 192) >= 512) return run_gemm<FMT, 48, 192>(a, stream);
-  if (a.M >= 96 && tiles(96, 192) >= 256) return run_gemm<FMT, 96, 192>(a, stream);
-  if (a.M >= 64 && tiles(64, 128) >= 256) return run_gemm<FMT, 64, 128>(a, stream);
-  if (tiles(32, 128) >= 256) return run_gemm<FMT, 32, 128>(a, stream);
-  return run_gemm<FMT, 32, 64>(a, stream);
+  // 48 x 192 tiles run two workgroups (eight waves) per CU; with the low-rank
+  // operands staged in LDS the tile no longer fits twice, so that case keeps 96 x 192.
+  if (!lr_lds && a.M >= 48 && tiles(48, 192) >= 512) return CFG_W48x192;
+  if (a.M >= 96 && tiles(96, 192) >= 256) return CFG_W96x192;
+  if (a.M >= 64 && tiles(64, 128) >= 256) return CFG_W64x128;
+  if (tiles(32, 128) >= 256) return CFG_W32x128;
+  return CFG_W32x64;
 }
 
-hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, hipStream_t stream) {
+hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, int force_cfg, hipStream_t stream) {
   const bool gemv = force_path == 1 || (force_path == 0 && a.M <= 16);
   if (gemv && a.M > 16) return hipErrorInvalidValue;
-  if (fmt == 0) return gemv ? run_gemv<0>(a, stream) : run_gemm_auto<0>(a, stream);
-  return gemv ? run_gemv<1>(a, stream) : run_gemm_auto<1>(a, stream);
+  if (fmt == 0) {
+    if (gemv) return run_gemv<0>(a, stream);
+    return run_gemm_cfg<0>(a, force_cfg > 0 ? force_cfg : gemm_auto_cfg<0>(a), stream);
+  }
+  if (gemv) return run_gemv<1>(a, stream);
+  return run_gemm_cfg<1>(a, force_cfg > 0 ? force_cfg : gemm_auto_cfg<1>(a), stream);
 }
 
 hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* tl, int64_t M, int64_t K, int r,

@@ -181,6 +181,54 @@ def test_linear_tile_configs(m, n, k):
     assert_close(y4, O.q4_linear(xb4, p4, s4, z4), f"q4 M={m} N={n} K={k}")
 
 
+# Every GEMM kernel configuration, forced through the test-only Q2_GEMM_TILE
+# override, on shapes with ragged M and N, block counts that leave the last
+# K set partial or shorter than one set, a single block and K = 0.
+GEMM_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
+             "kg2x1x4", "kg4x2x2", "kg2x1x2", "kg2x2x4", "kg2x2x2", "kg2x1x4r3"]
+CFG_SHAPES = [(75, 200, 1408), (128, 2560, 384), (33, 1000, 128), (40, 100, 0), (256, 700, 2560)]
+_cfg_ref = {}
+
+
+def _cfg_case(m, n, k):
+    key = (m, n, k)
+    if key not in _cfg_ref:
+        p_dev, s_dev, p_ref, s_ref = q2_weights(21, n, k)
+        xb, x = acts(21, m, k)
+        p4, s4, z4, xb4, x4, P, S, Z = q4_case(22, m, k, n)
+        _cfg_ref[key] = ((x, p_dev, s_dev, O.q2_linear(xb, p_ref, s_ref)),
+                         (x4, P, S, Z, O.q4_linear(xb4, p4, s4, z4)))
+    return _cfg_ref[key]
+
+
+@pytest.mark.parametrize("cfg", GEMM_CFGS)
+@pytest.mark.parametrize("m,n,k", CFG_SHAPES)
+def test_forced_gemm_configs(cfg, m, n, k, monkeypatch):
+    if cfg == "kpair":
+        m = 96 * ((m + 95) // 96)          # this configuration takes whole 96-row tiles only
+    (x, p, s, ref), (x4, P, S, Z, ref4) = _cfg_case(m, n, k)
+    monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+    y = torch.full((m, n), float("nan"), device=DEV)
+    q2.q2_linear(x, p, s, y)
+    y4 = torch.full((m, n), float("nan"), device=DEV)
+    q2.q4_linear(x4, P, S, Z, y4)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), ref, f"{cfg} M={m} N={n} K={k}")
+    assert_close(y4.cpu().numpy(), ref4, f"q4 {cfg} M={m} N={n} K={k}")
+
+
+def test_forced_gemm_config_errors(monkeypatch):
+    (x, p, s, _), _ = _cfg_case(75, 200, 1408)
+    monkeypatch.setenv("Q2_GEMM_TILE", "no-such-tile")
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_linear(x, p, s)
+    assert e.value.status == q2.Q2_ERR_ARG
+    monkeypatch.setenv("Q2_GEMM_TILE", "kpair")          # 75 rows are not whole 96-row tiles
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_linear(x, p, s)
+    assert e.value.status == q2.Q2_ERR_HIP
+
+
 def _offset_f16(t):
     """The same values in a buffer whose first element sits 2 bytes past a 4-byte boundary."""
     flat = torch.empty(t.numel() + 1, dtype=torch.float16, device=t.device)
