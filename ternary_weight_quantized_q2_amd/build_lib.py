@@ -48,7 +48,9 @@ def build(verbose=True, out=LIB, srcs=None):
         if log.strip() and verbose:
             print(log, file=sys.stderr)
     tmp = out + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
+    # -z defs: a symbol left undefined (such as a kernel launch stub that the
+    # host compilation pass failed to emit) fails the build instead of the load.
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *[o for o, _ in results]]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -172,6 +172,14 @@ constexpr int LR_RMAX = 64;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Buffer resource over `bytes` bytes from `base` for untyped 32-bit loads
+// (stride 0; the third word selects the 32-bit data format).  A copy through
+// it takes a 32-bit per-lane offset and a wave-uniform scalar offset, so the
+// address arithmetic of the global-to-LDS copies stays in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // and all its LDS operations are done, then meet the other waves.  Unlike
 // __syncthreads this does not drain every outstanding load, so the
@@ -658,10 +666,31 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
     woff[v] = (uint32_t)(gc * row_bytes + unit);
   }
   // Scale / zero word: wave wv covers block (wv >> 2) of the pair, columns (wv & 3) * 64 + lane.
+  // Each is copied as the aligned word that holds it, through a resource
+  // based 4 bytes below the tile's first scale (zero point): with h the
+  // half-word position of the column's block-0 value, the word of block blk
+  // sits at so_e (blk even) or so_o (blk odd) plus 2 blk.
   int64_t sgc = (wv & 3) * 64 + lane;
   sgc = sgc < BN ? sgc : BN - 1;
-  sgc = (n0 + sgc < N) ? n0 + sgc : N - 1;
-  const int64_t s_idx = sgc * KB;
+  sgc = (n0 + sgc < N) ? sgc : N - 1 - n0;                    // column from n0
+  const int64_t ncols = (N - n0) < BN ? (N - n0) : BN;
+  const uint32_t svl = (uint32_t)(2 * sgc * KB);
+  const uint32_t sbytes = (uint32_t)(2 * ncols * KB + 8);
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(reinterpret_cast<const uint8_t*>(a.s + n0 * KB) - 4, sbytes);
+  const uint32_t sh = (uint32_t)(((uintptr_t)(a.s + n0 * KB) + svl) >> 1) & 1u;
+  const uint32_t so_e = svl + 4 - 2 * sh, so_o = svl + 2 + 2 * sh;
+  __amdgpu_buffer_rsrc_t rz = rs;
+  uint32_t zo_e = 0, zo_o = 0;
+  if constexpr (FMT == 1) {
+    rz = buf_rsrc(reinterpret_cast<const uint8_t*>(a.z + n0 * KB) - 4, sbytes);
+    const uint32_t zh = (uint32_t)(((uintptr_t)(a.z + n0 * KB) + svl) >> 1) & 1u;
+    zo_e = svl + 4 - 2 * zh;
+    zo_o = svl + 2 + 2 * zh;
+  }
+  // Activation and code resources over the tile's rows (whole 96-row tiles
+  // here) and the tile's weight rows.
+  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x + m0 * K, (uint32_t)(BM * K * 2));
+  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.w + n0 * row_bytes, (uint32_t)(ncols * row_bytes));
 
   // ---- read side
   int aoff[4];
@@ -698,9 +727,9 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
         int64_t blk = b2 + q;
         blk = blk < KB ? blk : KB - 1;
         const int r0 = 16 * it + 4 * kk;                         // first tile row of this copy
-        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x + (m0 + r0) * K + blk * BLOCK_K);
-        __builtin_amdgcn_global_load_lds(base + (uint64_t)(xsrc ^ (uint32_t)(kk << 4)),
-                                         (lds_void*)(smem + (2 * slot + q) * XSTAGE + r0 * 256), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(smem + (2 * slot + q) * XSTAGE + r0 * 256), 16,
+                                                 xsrc ^ (uint32_t)(kk << 4),
+                                                 (uint32_t)(blk * 256 + (int64_t)r0 * K * 2), 0, 0);
       }
     } else if (unit < XUM + CU) {
       const int v = unit - XUM;
@@ -708,45 +737,45 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       const int q = ci0 / CPB;
       int64_t blk = b2 + q;
       blk = blk < KB ? blk : KB - 1;
-      const uint8_t* base = a.w + n0 * row_bytes + blk * BBYTES;
-      __builtin_amdgcn_global_load_lds(base + (uint64_t)woff[v],
-                                       (lds_void*)(smem + OFF_W + (2 * slot + q) * WSTAGE + (ci0 - q * CPB) * 16),
-                                       16, 0, 0);
+      // The offset goes through a local: with the array element itself as
+      // the operand, the host compilation pass drops this kernel's launch stub.
+      const uint32_t wo = woff[v];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (lds_void*)(smem + OFF_W + (2 * slot + q) * WSTAGE + (ci0 - q * CPB) * 16), 16, wo,
+          (uint32_t)(blk * BBYTES), 0, 0);
     } else {
       int64_t blk = b2 + (wv >> 2);
       blk = blk < KB ? blk : KB - 1;
-      const int64_t si = 2 * (s_idx + blk);
       const int dst = OFF_W + (2 * slot + (wv >> 2)) * WSTAGE + CODE_SLOT + (wv & 3) * 256;
+      const bool odd = (blk & 1) != 0;
       if (unit == XUM + CU) {
-        const uint8_t* sp = reinterpret_cast<const uint8_t*>(a.s);
-        __builtin_amdgcn_global_load_lds(sp + (si - (int64_t)(((uintptr_t)sp + si) & 3)), (lds_void*)(smem + dst), 4,
-                                         0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(smem + dst), 4, odd ? so_o : so_e,
+                                                 (uint32_t)(2 * blk), 0, 0);
       } else if constexpr (FMT == 1) {
-        const uint8_t* zp = reinterpret_cast<const uint8_t*>(a.z);
-        __builtin_amdgcn_global_load_lds(zp + (si - (int64_t)(((uintptr_t)zp + si) & 3)),
-                                         (lds_void*)(smem + dst + 1024), 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(smem + dst + 1024), 4, odd ? zo_o : zo_e,
+                                                 (uint32_t)(2 * blk), 0, 0);
       }
     }
   };
   // Low-rank operands into the two activation stages starting at stage st0.
+  // The tile's rows of T (whole 96-row tiles here) and its columns of B are
+  // each one contiguous byte range in global memory, copied as such in 16-byte
+  // units (both ranges are multiples of 1024 bytes since r % 8 == 0); the
+  // source of B's columns past N is clamped to its last 16 bytes.
   auto issue_lr = [&](int st0) {
     const int r = a.r;
-    const int tch = 2 * r / 8, bch = r / 8;
-    for (int base = wv * 64; base < BM * tch; base += 512) {
-      const int idx = base + lane;
-      const int row = idx / tch, ch = idx - row * tch;
-      int64_t gr = m0 + row;
-      gr = gr < M ? gr : M - 1;
-      __builtin_amdgcn_global_load_lds(a.lr_t + gr * 2 * r + ch * 8, (lds_void*)(smem + st0 * XSTAGE + base * 16), 16,
-                                       0, 0);
-    }
-    for (int base = wv * 64; base < BN * bch; base += 512) {
-      const int idx = base + lane;
-      const int col = idx / bch, ch = idx - col * bch;
-      int64_t gn = n0 + col;
-      gn = gn < N ? gn : N - 1;
-      __builtin_amdgcn_global_load_lds(a.lr_b + gn * r + ch * 8, (lds_void*)(smem + (st0 + 1) * XSTAGE + base * 16),
-                                       16, 0, 0);
+    const uint8_t* tsrc = reinterpret_cast<const uint8_t*>(a.lr_t + m0 * 2 * r);
+    const int tbytes = BM * 4 * r;
+    for (int base = wv * 1024; base < tbytes; base += 8 * 1024)
+      __builtin_amdgcn_global_load_lds(tsrc + (uint64_t)(uint32_t)(base + lane * 16),
+                                       (lds_void*)(smem + st0 * XSTAGE + base), 16, 0, 0);
+    const uint8_t* bsrc = reinterpret_cast<const uint8_t*>(a.lr_b + n0 * r);
+    const int64_t bavail = (N - n0) * 2 * r;               // bytes of B from column n0 on
+    const int bbytes = BN * 2 * r;
+    for (int base = wv * 1024; base < bbytes; base += 8 * 1024) {
+      int64_t off = base + lane * 16;
+      off = off + 16 <= bavail ? off : bavail - 16;
+      __builtin_amdgcn_global_load_lds(bsrc + off, (lds_void*)(smem + (st0 + 1) * XSTAGE + base), 16, 0, 0);
     }
   };
   auto afrag = [&](const uint8_t* st, int i, int t) -> q2_u32x4 {
