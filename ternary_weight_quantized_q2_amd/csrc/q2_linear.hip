@@ -633,6 +633,9 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   const int64_t nw = n0 + wn * (BN / 4);
   const int64_t M = a.M, N = a.N, K = a.K, KB = K / BLOCK_K;
   const int64_t row_bytes = (FMT == 0) ? K / 4 : K / 2;
+  // Block indices in 32 bits (K <= 2^24): uniform 64-bit compares would run on the vector ALU.
+  const int kb = (int)KB;
+  const uint32_t k2b = (uint32_t)(K * 2);                  // activation row bytes
   const NatConsts kc = (FMT == 0) ? q2_nat_consts() : q4_nat_consts();
 
   // ---- copy sources.  Activations are copied in 16-row tasks: the pair has
@@ -718,42 +721,42 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
     q = task >= 6 ? 1 : 0;
     it = task - 6 * q;
   };
-  auto issue_unit = [&](int unit, int64_t b2, int slot) {
+  auto issue_unit = [&](int unit, int b2, int slot) {
     if (unit < XUM) {
       const int k2 = unit >> 2, kk = unit & 3;
       if (k2 < xtasks) {
         int q, it;
         task_of(k2, q, it);
-        int64_t blk = b2 + q;
-        blk = blk < KB ? blk : KB - 1;
+        int blk = b2 + q;
+        blk = blk < kb ? blk : kb - 1;
         const int r0 = 16 * it + 4 * kk;                         // first tile row of this copy
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(smem + (2 * slot + q) * XSTAGE + r0 * 256), 16,
                                                  xsrc ^ (uint32_t)(kk << 4),
-                                                 (uint32_t)(blk * 256 + (int64_t)r0 * K * 2), 0, 0);
+                                                 (uint32_t)blk * 256u + (uint32_t)r0 * k2b, 0, 0);
       }
     } else if (unit < XUM + CU) {
       const int v = unit - XUM;
       const int ci0 = (v * 8 + wv) * 64;                       // uniform
       const int q = ci0 / CPB;
-      int64_t blk = b2 + q;
-      blk = blk < KB ? blk : KB - 1;
+      int blk = b2 + q;
+      blk = blk < kb ? blk : kb - 1;
       // The offset goes through a local: with the array element itself as
       // the operand, the host compilation pass drops this kernel's launch stub.
       const uint32_t wo = woff[v];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rw, (lds_void*)(smem + OFF_W + (2 * slot + q) * WSTAGE + (ci0 - q * CPB) * 16), 16, wo,
-          (uint32_t)(blk * BBYTES), 0, 0);
+          (uint32_t)blk * (uint32_t)BBYTES, 0, 0);
     } else {
-      int64_t blk = b2 + (wv >> 2);
-      blk = blk < KB ? blk : KB - 1;
+      int blk = b2 + (wv >> 2);
+      blk = blk < kb ? blk : kb - 1;
       const int dst = OFF_W + (2 * slot + (wv >> 2)) * WSTAGE + CODE_SLOT + (wv & 3) * 256;
       const bool odd = (blk & 1) != 0;
       if (unit == XUM + CU) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(smem + dst), 4, odd ? so_o : so_e,
-                                                 (uint32_t)(2 * blk), 0, 0);
+                                                 2u * (uint32_t)blk, 0, 0);
       } else if constexpr (FMT == 1) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(smem + dst + 1024), 4, odd ? zo_o : zo_e,
-                                                 (uint32_t)(2 * blk), 0, 0);
+                                                 2u * (uint32_t)blk, 0, 0);
       }
     }
   };
@@ -785,13 +788,13 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   const uint32_t sone = (FMT == 0) ? 0xBFA0BFA0u : 0xBF80BF80u;   // bf16 -1.25 / -1 pairs
   const q2_u32x4 sones = q2_u32x4{sone, sone, sone, sone};
   // Row sums of this wave's tasks of the pair starting at block b2 (slot `slot`).
-  auto row_sums = [&](int64_t b2, int slot) {
+  auto row_sums = [&](int b2, int slot) {
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       if (k2 < xtasks) {
         int q, it;
         task_of(k2, q, it);
-        if (b2 + q < KB) {
+        if (b2 + q < kb) {
           const uint8_t* st = smem + (2 * slot + q) * XSTAGE;
           q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -809,7 +812,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
     for (int j = 0; j < NT; ++j) acc[i][j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Decode of one block's weights for this wave's columns (from its weight stage).
-  auto decode = [&](const uint8_t* wst, int64_t blk, q2_u32x4 (&bf)[NT][4], float (&dc)[NT], float (&zc)[NT]) {
+  auto decode = [&](const uint8_t* wst, int blk, q2_u32x4 (&bf)[NT][4], float (&dc)[NT], float (&zc)[NT]) {
     const uint32_t pmask = (uint32_t)(blk & 1) ? 0xFFu : 0u;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -839,7 +842,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   // The next pair's copies (nb2 >= 0) are issued two units per row tile, so the
   // vector-memory path works in the background of the MFMAs.
   auto mainblk = [&](const uint8_t* st, const float* sb, const q2_u32x4 (&bf)[NT][4], const float (&dc)[NT],
-                     const float (&zc)[NT], int64_t nb2, int nslot) {
+                     const float (&zc)[NT], int nb2, int nslot) {
     q2_u32x4 a0[4], a1[4];
     q2_f32x4 s0, s1;
     auto rd = [&](int i, q2_u32x4 (&av)[4], q2_f32x4& s4) {
@@ -882,7 +885,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   };
   // This wave's activation copies of the next pair have landed once only its
   // NWU weight copies (issued after them) may still be in flight.
-  auto next_row_sums = [&](int64_t nb2, int nslot) {
+  auto next_row_sums = [&](int nb2, int nslot) {
     if (nb2 >= 0) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt((NWU & 15) | (7 << 4) | (15 << 8) | ((NWU >> 4) << 14));   // vmcnt(NWU)
@@ -902,21 +905,21 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
   if (KB > 0) {
     for (int un = 0; un < NU; ++un) issue_unit(un, 0, 0);
     next_row_sums(0, 0);
-    for (int64_t ip = 0; 2 * ip < KB; ++ip) {
+    for (int ip = 0; 2 * ip < kb; ++ip) {
       const int slot = (int)(ip & 1);
       stage_barrier<0>();                 // the pair's copies and row sums are complete; the previous pair is done
-      const int64_t nb2 = (2 * ip + 2 < KB) ? 2 * ip + 2 : -1;   // next pair, copied during the MFMAs
+      const int nb2 = (2 * ip + 2 < kb) ? 2 * ip + 2 : -1;       // next pair, copied during the MFMAs
       if constexpr (LR) {
         if (nb2 < 0) {
           lr_st0 = 2 * (slot ^ 1);
           issue_lr(lr_st0);
         }
       }
-      const int64_t bp = 2 * ip + par;
+      const int bp = 2 * ip + par;
       q2_u32x4 bf[NT][4];
       float dc[NT], zc[NT];
       decode(smem + OFF_W + (2 * slot + par) * WSTAGE, bp, bf, dc, zc);
-      if (bp < KB) {
+      if (bp < kb) {
         mainblk(smem + (2 * slot + par) * XSTAGE, ss[slot][par], bf, dc, zc, nb2, slot ^ 1);
       } else if (nb2 >= 0) {
         for (int un = 0; un < NU; ++un) issue_unit(un, nb2, slot ^ 1);
@@ -1075,7 +1078,9 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t nw = n0 + wn * (BN / 4);
   const int64_t M = a.M, N = a.N, K = a.K, KB = K / BLOCK_K;
-  const int64_t NS = (KB + KG - 1) / KG;                      // sets
+  // Block and set indices in 32 bits (K <= 2^24): uniform 64-bit compares would run on the vector ALU.
+  const int kb = (int)KB;
+  const int NS = (kb + KG - 1) / KG;                          // sets
   const int64_t row_bytes = (FMT == 0) ? K / 4 : K / 2;
   const NatConsts kc = (FMT == 0) ? q2_nat_consts() : q4_nat_consts();
 
@@ -1168,48 +1173,48 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   // Copies of set `set` into ring slot `slot`, one unit at a time: units
   // 0 .. XUM-1 the activation copies of this wave's tasks, then the codes, the
   // scale words [and zero words].  Blocks past the end re-copy the last one.
-  auto issue_unit = [&](int unit, int64_t set, int slot) {
-    const int64_t b0 = KG * set;
+  auto issue_unit = [&](int unit, int set, int slot) {
+    const int b0 = KG * set;
     if (unit < XUM) {
       const int k2 = unit >> 2, kk = unit & 3;
       if (k2 < xtasks) {
         const int task = wv + W * k2;
         const int q = task / MT, it = task - q * MT;
-        int64_t blk = b0 + q;
-        blk = blk < KB ? blk : KB - 1;
+        int blk = b0 + q;
+        blk = blk < kb ? blk : kb - 1;
         // Offsets go through locals: with an array element as the operand the
         // host compilation pass drops the kernel's launch stub.
         const uint32_t xo = xoff[k2][kk];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rx, (lds_void*)(smem + (slot * KG + q) * XSTAGE + (16 * it + 4 * kk) * 256), 16, xo,
-            (uint32_t)(blk * 256), 0, 0);
+            (uint32_t)blk * 256u, 0, 0);
       }
     } else if (unit < XUM + CU) {
       const int v = unit - XUM;
       int ci = v * W + wv;                                     // uniform
       ci = ci < CINS ? ci : CINS - 1;
       const int q = ci * 64 / CPB;
-      int64_t blk = b0 + q;
-      blk = blk < KB ? blk : KB - 1;
+      int blk = b0 + q;
+      blk = blk < kb ? blk : kb - 1;
       const uint32_t wo = woff[v];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rw, (lds_void*)(smem + OFF_W + (slot * KG + q) * WSTAGE + ((ci * 64) % CPB) * 16), 16, wo,
-          (uint32_t)(blk * BBYTES), 0, 0);
+          (uint32_t)blk * (uint32_t)BBYTES, 0, 0);
     } else {
-      int64_t blk = b0 + kg;
-      blk = blk < KB ? blk : KB - 1;
+      int blk = b0 + kg;
+      blk = blk < kb ? blk : kb - 1;
       const int dst = OFF_W + (slot * KG + kg) * WSTAGE + CODE_SLOT + sq * 256;
       const bool odd = (blk & 1) != 0;
       if (unit == XUM + CU) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(smem + dst), 4, odd ? so_o : so_e,
-                                                 (uint32_t)(2 * blk), 0, 0);
+                                                 2u * (uint32_t)blk, 0, 0);
       } else if constexpr (FMT == 1) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(smem + dst + SWORDS), 4, odd ? zo_o : zo_e,
-                                                 (uint32_t)(2 * blk), 0, 0);
+                                                 2u * (uint32_t)blk, 0, 0);
       }
     }
   };
-  auto issue_set = [&](int64_t set, int slot) {
+  auto issue_set = [&](int set, int slot) {
     for (int un = 0; un < NU; ++un) issue_unit(un, set, slot);
   };
   auto afrag = [&](const uint8_t* st, int i, int t) -> q2_u32x4 {
@@ -1219,13 +1224,13 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   const uint32_t sone = (FMT == 0) ? 0xBFA0BFA0u : 0xBF80BF80u;   // bf16 -1.25 / -1 pairs
   const q2_u32x4 sones = q2_u32x4{sone, sone, sone, sone};
   // Row sums of this wave's tasks of set `set` (slot `slot`).
-  auto row_sums = [&](int64_t set, int slot) {
+  auto row_sums = [&](int set, int slot) {
 #pragma unroll
     for (int k2 = 0; k2 < XT; ++k2) {
       if (k2 < xtasks) {
         const int task = wv + W * k2;
         const int q = task / MT, it = task - q * MT;
-        if (KG * set + q < KB) {
+        if (KG * set + q < kb) {
           const uint8_t* st = smem + (slot * KG + q) * XSTAGE;
           q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1258,7 +1263,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
     for (int j = 0; j < NT; ++j) acc[i][j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Decode of one block's weights for this wave's columns (from its weight stage).
-  auto decode = [&](const uint8_t* wst, int64_t blk, q2_u32x4 (&bf)[NT][4], float (&dc)[NT], float (&zc)[NT]) {
+  auto decode = [&](const uint8_t* wst, int blk, q2_u32x4 (&bf)[NT][4], float (&dc)[NT], float (&zc)[NT]) {
     const uint32_t pmask = (uint32_t)(blk & 1) ? 0xFFu : 0u;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -1285,7 +1290,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   // MFMAs of one block over the staged activations `st`, row sums `sb`; the
   // copies of set `cset` (if >= 0) are issued UPT units per row tile.
   auto mainblk = [&](const uint8_t* st, const float* sb, const q2_u32x4 (&bf)[NT][4], const float (&dc)[NT],
-                     const float (&zc)[NT], int64_t cset, int cslot) {
+                     const float (&zc)[NT], int cset, int cslot) {
     q2_u32x4 a0[4], a1[4];
     q2_f32x4 s0, s1;
     auto rd = [&](int i, q2_u32x4 (&av)[4], q2_f32x4& s4) {
@@ -1340,13 +1345,13 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
     }
     row_sums(0, 0);
     int slot = 0;
-    for (int64_t s = 0; s < NS; ++s) {
+    for (int s = 0; s < NS; ++s) {
       if constexpr (NSET == 3) stage_barrier<63>();
       else stage_barrier<0>();
-      const int64_t cset = (s + NSET - 1 < NS) ? s + NSET - 1 : -1;   // the set copied during this one
+      const int cset = (s + NSET - 1 < NS) ? s + NSET - 1 : -1;       // the set copied during this one
       const int cslot = (slot + NSET - 1 >= NSET) ? slot - 1 : slot + NSET - 1;   // (s + NSET - 1) % NSET
-      const int64_t bp = KG * s + kg;
-      if (bp < KB) {
+      const int bp = KG * s + kg;
+      if (bp < kb) {
         q2_u32x4 bf[NT][4];
         float dc[NT], zc[NT];
         decode(smem + OFF_W + (slot * KG + kg) * WSTAGE, bp, bf, dc, zc);
