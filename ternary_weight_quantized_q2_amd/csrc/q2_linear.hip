@@ -1766,9 +1766,9 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, hipStream_t stream) {
 // whatever shapes the automatic choice gives it.
 static const char* const kGemmCfgNames[] = {"auto",    "kpair",   "w48x192", "w96x192", "w64x128",
                                             "w32x128", "w32x64",  "kg2x1x4", "kg4x2x2", "kg2x1x2",
-                                            "kg2x2x4", "kg2x2x2", "kg2x1x4r3"};
+                                            "kg2x2x4", "kg2x2x2", "kg2x1x4r3", "kg6x3x2"};
 enum GemmCfg { CFG_AUTO, CFG_KPAIR, CFG_W48x192, CFG_W96x192, CFG_W64x128, CFG_W32x128, CFG_W32x64, CFG_KG2x1x4,
-               CFG_KG4x2x2, CFG_KG2x1x2, CFG_KG2x2x4, CFG_KG2x2x2, CFG_KG2x1x4R3, CFG_COUNT };
+               CFG_KG4x2x2, CFG_KG2x1x2, CFG_KG2x2x4, CFG_KG2x2x2, CFG_KG2x1x4R3, CFG_KG6x3x2, CFG_COUNT };
 static_assert(sizeof kGemmCfgNames / sizeof kGemmCfgNames[0] == CFG_COUNT, "configuration names");
 
 int gemm_config_id(const char* name) {
@@ -1795,6 +1795,7 @@ static hipError_t run_gemm_cfg(const LinearArgs& a, int cfg, hipStream_t stream)
     case CFG_KG2x2x4: return run_gemm_kgroup<FMT, 2, 2, 4, 2>(a, stream);
     case CFG_KG2x2x2: return run_gemm_kgroup<FMT, 2, 2, 2, 2>(a, stream);
     case CFG_KG2x1x4R3: return run_gemm_kgroup<FMT, 2, 1, 4, 3>(a, stream);
+    case CFG_KG6x3x2: return run_gemm_kgroup<FMT, 6, 3, 2, 2>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1815,6 +1816,16 @@ static int gemm_auto_cfg(const LinearArgs& a) {
     if (a.M <= 256) return tiles(32, 128) >= 400 ? (FMT == 0 ? CFG_KG2x2x2 : CFG_KG2x1x2) : CFG_KG2x2x4;
     if (a.M % 96 == 0 && tiles(96, 192) >= 128) return CFG_KPAIR;
     return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : CFG_KG2x2x4;
+  }
+  if (a.r == 0) {
+#ifndef Q2_NO_KPAIR
+    if (a.M % 96 == 0 && tiles(96, 192) >= 256) return CFG_KPAIR;
+#endif
+    if (a.M <= 640) return tiles(32, 128) >= 400 ? CFG_KG2x2x2 : CFG_KG4x2x2;
+    // Any M: the 96 x 192 K-group tile (rows past M clamped) once it gives
+    // enough workgroups, else two 48 x 192 workgroups per CU.
+    if (tiles(96, 192) >= 160) return CFG_KG6x3x2;
+    if (a.M >= 48 && tiles(48, 192) >= 256) return CFG_W48x192;
   }
   // Otherwise prefer the largest tile that still gives a few waves of
   // workgroups over the 256 compute units.

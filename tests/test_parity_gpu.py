@@ -185,7 +185,7 @@ def test_linear_tile_configs(m, n, k):
 # override, on shapes with ragged M and N, block counts that leave the last
 # K set partial or shorter than one set, a single block and K = 0.
 GEMM_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
-             "kg2x1x4", "kg4x2x2", "kg2x1x2", "kg2x2x4", "kg2x2x2", "kg2x1x4r3"]
+             "kg2x1x4", "kg4x2x2", "kg2x1x2", "kg2x2x4", "kg2x2x2", "kg2x1x4r3", "kg6x3x2"]
 CFG_SHAPES = [(75, 200, 1408), (128, 2560, 384), (33, 1000, 128), (40, 100, 0), (256, 700, 2560)]
 _cfg_ref = {}
 
@@ -210,10 +210,11 @@ def test_forced_gemm_configs(cfg, m, n, k, monkeypatch):
     monkeypatch.setenv("Q2_GEMM_TILE", cfg)
     y = torch.full((m, n), float("nan"), device=DEV)
     q2.q2_linear(x, p, s, y)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), ref, f"{cfg} M={m} N={n} K={k}")
     y4 = torch.full((m, n), float("nan"), device=DEV)
     q2.q4_linear(x4, P, S, Z, y4)
     torch.cuda.synchronize()
-    assert_close(y.cpu().numpy(), ref, f"{cfg} M={m} N={n} K={k}")
     assert_close(y4.cpu().numpy(), ref4, f"q4 {cfg} M={m} N={n} K={k}")
 
 
