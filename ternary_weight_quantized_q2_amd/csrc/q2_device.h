@@ -211,6 +211,21 @@ __device__ __forceinline__ void f16_split_bf16(uint16_t h, uint16_t& hi, uint16_
   lo = (uint16_t)(__builtin_bit_cast(uint32_t, f - fh) >> 16);
 }
 
+// Exact bf16 limbs of two f16 values packed in a dword: the high limb is the
+// upper half of each value's fp32 bits, the low limb the rest (at most three
+// significant bits, exact in bf16).  Returned as packed bf16 pairs.
+__device__ __forceinline__ uint32_t f16x2_bf16_hi(uint32_t h2) {
+  const uint32_t f0 = __builtin_bit_cast(uint32_t, f16_to_f32((uint16_t)(h2 & 0xFFFFu)));
+  const uint32_t f1 = __builtin_bit_cast(uint32_t, f16_to_f32((uint16_t)(h2 >> 16)));
+  return __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+}
+__device__ __forceinline__ uint32_t f16x2_bf16_lo(uint32_t h2) {
+  const float f0 = f16_to_f32((uint16_t)(h2 & 0xFFFFu)), f1 = f16_to_f32((uint16_t)(h2 >> 16));
+  const float l0 = f0 - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f0) & 0xFFFF0000u);
+  const float l1 = f1 - __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f1) & 0xFFFF0000u);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, l1), __builtin_bit_cast(uint32_t, l0), 0x07060302u);
+}
+
 // Round fp32 to bf16 (nearest even; finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rn(float f) {
   const uint32_t b = __builtin_bit_cast(uint32_t, f);

@@ -941,13 +941,14 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       for (int e = 0; e < 4; ++e) acc[i][j][e] *= fin;
 
   if constexpr (LR) {
-    // Parity-1 waves add the branch to their partial sums.
-    if (par == 1) {
+    // Both waves of a column group add the branch to their partial sums, the
+    // branch's K steps alternating between them.
+    {
       const uint16_t* lt = reinterpret_cast<const uint16_t*>(smem + lr_st0 * XSTAGE);
       const uint16_t* lb = reinterpret_cast<const uint16_t*>(smem + (lr_st0 + 1) * XSTAGE);
       const int r = a.r;
       const int ks = (3 * r + 31) / 32;
-      for (int t = 0; t < ks; ++t) {
+      for (int t = par; t < ks; t += 2) {
         const int q0 = 32 * t + 8 * g;
         const bool lv = q0 < 3 * r;
         const int part = q0 / r, jj = q0 - part * r;
@@ -959,12 +960,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
           if (lv) {
             const q2_u32x4 raw = *reinterpret_cast<const q2_u32x4*>(&lb[col * r + jj]);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              uint16_t h0, l0, h1, l1;
-              f16_split_bf16((uint16_t)(raw[d] & 0xFFFFu), h0, l0);
-              f16_split_bf16((uint16_t)(raw[d] >> 16), h1, l1);
-              v[d] = (part == 1) ? ((uint32_t)l0 | ((uint32_t)l1 << 16)) : ((uint32_t)h0 | ((uint32_t)h1 << 16));
-            }
+            for (int d = 0; d < 4; ++d) v[d] = (part == 1) ? f16x2_bf16_lo(raw[d]) : f16x2_bf16_hi(raw[d]);
           }
           bq[j] = v;
         }
@@ -1597,8 +1593,8 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
 // ============================================================================
 // x A^T for the low-rank branch: bf16 limbs [M, 2r] = (hi | lo)
 // ============================================================================
-constexpr int LR_WAVES = 8;
-constexpr int LR_UNROLL = 12;    // k-steps per wave whose loads are issued together
+constexpr int LR_WAVES = 16;
+constexpr int LR_UNROLL = 6;     // k-steps per wave whose loads are issued together
 
 // A workgroup owns 16 rows of x and 16 columns of A (one MFMA tile); its waves
 // split K in 32-wide steps, issue all their loads first, and are reduced in a
@@ -1630,11 +1626,8 @@ __global__ __launch_bounds__(LR_WAVES * 64) void lowrank_t_kernel(const uint16_t
         q2_u32x4 bh, bl;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          uint16_t h0, l0, h1, l1;
-          f16_split_bf16((uint16_t)(bv[u][d] & 0xFFFFu), h0, l0);
-          f16_split_bf16((uint16_t)(bv[u][d] >> 16), h1, l1);
-          bh[d] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          bl[d] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          bh[d] = f16x2_bf16_hi(bv[u][d]);
+          bl[d] = f16x2_bf16_lo(bv[u][d]);
         }
         acc = mfma(av[u], bh, acc);
         acc = mfma(av[u], bl, acc);
