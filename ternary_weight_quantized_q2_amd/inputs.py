@@ -52,6 +52,17 @@ def q2_codes(config_id: int, n: int, k: int, p=(0.3, 0.4, 0.3)) -> np.ndarray:
     return g.choice(3, size=(n, k), p=list(p)).astype(np.uint8)
 
 
+_DIGIT_TO_CODE = np.array([0, 0, 0, 1, 1, 1, 1, 2, 2, 2], dtype=np.uint8)
+
+
+def q2_codes_fast(config_id: int, n: int, k: int) -> np.ndarray:
+    """u8 [n, k] codes in {0, 1, 2} with p = (0.3, 0.4, 0.3), drawn as a uniform
+    decimal digit mapped 0-2 / 3-6 / 7-9 (an order of magnitude faster than
+    q2_codes, for the 100-linear layer lists)."""
+    g = stream(config_id, T_CODES)
+    return _DIGIT_TO_CODE[g.integers(0, 10, size=(n, k), dtype=np.uint8)]
+
+
 def q2_scales(config_id: int, n: int, k: int) -> np.ndarray:
     """float32 [n, k/128] block scales whose values are exactly representable in f16."""
     g = stream(config_id, T_SCALES)

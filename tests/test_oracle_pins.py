@@ -65,6 +65,17 @@ def test_bf16_decode_exhaustive():
     assert np.array_equal(ref[~nan], vec[~nan])
 
 
+def test_fast_code_generator_distribution():
+    """The digit-mapped generator of the layer lists draws codes in {0, 1, 2}
+    with p = (0.3, 0.4, 0.3), reproducibly from its seed."""
+    c = I.q2_codes_fast(97, 300, 1024)
+    assert c.dtype == np.uint8 and c.shape == (300, 1024) and c.max() <= 2
+    freq = np.bincount(c.ravel(), minlength=3) / c.size
+    assert np.allclose(freq, [0.3, 0.4, 0.3], atol=0.005)
+    assert np.array_equal(c, I.q2_codes_fast(97, 300, 1024))
+    assert not np.array_equal(c, I.q2_codes_fast(98, 300, 1024))
+
+
 def test_bf16_rounding_of_inputs_is_nearest_even():
     x = np.random.default_rng(5).standard_normal(100000).astype(np.float32)
     ours = I.f32_to_bf16_bits(x)
