@@ -106,6 +106,43 @@ def cpu_baseline():
             "sample": f"{reps} x Q2_0 linear M={m} K={k} N={n} (unpack + float64 dgemm), {dt:.1f} s"}
 
 
+def measure_layer_list(torch, q2, I, dev):
+    """The low-rank layer list: LOWRANK["linears"] distinct rank-32 linears
+    (own W, A, B) on one shared x, LOWRANK["steps"] passes in one graph.  The
+    weights (about 0.9 GB) exceed the 256 MB Infinity Cache, so every call
+    reads its weights from HBM.  Reported beside the step, not part of it."""
+    c = I.LOWRANK
+    m, k, n, r, layers, steps = c["M"], c["K"], c["N"], 32, c["linears"], c["steps"]
+    x = torch.from_numpy(I.activations_bf16(900, m, k).view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = torch.empty(q2.lowrank_workspace_bytes(m, r), dtype=torch.uint8, device=dev)
+    y = torch.empty((m, n), device=dev)
+    weights = []
+    for i in range(layers):
+        p, s = q2.q2_pack(torch.from_numpy(I.q2_codes_fast(1000 * r + i, n, k)).to(dev),
+                          torch.from_numpy(I.q2_scales(1000 * r + i, n, k)).to(dev))
+        a, b = I.lowrank_factors(1000 * r + i, r, k, n)
+        weights.append((p, s, torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16),
+                        torch.from_numpy(b.view(np.int16)).to(dev).view(torch.float16)))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            for p, s, A, B in weights:
+                q2.q2_linear_lowrank(x, p, s, A, B, y=y, workspace=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / (steps * layers)
+    flops = 2.0 * m * n * k + 2.0 * m * r * (k + n)
+    return {"linears": layers, "steps": steps, "r": r, "shape": f"M={m} K={k} N={n}",
+            "us_per_call": round(t * 1e6, 3), "tflops": round(flops / t / 1e12, 3),
+            "frac": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "weight_bytes": int(layers * (Q2_BYTES_PER_WEIGHT * n * k + 2 * r * (k + n) * 2))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +153,8 @@ def main():
                     "print only the wall time (no graph, no per-call events)")
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
                     "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref")
+    ap.add_argument("--no-layer-list", action="store_true",
+                    help="skip the 100-linear rank-32 layer list report")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -257,6 +296,8 @@ def main():
         per.append(e0.elapsed_time(e1) * 1e-3 / reps)
         del g
 
+    layer_list = None if (args.no_layer_list or args.only) else measure_layer_list(torch, q2, I, dev)
+
     parts = {}
     fam_time, fam_flops, fam_bytes = {}, {}, {}
     for c, t in zip(calls, per):
@@ -304,6 +345,8 @@ def main():
         "m1_weight_gbs": round(gemv_ach, 2),
         "parts": parts,
     }
+    if layer_list is not None:
+        out["layer_list"] = layer_list
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
