@@ -150,7 +150,7 @@ def test_linear_identity_is_exact(path, m):
     assert np.array_equal(y.astype(np.float64), w[:, :m].T)
 
 
-SHAPES = [(1, 1, 128), (1, 17, 384), (3, 130, 1280), (7, 1000, 256), (16, 257, 512), (17, 65, 640),
+SHAPES = [(1, 1, 128), (1, 17, 384), (3, 130, 1280), (4, 64, 256), (7, 1000, 256), (16, 257, 512), (17, 65, 640),
           (33, 200, 128), (100, 333, 384), (257, 190, 1024), (96, 192, 3072), (300, 450, 2048)]
 
 
@@ -163,9 +163,9 @@ def test_linear_ragged(path, m, n, k):
     assert_close(y, O.q2_linear(xb, p_ref, s_ref), f"{path} M={m} N={n} K={k}")
 
 
-# One case per GEMM tile configuration (eight-wave 96x192 with an odd and a
-# single block, 48x192, 96x192, 64x128, 32x128, 32x64), ragged in N and,
-# where the configuration allows, in M.
+# Shapes across the automatic configuration choice (several workgroup waves,
+# an odd and a single block count, ragged N and, where allowed, ragged M);
+# every configuration is also forced in test_forced_gemm_configs.
 TILE_CASES = [(192, 24700, 384), (96, 49300, 128), (203, 24700, 384), (500, 8500, 256), (250, 8100, 256),
               (40, 16300, 256), (20, 300, 256)]
 
