@@ -1,21 +1,23 @@
 // q2_linear.hip - the Q2_0 ternary linear (and the 4-bit variant) on CDNA4.
 //
-// Two kernels compute y = x W^T for packed weights:
-//  * gemm_kernel (M > 16): a workgroup owns a BM x BN output tile; its four
-//    waves split the tile along N.  Per 128-wide K block the workgroup stages
-//    the activation rows into LDS (in the weight decoder's pair order, plus the
-//    per-row block sum), each wave loads its rows' packed codes straight from
-//    HBM into registers, decodes them into bf16 matrix-core operands and runs
-//    16x16x32 bf16 MFMAs into a per-block accumulator that is scaled by the
-//    block's f16 scale into the fp32 result.  Activations of block b+1 and
-//    weights of block b+1 are fetched while block b computes.
-//  * gemv_kernel (M <= 16): a workgroup owns 16 weight rows (one MFMA column
-//    tile); its waves split K block by block, stream the packed codes with
-//    coalesced loads and finish with a fixed-order cross-wave reduction, so
-//    there is one HBM pass over the weights and no atomics.
-// The rank-r side branch y += (x A^T) B^T is added in both epilogues with
-// extra MFMA steps over the bf16 limbs of x A^T (computed once per call by
-// lowrank_t_kernel) and the exact bf16 hi/lo split of B.
+// y = x W^T for packed weights; every operand of the GEMMs reaches LDS through
+// direct copies, the weights are decoded into bf16 matrix-core operands by a
+// magic-number OR, and 16x16x32 bf16 MFMAs accumulate each 128-wide block
+// from a start value of -1.25 (or -(1 + z/16)) times the block's row sums,
+// after which one FMA per output applies the block's f16 scale.
+//  * gemm_kpair_kernel (M a multiple of 96, enough 96 x 192 tiles): eight
+//    waves, the two on each SIMD taking alternate K blocks of the same output
+//    columns; partial sums added once at the end.  Also carries the rank-r
+//    branch in its epilogue.
+//  * gemm_kgroup_kernel (smaller and ragged M): the same idea for KG groups of
+//    four waves and 16 MT x 64 NT tiles.
+//  * gemm_kernel (the low-rank branch outside the K-pair kernel's reach, narrow
+//    mid-size outputs): four waves splitting N, one block per barrier.
+//  * gemv_kernel (M <= 16): a workgroup owns 16 weight rows; its waves split
+//    K, stream the codes with coalesced loads, transpose them through LDS into
+//    the matrix-core layout and finish with a fixed-order reduction.
+//  * lowrank_t_kernel: x A^T once per call, as bf16 hi/lo limbs, for the
+//    branch y += (x A^T) B^T that the GEMM and GEMV epilogues add.
 //
 // Every summation order is fixed, so results are bitwise reproducible.
 #include "q2_device.h"
@@ -33,27 +35,6 @@ template <> struct WFmt<1> {           // 4-bit: 64 bytes per row and group
   static constexpr int BLOCK_BYTES = 64;
   static constexpr int LANE_DW = 4;    // lane group g holds dwords 4g .. 4g+3
 };
-
-// Packed codes, scale and zero point of one block of one weight row.  The row
-// index must already be clamped to a valid row: rows past N load row N-1,
-// whose outputs are computed but never stored, so loads never branch.
-template <int FMT>
-__device__ __forceinline__ void load_wblock(const LinearArgs& a, int64_t row, int64_t blk, int g,
-                                            uint32_t (&out)[WFmt<FMT>::LANE_DW], float& sc, float& zp) {
-  constexpr int DW = WFmt<FMT>::LANE_DW;
-  const int64_t row_bytes = (FMT == 0) ? a.K / 4 : a.K / 2;
-  const uint8_t* p = a.w + row * row_bytes + blk * WFmt<FMT>::BLOCK_BYTES + g * DW * 4;
-  if constexpr (DW == 2) {
-    const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(p);
-    out[0] = v[0]; out[1] = v[1];
-  } else {
-    const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(p);
-    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
-  }
-  const int64_t si = row * (a.K / BLOCK_K) + blk;
-  sc = f16_to_f32(a.s[si]);
-  zp = (FMT == 1) ? f16_to_f32(a.z[si]) : 0.f;
-}
 
 template <int FMT>
 __device__ __forceinline__ void decode_block(const uint32_t (&w)[WFmt<FMT>::LANE_DW], q2_u32x4 (&bf)[4],
