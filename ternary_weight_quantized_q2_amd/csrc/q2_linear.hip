@@ -19,7 +19,10 @@
 //  * lowrank_t_kernel: x A^T once per call, as bf16 hi/lo limbs, for the
 //    branch y += (x A^T) B^T that the GEMM and GEMV epilogues add.
 //
-// Every summation order is fixed, so results are bitwise reproducible.
+// Every summation order is fixed, so results are bitwise reproducible.  The
+// GEMMs write y with non-temporal stores: the fp32 outputs (tens of MB) would
+// otherwise push the activations and weights that later tiles re-read out of
+// the caches.
 #include "q2_device.h"
 #include "q2_internal.h"
 #include <cstring>
@@ -567,7 +570,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (m < M) a.y[m * N + n] = acc[i][j][e];
+          if (m < M) __builtin_nontemporal_store(acc[i][j][e], &a.y[m * N + n]);
         }
       }
     }
@@ -981,7 +984,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
         for (int e = 0; e < 4; ++e) {
           const float v = acc[i][j][e] + red[((i * NT + j) * 4 + e) * 64 + lane];
           const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (m < M && n < N) a.y[m * N + n] = v;
+          if (m < M && n < N) __builtin_nontemporal_store(v, &a.y[m * N + n]);
         }
       }
     }
@@ -1377,7 +1380,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
 #pragma unroll
           for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
           const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (m < M && n < N) a.y[m * N + n] = v * fin;
+          if (m < M && n < N) __builtin_nontemporal_store(v * fin, &a.y[m * N + n]);
         }
       }
     }
