@@ -974,7 +974,41 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
         for (int e = 0; e < 4; ++e) red[((i * NT + j) * 4 + e) * 64 + lane] = acc[i][j][e];
   }
   __syncthreads();
-  if (par == 0) {
+  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0) {
+    // The finished tile goes through LDS once more (rows padded to OS floats,
+    // so the writes are conflict-free), and every lane then stores 16
+    // contiguous bytes of a row: whole lines reach memory instead of the
+    // 64-byte pieces of the matrix-core layout.
+    constexpr int OS = BN + 4;
+    static_assert(BM * OS * 4 <= SMEM, "output tile");
+    if (par == 0) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += red[((i * NT + j) * 4 + e) * 64 + lane];
+    }
+    __syncthreads();                      // the partial sums are read; their space takes the tile
+    float* const out = reinterpret_cast<float*>(smem);
+    if (par == 0) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * OS + wn * (BN / 4) + 16 * j + c] = acc[i][j][e];
+    }
+    __syncthreads();
+    const int64_t ncols = (N - n0) < BN ? (N - n0) : BN;
+    for (int idx = tid; idx < BM * (BN / 4); idx += 512) {
+      const int row = idx / (BN / 4), q = idx - row * (BN / 4);
+      const int64_t m = m0 + row;
+      if (m < M && 4 * q < ncols)
+        __builtin_nontemporal_store(*reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]),
+                                    reinterpret_cast<q2_f32x4*>(&a.y[m * N + n0 + 4 * q]));
+    }
+  } else if (par == 0) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll

@@ -186,7 +186,7 @@ def test_linear_tile_configs(m, n, k):
 # K set partial or shorter than one set, a single block and K = 0.
 GEMM_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
              "kg2x1x4", "kg4x2x2", "kg2x1x2", "kg2x2x4", "kg2x2x2", "kg2x1x4r3", "kg6x3x2"]
-CFG_SHAPES = [(75, 200, 1408), (128, 2560, 384), (33, 1000, 128), (40, 100, 0), (256, 700, 2560)]
+CFG_SHAPES = [(75, 200, 1408), (128, 2560, 384), (33, 1000, 128), (40, 100, 0), (256, 700, 2560), (96, 333, 640)]
 _cfg_ref = {}
 
 
@@ -216,6 +216,21 @@ def test_forced_gemm_configs(cfg, m, n, k, monkeypatch):
     q2.q4_linear(x4, P, S, Z, y4)
     torch.cuda.synchronize()
     assert_close(y4.cpu().numpy(), ref4, f"q4 {cfg} M={m} N={n} K={k}")
+
+
+@pytest.mark.parametrize("cfg", ["kpair", "kg6x3x2", "w48x192"])
+def test_output_not_16_byte_aligned(cfg, monkeypatch):
+    """y 4 bytes past a 16-byte boundary takes the per-element store path."""
+    m, n, k = 192, 400, 640
+    (x, p, s, ref), _ = _cfg_case(m, n, k)
+    monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+    flat = torch.full((m * n + 4,), float("nan"), device=DEV)
+    y = flat[1:1 + m * n].view(m, n)
+    assert y.data_ptr() % 16 == 4
+    q2.q2_linear(x, p, s, y)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), ref, f"{cfg} unaligned y")
+    assert torch.isnan(flat[0]) and torch.isnan(flat[1 + m * n:]).all()
 
 
 def test_forced_gemm_config_errors(monkeypatch):
