@@ -1401,8 +1401,45 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
         for (int e = 0; e < 4; ++e) mine[((i * NT + j) * 4 + e) * 64 + lane] = acc[i][j][e];
   }
   __syncthreads();
-  if (kg == 0) {
-    const float fin = (FMT == 0) ? 4.f : 16.f;
+  const float fin = (FMT == 0) ? 4.f : 16.f;
+  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0) {
+    // As in the K-pair kernel: the finished tile goes through LDS (rows padded
+    // to OS floats) and is stored as 16-byte pieces of contiguous rows.
+    constexpr int OS = BN + 4;
+    static_assert(BM * OS * 4 <= SMEM, "output tile");
+    if (kg == 0) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = acc[i][j][e];
+#pragma unroll
+            for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
+            acc[i][j][e] = v * fin;
+          }
+    }
+    __syncthreads();                      // the partial sums are read; their space takes the tile
+    float* const out = reinterpret_cast<float*>(smem);
+    if (kg == 0) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * OS + wn * (BN / 4) + 16 * j + c] = acc[i][j][e];
+    }
+    __syncthreads();
+    const int64_t ncols = (N - n0) < BN ? (N - n0) : BN;
+    for (int idx = tid; idx < BM * (BN / 4); idx += 64 * W) {
+      const int row = idx / (BN / 4), q = idx - row * (BN / 4);
+      const int64_t m = m0 + row;
+      if (m < M && 4 * q < ncols)
+        __builtin_nontemporal_store(*reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]),
+                                    reinterpret_cast<q2_f32x4*>(&a.y[m * N + n0 + 4 * q]));
+    }
+  } else if (kg == 0) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
