@@ -336,7 +336,7 @@ def main():
             "activations": "bf16 N(0,1)",
             "parallelism": "single GPU",
         },
-        "roofline": {"bound": "mfma", "kernel": "gemm_kpair_kernel (Q2_0, M=1536)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_kgroup_kernel<0, 6, 3, 2, 2> (Q2_0, M=1536)",
                      "achieved": round(gemm_ach, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "roofline_gemv": {"bound": "hbm", "kernel": "gemv_kernel (Q2_0, M=1)", "achieved": round(gemv_ach, 2),
