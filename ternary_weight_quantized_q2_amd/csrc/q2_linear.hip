@@ -1029,9 +1029,11 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
 // GEMM for few rows: KG groups of four waves split the K blocks
 // ============================================================================
 // Consecutive workgroup ids are dispatched to the eight XCDs in turn.  This
-// hands each XCD a contiguous range of tiles instead; tiles are numbered
-// row-fastest, so the row tiles that read the same weight columns meet in one
-// L2 and the weights come from HBM about once.
+// hands each XCD a contiguous range of tile numbers instead, and the numbers
+// run over groups of group_m row tiles, row-fastest inside a group: with
+// group_m = all row tiles each XCD reads 1/8 of the weights and all of x (few
+// rows), with group_m = 1/8 of them each XCD reads 1/8 of x and all of the
+// weights (many rows), and in between the tile grid is cut into 8 blocks.
 __device__ __forceinline__ int xcd_tile(int b, int tiles) {
   const int per = tiles >> 3, rem = tiles & 7;
   const int xcd = b & 7, local = b >> 3;
@@ -1052,7 +1054,7 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles) {
 // sums once its own copies have landed; one barrier per set publishes them.
 // Rows past M are clamped on the copy side and dropped at the store.
 template <int FMT, int MT, int NT, int KG, int NSET>
-__global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int tiles_m) {
+__global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int tiles_m, int group_m) {
   constexpr int W = 4 * KG;                                   // waves
   constexpr int BM = 16 * MT, BN = 64 * NT;
   constexpr int DW = WFmt<FMT>::LANE_DW;
@@ -1088,7 +1090,9 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   const int c = lane & 15, g = lane >> 4;
   const int tiles_n = (int)((a.N + BN - 1) / BN);
   const int tile = xcd_tile((int)blockIdx.x, tiles_m * tiles_n);
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int grp = tile / (group_m * tiles_n), gi = tile - grp * group_m * tiles_n;
+  const int gm = min(group_m, tiles_m - grp * group_m);          // row tiles in this group
+  const int tm = grp * group_m + gi % gm, tn = gi / gm;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t nw = n0 + wn * (BN / 4);
   const int64_t M = a.M, N = a.N, K = a.K, KB = K / BLOCK_K;
@@ -1798,6 +1802,20 @@ static hipError_t run_gemm_kpair(const LinearArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Row tiles per group of the K-group tile order.  Cutting the tile grid into
+// p row parts times 8 / p column parts, one block per XCD, makes the XCDs
+// together read x (8 / p) times and the weights p times; p is the power of two
+// (at most the row-tile count) that minimises that sum.
+template <int FMT>
+static int kgroup_group_rows(const LinearArgs& a, int tiles_m) {
+  const double xb = 2.0 * (double)a.M * (double)a.K;
+  const double wb = (double)a.N * (double)a.K * (FMT == 0 ? 0.265625 : 0.53125);
+  int best = 1;
+  for (int p = 2; p <= 8 && p <= tiles_m; p *= 2)
+    if ((8.0 / p) * xb + p * wb < (8.0 / best) * xb + best * wb) best = p;
+  return (tiles_m + best - 1) / best;
+}
+
 template <int FMT, int MT, int NT, int KG, int NSET>
 static hipError_t run_gemm_kgroup(const LinearArgs& a, hipStream_t stream) {
   constexpr int BM = 16 * MT, BN = 64 * NT;
@@ -1805,7 +1823,7 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, hipStream_t stream) {
   const int64_t tiles = tiles_m * ((a.N + BN - 1) / BN);
   if (tiles > 0x7fffffff || a.r > 0) return hipErrorInvalidValue;   // no low-rank epilogue here
   hipLaunchKernelGGL((gemm_kgroup_kernel<FMT, MT, NT, KG, NSET>), dim3((unsigned)tiles), dim3(256 * KG), 0, stream,
-                     a, (int)tiles_m);
+                     a, (int)tiles_m, kgroup_group_rows<FMT>(a, (int)tiles_m));
   return hipGetLastError();
 }
 
