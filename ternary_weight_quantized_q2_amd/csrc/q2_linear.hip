@@ -25,6 +25,8 @@
 // the caches.
 #include "q2_device.h"
 #include "q2_internal.h"
+#include <algorithm>
+#include <cmath>
 #include <cstring>
 
 namespace q2dev {
@@ -1804,15 +1806,24 @@ static hipError_t run_gemm_kpair(const LinearArgs& a, hipStream_t stream) {
 
 // Row tiles per group of the K-group tile order.  Cutting the tile grid into
 // p row parts times 8 / p column parts, one block per XCD, makes the XCDs
-// together read x (8 / p) times and the weights p times; p is the power of two
-// (at most the row-tile count) that minimises that sum.
+// together read the weights p times and x 8 / p times, the latter only while
+// an XCD's rows of x stay in its 4 MB L2: an XCD runs one tile per CU (32 at
+// once), row-fastest through its block, so when the block takes several such
+// rounds and its rows of x exceed ~2.5 MB, every round reads them again.  p is
+// the power of two (at most the row-tile count) with the least modelled sum.
 template <int FMT>
-static int kgroup_group_rows(const LinearArgs& a, int tiles_m) {
-  const double xb = 2.0 * (double)a.M * (double)a.K;
+static int kgroup_group_rows(const LinearArgs& a, int bm, int tiles_m, int tiles_n) {
+  const double xrow = 2.0 * (double)std::min<int64_t>(bm, a.M) * (double)a.K;   // one row tile of x
   const double wb = (double)a.N * (double)a.K * (FMT == 0 ? 0.265625 : 0.53125);
+  const double rounds = std::max(1.0, std::ceil((double)tiles_m * tiles_n / 8.0 / 32.0));
+  auto cost = [&](int p) {
+    const int group = (tiles_m + p - 1) / p;
+    const double xpart = group * xrow;
+    return 8.0 * xpart * (xpart <= 2.5e6 ? 1.0 : rounds) + p * wb;
+  };
   int best = 1;
   for (int p = 2; p <= 8 && p <= tiles_m; p *= 2)
-    if ((8.0 / p) * xb + p * wb < (8.0 / best) * xb + best * wb) best = p;
+    if (cost(p) < cost(best)) best = p;
   return (tiles_m + best - 1) / best;
 }
 
@@ -1823,7 +1834,7 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, hipStream_t stream) {
   const int64_t tiles = tiles_m * ((a.N + BN - 1) / BN);
   if (tiles > 0x7fffffff || a.r > 0) return hipErrorInvalidValue;   // no low-rank epilogue here
   hipLaunchKernelGGL((gemm_kgroup_kernel<FMT, MT, NT, KG, NSET>), dim3((unsigned)tiles), dim3(256 * KG), 0, stream,
-                     a, (int)tiles_m, kgroup_group_rows<FMT>(a, (int)tiles_m));
+                     a, (int)tiles_m, kgroup_group_rows<FMT>(a, BM, (int)tiles_m, (int)((a.N + BN - 1) / BN)));
   return hipGetLastError();
 }
 
