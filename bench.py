@@ -143,6 +143,55 @@ def measure_layer_list(torch, q2, I, dev):
             "weight_bytes": int(layers * (Q2_BYTES_PER_WEIGHT * n * k + 2 * r * (k + n) * 2))}
 
 
+def measure_split_projection(torch, q2, I, dev, reps=20):
+    """The fused output projection of a single transformer block, cut along
+    its input axis (attention output 3072 + MLP output 12288 -> 3072): one
+    writing call and one accumulating call over the two input slices of the
+    weight, against the same product as one call over the whole input (x
+    concatenated).  Reported beside the step, not part of it."""
+    m, k1, k2, n = I.GEMM_M, 3072, 12288, 3072
+    k = k1 + k2
+    p, s = q2.q2_pack(torch.from_numpy(I.q2_codes_fast(950, n, k)).to(dev),
+                      torch.from_numpy(I.q2_scales(950, n, k)).to(dev))
+    p1, s1 = q2.q2_slice(p, s, 0, n, 0, k1)
+    p2, s2 = q2.q2_slice(p, s, 0, n, k1, k)
+    x = torch.from_numpy(I.activations_bf16(950, m, k).view(np.int16)).to(dev).view(torch.bfloat16)
+    x1, x2 = x[:, :k1].contiguous(), x[:, k1:].contiguous()
+    y = torch.empty((m, n), device=dev)
+
+    def split():
+        q2.q2_linear_ex(x1, p1, s1, y=y)
+        q2.q2_linear_ex(x2, p2, s2, y=y, accumulate=True)
+
+    def whole():
+        q2.q2_linear(x, p, s, y=y)
+
+    res = {}
+    for name, fn in (("split", split), ("whole", whole)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):                  # best of three replays: the clocks settle after the layer list
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3 / reps)
+        res[name] = best
+        del g
+    flops = 2.0 * m * n * k
+    return {"shape": f"M={m} K={k1}+{k2} N={n}", "us_split": round(res["split"] * 1e6, 3),
+            "us_whole": round(res["whole"] * 1e6, 3), "tflops_split": round(flops / res["split"] / 1e12, 3),
+            "frac_split": round(flops / res["split"] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +202,7 @@ def main():
                     "print only the wall time (no graph, no per-call events)")
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
                     "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref")
+    ap.add_argument("--no-split", action="store_true", help="skip the split output projection measurement")
     ap.add_argument("--no-layer-list", action="store_true",
                     help="skip the 100-linear rank-32 layer list report")
     args = ap.parse_args()
@@ -297,6 +347,7 @@ def main():
         del g
 
     layer_list = None if (args.no_layer_list or args.only) else measure_layer_list(torch, q2, I, dev)
+    split_proj = None if (args.no_split or args.only) else measure_split_projection(torch, q2, I, dev)
 
     parts = {}
     fam_time, fam_flops, fam_bytes = {}, {}, {}
@@ -347,6 +398,8 @@ def main():
     }
     if layer_list is not None:
         out["layer_list"] = layer_list
+    if split_proj is not None:
+        out["split_projection"] = split_proj
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

@@ -17,7 +17,8 @@
  *  - Sizes are int64.  M, N, K, r >= 0; K must be a multiple of 128, and at
  *    most 2^24 for the linear entry points (Q2_ERR_SHAPE otherwise).  A call
  *    with M == 0 or N == 0 does nothing and returns Q2_OK; K == 0 writes
- *    zeros (an empty sum).  Pointers to buffers of zero bytes may be NULL.
+ *    zeros (an empty sum), or leaves y as it is under Q2_ACCUMULATE.
+ *    Pointers to buffers of zero bytes may be NULL.
  *  - All array pointers are device pointers; all arrays are dense row-major.
  *    The caller owns every buffer; the library keeps no state between calls
  *    except a per-device architecture check, and is safe to call from several
@@ -122,6 +123,55 @@ int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint1
                       const uint16_t* A_f16, const uint16_t* B_f16, int64_t r,
                       float* y, int64_t M, int64_t N, int64_t K,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Flags of q2_linear_ex. */
+#define Q2_ACCUMULATE 0x1u  /* y += result: y is read, the result added in fp32 once */
+
+/*
+ * q2_linear_ex - q2_linear (r == 0) or q2_linear_lowrank (r > 0) with flags.
+ * Source: We're Teaching Your Browser to Paint, section "The GPU driver, and
+ * the bug that looked like broken math": the fused output projection takes
+ * the concatenation of two activations along its input axis, and is computed
+ * as two multiplies over the matching input slices of the weight (q2_slice),
+ * whose results are summed.  With Q2_ACCUMULATE the second call adds into the
+ * first call's y: each output becomes y_old + v in fp32, where v is exactly
+ * the value the call would write without the flag (so the sum is run-to-run
+ * deterministic).  For a low-rank weight, A is sliced along its input axis
+ * the same way and B is shared: the two branch terms add up to the branch of
+ * the whole input.
+ *   flags  0 or Q2_ACCUMULATE; other bits give Q2_ERR_ARG.
+ * Every other argument, the rules on A, B and the workspace (when r > 0)
+ * and the errors are those of q2_linear_lowrank.  With Q2_ACCUMULATE, y must
+ * not overlap any input.  Asynchronous.
+ */
+int q2_linear_ex(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
+                 const uint16_t* A_f16, const uint16_t* B_f16, int64_t r,
+                 float* y, int64_t M, int64_t N, int64_t K,
+                 void* workspace, size_t workspace_bytes, uint32_t flags, hipStream_t stream);
+
+/*
+ * q2_slice - load-time slicing of a packed weight: rows [n0, n1) and inputs
+ * [k0, k1) of a Q2_0 matrix of N rows and K inputs, copied into a dense
+ * packed matrix of n1 - n0 rows and k1 - k0 inputs.
+ * Source: We're Teaching Your Browser to Paint, section "The GPU driver, and
+ * the bug that looked like broken math": a fused projection (one matrix for
+ * Q, K, V and the MLP input) is cut into its logical row ranges once at load
+ * time, since each row is an independent byte run; the fused output
+ * projection is cut along its input axis.  Codes and scales are copied
+ * unchanged, so the slice's weights equal W[n0:n1, k0:k1] exactly.
+ *   packed, scales_f16   the source, as produced by q2_pack         (in)
+ *   n0, n1               0 <= n0 <= n1 <= N, else Q2_ERR_ARG
+ *   k0, k1               0 <= k0 <= k1 <= K, else Q2_ERR_ARG; multiples of
+ *                        128 (whole blocks), else Q2_ERR_SHAPE
+ *   out_packed  u8  [n1 - n0, (k1 - k0)/4], 16-byte aligned          (out)
+ *   out_scales  u16 [n1 - n0, (k1 - k0)/128]                         (out)
+ * A row range alone needs no copy: rows [n0, n1) of packed start at byte
+ * n0 * K/4 and their scales at element n0 * K/128.  The outputs must not
+ * overlap the source.  An empty range does nothing.  Asynchronous.
+ */
+int q2_slice(const uint8_t* packed, const uint16_t* scales_f16, int64_t N, int64_t K,
+             int64_t n0, int64_t n1, int64_t k0, int64_t k1,
+             uint8_t* out_packed, uint16_t* out_scales, hipStream_t stream);
 
 /*
  * q4_linear - 4-bit variant: y = x W^T with W[n, k] = (q[n, k] - z[n, k/128]) * s[n, k/128],

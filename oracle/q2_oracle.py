@@ -126,9 +126,16 @@ def pack_q2(codes: np.ndarray, scales: np.ndarray):
     bad = np.flatnonzero(~ok)
     if bad.size:
         raise PackError("scale", int(bad[0]))
-    c = codes.reshape(n, k // 4, 4).astype(np.uint32)
+    return pack_codes_q2(codes), half.view(np.uint16)
+
+
+def pack_codes_q2(codes: np.ndarray) -> np.ndarray:
+    """codes [N, K] in {0,1,2} (K a multiple of 4) -> bytes [N, K/4], byte j
+    = c[4j] | c[4j+1] << 2 | c[4j+2] << 4 | c[4j+3] << 6."""
+    n, k = codes.shape
+    c = np.asarray(codes).reshape(n, k // 4, 4).astype(np.uint32)
     packed = c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)
-    return packed.astype(np.uint8), half.view(np.uint16)
+    return packed.astype(np.uint8)
 
 
 # ---------------------------------------------------------------------------
@@ -177,6 +184,36 @@ def q2_linear_cols(x_bits, packed, scale_bits, cols) -> np.ndarray:
     """The columns `cols` of q2_linear, decoding only those weight rows."""
     cols = np.asarray(cols)
     return bf16_to_f64(x_bits) @ unpack_q2(packed[cols], scale_bits[cols]).T
+
+
+# ---------------------------------------------------------------------------
+# Weight slices and the input-axis split
+# ---------------------------------------------------------------------------
+# "We're Teaching Your Browser to Paint", section "The GPU driver, and the bug
+# that looked like broken math": a fused weight is cut once at load time into
+# its logical row ranges, and the fused output projection, whose input is two
+# activations side by side, is cut along its input axis into two products that
+# are summed -- the same mathematics as the whole product.
+
+def slice_q2(packed: np.ndarray, scale_bits: np.ndarray, n0: int, n1: int, k0: int, k1: int):
+    """The Q2_0 form of the sub-matrix W[n0:n1, k0:k1] (k0, k1 multiples of
+    128): its codes packed four per byte from column k0 on, and the scales of
+    its whole blocks, unchanged."""
+    if k0 % GROUP or k1 % GROUP:
+        raise ValueError("slice_q2: input range must fall on 128-weight blocks")
+    codes = codes_q2(packed)[n0:n1, k0:k1]
+    return pack_codes_q2(codes), np.ascontiguousarray(scale_bits[n0:n1, k0 // GROUP:k1 // GROUP])
+
+
+def q2_linear_sum(parts, y0=None) -> np.ndarray:
+    """y0 (when given) plus the sum over parts of each part's linear.  A part
+    is (x_bits, packed, scale_bits) or (x_bits, packed, scale_bits, a_bits,
+    b_bits), as for q2_linear / q2_linear_lowrank."""
+    y = None if y0 is None else np.asarray(y0, dtype=np.float64).copy()
+    for part in parts:
+        term = q2_linear(*part) if len(part) == 3 else q2_linear_lowrank(*part)
+        y = term if y is None else y + term
+    return y
 
 
 # ---------------------------------------------------------------------------

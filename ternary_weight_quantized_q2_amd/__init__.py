@@ -26,8 +26,10 @@ LIB_PATH = os.environ.get("Q2_LIB") or os.path.join(_HERE, "libq2.so")
 Q2_OK, Q2_ERR_ARG, Q2_ERR_SHAPE, Q2_ERR_ALIGN, Q2_ERR_CODE, Q2_ERR_SCALE, Q2_ERR_DEVICE, Q2_ERR_HIP, \
     Q2_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
-EXPORTS = ("q2_pack", "q2_linear", "q2_lowrank_workspace_bytes", "q2_linear_lowrank", "q4_linear",
-           "q2_dequant", "q2_strerror", "q2_last_error")
+Q2_ACCUMULATE = 0x1      # q2_linear_ex flag: y += result
+
+EXPORTS = ("q2_pack", "q2_linear", "q2_lowrank_workspace_bytes", "q2_linear_lowrank", "q2_linear_ex", "q2_slice",
+           "q4_linear", "q2_dequant", "q2_strerror", "q2_last_error")
 
 _lib = None
 
@@ -54,6 +56,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "q2_linear": ([p, p, p, p, i64, i64, i64, p], ctypes.c_int),
         "q2_lowrank_workspace_bytes": ([i64, i64], sz),
         "q2_linear_lowrank": ([p, p, p, p, p, i64, p, i64, i64, i64, p, sz, p], ctypes.c_int),
+        "q2_linear_ex": ([p, p, p, p, p, i64, p, i64, i64, i64, p, sz, ctypes.c_uint32, p], ctypes.c_int),
+        "q2_slice": ([p, p, i64, i64, i64, i64, i64, i64, p, p, p], ctypes.c_int),
         "q4_linear": ([p, p, p, p, p, i64, i64, i64, p], ctypes.c_int),
         "q2_dequant": ([p, p, p, i64, i64, p], ctypes.c_int),
         "q2_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -146,6 +150,58 @@ def q2_linear_lowrank(x, packed, scales, A, B, y=None, workspace=None) -> torch.
                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     _check(st)
     return y
+
+
+def q2_linear_ex(x, packed, scales, y=None, A=None, B=None, accumulate=False, workspace=None) -> torch.Tensor:
+    """q2_linear (A, B None) or q2_linear_lowrank with flags; accumulate=True adds the result into y,
+    which must then be given."""
+    lib = load()
+    m, k = x.shape
+    n = packed.shape[0]
+    _want(x, torch.bfloat16, (m, k), "x")
+    _want(packed, torch.uint8, (n, k // 4), "packed")
+    _want(scales, torch.float16, (n, k // 128), "scales")
+    if (A is None) != (B is None):
+        raise ValueError("A and B come together")
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _want(A, torch.float16, (r, k), "A")
+        _want(B, torch.float16, (n, r), "B")
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs y")
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _want(y, torch.float32, (m, n), "y")
+    ws_bytes = 0
+    if r:
+        need = lowrank_workspace_bytes(m, r)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.q2_linear_ex(_ptr(x), _ptr(packed), _ptr(scales), _ptr(A), _ptr(B), r, _ptr(y), m, n, k,
+                          _ptr(workspace), ws_bytes, Q2_ACCUMULATE if accumulate else 0, _stream())
+    _check(st)
+    return y
+
+
+def q2_slice(packed, scales, n0: int, n1: int, k0: int, k1: int, out=None, out_scales=None):
+    """Rows [n0, n1) and inputs [k0, k1) (multiples of 128) of a packed Q2_0 weight, as a new dense
+    packed weight: (packed u8 [n1-n0, (k1-k0)/4], scales f16 [n1-n0, (k1-k0)/128])."""
+    lib = load()
+    n, kq = packed.shape
+    k = kq * 4
+    _want(packed, torch.uint8, (n, kq), "packed")
+    _want(scales, torch.float16, (n, k // 128), "scales")
+    rows, ks = max(n1 - n0, 0), max(k1 - k0, 0)
+    dev = packed.device
+    if out is None:
+        out = torch.empty((rows, ks // 4), dtype=torch.uint8, device=dev)
+    if out_scales is None:
+        out_scales = torch.empty((rows, ks // 128), dtype=torch.float16, device=dev)
+    _want(out, torch.uint8, (rows, ks // 4), "out")
+    _want(out_scales, torch.float16, (rows, ks // 128), "out_scales")
+    _check(lib.q2_slice(_ptr(packed), _ptr(scales), n, k, n0, n1, k0, k1, _ptr(out), _ptr(out_scales), _stream()))
+    return out, out_scales
 
 
 def q4_linear(x, packed4, scale, zero, y=None) -> torch.Tensor:

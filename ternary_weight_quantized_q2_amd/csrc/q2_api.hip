@@ -100,16 +100,52 @@ int forced_cfg() {
 
 int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* s, const uint16_t* z, float* y,
                   int64_t M, int64_t N, int64_t K, const uint16_t* lr_t, const uint16_t* lr_b, int64_t r,
-                  hipStream_t stream) {
+                  bool accumulate, hipStream_t stream) {
   q2dev::LinearArgs a;
   a.x = x; a.w = w; a.s = s; a.z = z; a.y = y;
   a.M = M; a.N = N; a.K = K;
   a.lr_t = lr_t; a.lr_b = lr_b; a.r = (int)r;
+  a.acc = accumulate ? 1 : 0;
   int path = forced_path();
   if (path == 1 && M > 16) path = 0;
   const int cfg = forced_cfg();
   if (cfg < 0) return fail(Q2_ERR_ARG, "unknown Q2_GEMM_TILE configuration");
   return hip_status(q2dev::launch_linear(a, fmt, path, cfg, stream), fmt == 0 ? "q2 linear launch" : "q4 linear launch");
+}
+
+// The Q2_0 linear entry points: y = x W^T (+ (x A^T) B^T when r > 0), written
+// or, with Q2_ACCUMULATE, added to y.
+int linear_entry(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16, const uint16_t* A_f16,
+                 const uint16_t* B_f16, int64_t r, float* y, int64_t M, int64_t N, int64_t K, void* workspace,
+                 size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+  int st = check_sizes(M, N, K);
+  if (st || (st = check_linear_k(K))) return st;
+  if (flags & ~(uint32_t)Q2_ACCUMULATE) return fail(Q2_ERR_ARG, "unknown flag bits 0x%x", flags & ~Q2_ACCUMULATE);
+  if (r < 0) return fail(Q2_ERR_ARG, "negative rank r=%lld", (long long)r);
+  if (r > 65535) return fail(Q2_ERR_ARG, "rank r=%lld too large (at most 65535)", (long long)r);
+  if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
+      (st = check_ptr(packed, N > 0 && K > 0, 16, "packed")) ||
+      (st = check_ptr(scales_f16, N > 0 && K > 0, 2, "scales_f16")))
+    return st;
+  if (r > 0 && ((st = check_ptr(A_f16, K > 0, 16, "A")) || (st = check_ptr(B_f16, N > 0, 2, "B")))) return st;
+  if ((st = check_ptr(y, M > 0 && N > 0, 4, "y"))) return st;
+  if (M == 0 || N == 0) return ok();
+  const bool accumulate = (flags & Q2_ACCUMULATE) != 0;
+  if (accumulate && K == 0) return ok();           // an empty sum added: y stays as it is
+  uint16_t* tl = nullptr;
+  if (r > 0) {
+    const size_t need = q2_lowrank_workspace_bytes(M, r);
+    if (workspace_bytes < need)
+      return fail(Q2_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (workspace == nullptr) return fail(Q2_ERR_ARG, "workspace is NULL");
+    if (!aligned(workspace, 256)) return fail(Q2_ERR_ALIGN, "workspace is not 256-byte aligned");
+    tl = static_cast<uint16_t*>(workspace);
+  }
+  if ((st = check_device())) return st;
+  if (r > 0 &&
+      (st = hip_status(q2dev::launch_lowrank_t(x_bf16, A_f16, tl, M, K, (int)r, stream), "low-rank x A^T launch")))
+    return st;
+  return linear_common(0, x_bf16, packed, scales_f16, nullptr, y, M, N, K, tl, B_f16, r, accumulate, stream);
 }
 
 }  // namespace
@@ -175,43 +211,21 @@ int q2_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K, uin
 
 int q2_linear(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16, float* y, int64_t M,
               int64_t N, int64_t K, hipStream_t stream) {
-  int st = check_sizes(M, N, K);
-  if (st || (st = check_linear_k(K))) return st;
-  if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
-      (st = check_ptr(packed, N > 0 && K > 0, 16, "packed")) ||
-      (st = check_ptr(scales_f16, N > 0 && K > 0, 2, "scales_f16")) ||
-      (st = check_ptr(y, M > 0 && N > 0, 4, "y")))
-    return st;
-  if (M == 0 || N == 0) return ok();
-  if ((st = check_device())) return st;
-  return linear_common(0, x_bf16, packed, scales_f16, nullptr, y, M, N, K, nullptr, nullptr, 0, stream);
+  return linear_entry(x_bf16, packed, scales_f16, nullptr, nullptr, 0, y, M, N, K, nullptr, 0, 0u, stream);
 }
 
 int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
                       const uint16_t* A_f16, const uint16_t* B_f16, int64_t r, float* y, int64_t M, int64_t N,
                       int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int st = check_sizes(M, N, K);
-  if (st || (st = check_linear_k(K))) return st;
-  if (r < 0) return fail(Q2_ERR_ARG, "negative rank r=%lld", (long long)r);
-  if (r > 65535) return fail(Q2_ERR_ARG, "rank r=%lld too large (at most 65535)", (long long)r);
-  if (r == 0) return q2_linear(x_bf16, packed, scales_f16, y, M, N, K, stream);
-  if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
-      (st = check_ptr(packed, N > 0 && K > 0, 16, "packed")) ||
-      (st = check_ptr(scales_f16, N > 0 && K > 0, 2, "scales_f16")) ||
-      (st = check_ptr(A_f16, K > 0, 16, "A")) || (st = check_ptr(B_f16, N > 0, 2, "B")) ||
-      (st = check_ptr(y, M > 0 && N > 0, 4, "y")))
-    return st;
-  if (M == 0 || N == 0) return ok();
-  const size_t need = q2_lowrank_workspace_bytes(M, r);
-  if (workspace_bytes < need)
-    return fail(Q2_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  if (workspace == nullptr) return fail(Q2_ERR_ARG, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(Q2_ERR_ALIGN, "workspace is not 256-byte aligned");
-  if ((st = check_device())) return st;
-  uint16_t* tl = static_cast<uint16_t*>(workspace);
-  if ((st = hip_status(q2dev::launch_lowrank_t(x_bf16, A_f16, tl, M, K, (int)r, stream), "low-rank x A^T launch")))
-    return st;
-  return linear_common(0, x_bf16, packed, scales_f16, nullptr, y, M, N, K, tl, B_f16, r, stream);
+  return linear_entry(x_bf16, packed, scales_f16, A_f16, B_f16, r, y, M, N, K, workspace, workspace_bytes, 0u,
+                      stream);
+}
+
+int q2_linear_ex(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16, const uint16_t* A_f16,
+                 const uint16_t* B_f16, int64_t r, float* y, int64_t M, int64_t N, int64_t K, void* workspace,
+                 size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+  return linear_entry(x_bf16, packed, scales_f16, A_f16, B_f16, r, y, M, N, K, workspace, workspace_bytes, flags,
+                      stream);
 }
 
 int q4_linear(const uint16_t* x_bf16, const uint8_t* packed4, const uint16_t* scale_f16, const uint16_t* zero_f16,
@@ -225,7 +239,28 @@ int q4_linear(const uint16_t* x_bf16, const uint8_t* packed4, const uint16_t* sc
     return st;
   if (M == 0 || N == 0) return ok();
   if ((st = check_device())) return st;
-  return linear_common(1, x_bf16, packed4, scale_f16, zero_f16, y, M, N, K, nullptr, nullptr, 0, stream);
+  return linear_common(1, x_bf16, packed4, scale_f16, zero_f16, y, M, N, K, nullptr, nullptr, 0, false, stream);
+}
+
+int q2_slice(const uint8_t* packed, const uint16_t* scales_f16, int64_t N, int64_t K, int64_t n0, int64_t n1,
+             int64_t k0, int64_t k1, uint8_t* out_packed, uint16_t* out_scales, hipStream_t stream) {
+  int st = check_sizes(0, N, K);
+  if (st) return st;
+  if (n0 < 0 || n1 < n0 || n1 > N || k0 < 0 || k1 < k0 || k1 > K)
+    return fail(Q2_ERR_ARG, "slice rows [%lld, %lld) / inputs [%lld, %lld) outside N=%lld K=%lld", (long long)n0,
+                (long long)n1, (long long)k0, (long long)k1, (long long)N, (long long)K);
+  if (k0 % 128 != 0 || k1 % 128 != 0)
+    return fail(Q2_ERR_SHAPE, "slice inputs [%lld, %lld) not on 128-weight block boundaries", (long long)k0,
+                (long long)k1);
+  const bool ne = n1 > n0 && k1 > k0;
+  if ((st = check_ptr(packed, ne, 16, "packed")) || (st = check_ptr(scales_f16, ne, 2, "scales_f16")) ||
+      (st = check_ptr(out_packed, ne, 16, "out_packed")) || (st = check_ptr(out_scales, ne, 2, "out_scales")))
+    return st;
+  if (!ne) return ok();
+  if ((st = check_device())) return st;
+  return hip_status(q2dev::launch_slice(packed, scales_f16, K, n0, n1 - n0, k0, k1 - k0, out_packed, out_scales,
+                                        stream),
+                    "slice launch");
 }
 
 int q2_dequant(const uint8_t* packed, const uint16_t* scales_f16, float* w, int64_t N, int64_t K,

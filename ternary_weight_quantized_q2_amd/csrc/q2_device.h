@@ -39,6 +39,30 @@ namespace q2dev {
 constexpr int WAVE = 64;
 constexpr int BLOCK_K = 128;          // weights per Q2_0 block / 4-bit group
 
+// Output tiles of the GEMM kernels are stored non-temporally, so the fp32
+// output does not displace the operands that later tiles read from L2.  Under
+// accumulation (y += result) a thread first loads every y value it will write,
+// all at once, before the tile's final reduction: a load issued after a store
+// would wait for that store (loads and stores share one counter), so loading
+// piece by piece between the stores would pay one memory round trip each.
+__device__ __forceinline__ float y_old(const float* p, bool valid) {
+  return valid ? __builtin_nontemporal_load(p) : 0.0f;
+}
+__device__ __forceinline__ q2_f32x4 y_old4(const q2_f32x4* p, bool valid) {
+  return valid ? __builtin_nontemporal_load(p) : q2_f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Piece t of the row-major stores of a BM x BN output tile by THREADS
+// threads: 16 bytes at tile row `row`, columns 4q .. 4q+3.  False when the
+// piece is past the tile, past row M - 1 or past the ncols valid columns.
+template <int BM, int BN, int THREADS>
+__device__ __forceinline__ bool row_piece(int t, int tid, int64_t m0, int64_t M, int64_t ncols, int& row, int& q) {
+  const int idx = tid + t * THREADS;
+  row = idx / (BN / 4);
+  q = idx - row * (BN / 4);
+  return idx < BM * (BN / 4) && m0 + row < M && 4 * q < ncols;
+}
+
 __device__ __forceinline__ q2_f32x4 mfma(q2_u32x4 a, q2_u32x4 b, q2_f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(q2_bf16x8, a),
                                                   __builtin_bit_cast(q2_bf16x8, b), c, 0, 0, 0);

@@ -18,6 +18,7 @@ struct LinearArgs {
   const uint16_t* lr_t;
   const uint16_t* lr_b;
   int r;
+  int acc;               // 1: y += result (y is read), 0: y = result
 };
 
 // Path selection for tests: force_path 0 = automatic, 1 = force GEMV, 2 = force
@@ -32,6 +33,7 @@ hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t N, int
                        hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* packed, const uint16_t* scales, float* w,
                           int64_t N, int64_t K, hipStream_t stream);
-hipError_t launch_zero_fill(float* y, int64_t count, hipStream_t stream);
+hipError_t launch_slice(const uint8_t* packed, const uint16_t* scales, int64_t K, int64_t n0, int64_t rows,
+                        int64_t k0, int64_t ks, uint8_t* out, uint16_t* out_scales, hipStream_t stream);
 
 }  // namespace q2dev

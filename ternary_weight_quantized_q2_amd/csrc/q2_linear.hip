@@ -563,6 +563,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
     }
   }
 
+  if (a.acc) {                            // every old value in flight at once, then added
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t m = m0 + 16 * i + 4 * g + e, n = nw + 16 * j + c;
+          acc[i][j][e] += y_old(&a.y[m * N + n], m < M && n < N);
+        }
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -961,6 +972,19 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       }
     }
   }
+  // Under accumulation the old y values of the row-major stores are loaded
+  // now, while the tile is reduced.
+  const bool rows16 = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
+  constexpr int RP = (BM * (BN / 4) + 511) / 512;
+  q2_f32x4 yo4[RP];
+  if (a.acc && rows16) {
+#pragma unroll
+    for (int t = 0; t < RP; ++t) {
+      int row, q;
+      const bool v = row_piece<BM, BN, 512>(t, tid, m0, M, ncols, row, q);
+      yo4[t] = y_old4(reinterpret_cast<const q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]), v);
+    }
+  }
   // Every wave is done reading activations and low-rank operands: the reduction
   // buffer may overwrite them.
   __syncthreads();
@@ -976,7 +1000,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
         for (int e = 0; e < 4; ++e) red[((i * NT + j) * 4 + e) * 64 + lane] = acc[i][j][e];
   }
   __syncthreads();
-  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0) {
+  if (rows16) {
     // The finished tile goes through LDS once more (rows padded to OS floats,
     // so the writes are conflict-free), and every lane then stores 16
     // contiguous bytes of a row: whole lines reach memory instead of the
@@ -1002,15 +1026,28 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
           for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * OS + wn * (BN / 4) + 16 * j + c] = acc[i][j][e];
     }
     __syncthreads();
-    const int64_t ncols = (N - n0) < BN ? (N - n0) : BN;
-    for (int idx = tid; idx < BM * (BN / 4); idx += 512) {
-      const int row = idx / (BN / 4), q = idx - row * (BN / 4);
-      const int64_t m = m0 + row;
-      if (m < M && 4 * q < ncols)
-        __builtin_nontemporal_store(*reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]),
-                                    reinterpret_cast<q2_f32x4*>(&a.y[m * N + n0 + 4 * q]));
+#pragma unroll
+    for (int t = 0; t < RP; ++t) {
+      int row, q;
+      if (row_piece<BM, BN, 512>(t, tid, m0, M, ncols, row, q)) {
+        q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
+        if (a.acc) v += yo4[t];
+        __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
+      }
     }
   } else if (par == 0) {
+    float yo[MT][NT][4];
+    if (a.acc) {                          // every old value in flight at once, then added
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t m = m0 + 16 * i + 4 * g + e, n = nw + 16 * j + c;
+            yo[i][j][e] = y_old(&a.y[m * N + n], m < M && n < N);
+          }
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -1018,7 +1055,8 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
         const int64_t n = nw + 16 * j + c;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float v = acc[i][j][e] + red[((i * NT + j) * 4 + e) * 64 + lane];
+          float v = acc[i][j][e] + red[((i * NT + j) * 4 + e) * 64 + lane];
+          if (a.acc) v += yo[i][j][e];
           const int64_t m = m0 + 16 * i + 4 * g + e;
           if (m < M && n < N) __builtin_nontemporal_store(v, &a.y[m * N + n]);
         }
@@ -1394,6 +1432,20 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   __builtin_amdgcn_s_waitcnt(0);          // every copy of this wave has landed
   __syncthreads();                        // and every wave is done reading the stages
 
+  // Under accumulation the old y values of the row-major stores are loaded
+  // now, while the tile is reduced.
+  const bool rows16 = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
+  constexpr int RP = (BM * (BN / 4) + 64 * W - 1) / (64 * W);
+  q2_f32x4 yo4[RP];
+  if (a.acc && rows16) {
+#pragma unroll
+    for (int t = 0; t < RP; ++t) {
+      int row, q;
+      const bool v = row_piece<BM, BN, 64 * W>(t, tid, m0, M, ncols, row, q);
+      yo4[t] = y_old4(reinterpret_cast<const q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]), v);
+    }
+  }
+
   // Partial sums of groups 1 .. KG-1 -> LDS -> added in group order by group 0.
   float* const red = reinterpret_cast<float*>(smem);
   constexpr int PART = MT * NT * 4 * 64;  // floats per wave
@@ -1408,7 +1460,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   }
   __syncthreads();
   const float fin = (FMT == 0) ? 4.f : 16.f;
-  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0) {
+  if (rows16) {
     // As in the K-pair kernel: the finished tile goes through LDS (rows padded
     // to OS floats) and is stored as 16-byte pieces of contiguous rows.
     constexpr int OS = BN + 4;
@@ -1437,15 +1489,28 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
           for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * OS + wn * (BN / 4) + 16 * j + c] = acc[i][j][e];
     }
     __syncthreads();
-    const int64_t ncols = (N - n0) < BN ? (N - n0) : BN;
-    for (int idx = tid; idx < BM * (BN / 4); idx += 64 * W) {
-      const int row = idx / (BN / 4), q = idx - row * (BN / 4);
-      const int64_t m = m0 + row;
-      if (m < M && 4 * q < ncols)
-        __builtin_nontemporal_store(*reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]),
-                                    reinterpret_cast<q2_f32x4*>(&a.y[m * N + n0 + 4 * q]));
+#pragma unroll
+    for (int t = 0; t < RP; ++t) {
+      int row, q;
+      if (row_piece<BM, BN, 64 * W>(t, tid, m0, M, ncols, row, q)) {
+        q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
+        if (a.acc) v += yo4[t];
+        __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
+      }
     }
   } else if (kg == 0) {
+    float yo[MT][NT][4];
+    if (a.acc) {                          // every old value in flight at once, then added
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t m = m0 + 16 * i + 4 * g + e, n = nw + 16 * j + c;
+            yo[i][j][e] = y_old(&a.y[m * N + n], m < M && n < N);
+          }
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -1456,8 +1521,10 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
           float v = acc[i][j][e];
 #pragma unroll
           for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
+          v *= fin;
+          if (a.acc) v += yo[i][j][e];
           const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (m < M && n < N) __builtin_nontemporal_store(v * fin, &a.y[m * N + n]);
+          if (m < M && n < N) __builtin_nontemporal_store(v, &a.y[m * N + n]);
         }
       }
     }
@@ -1628,6 +1695,16 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
     __syncthreads();
   }
 
+  // Under accumulation wave 0 loads its old y values before the reduction.
+  float yo[4] = {0.f, 0.f, 0.f, 0.f};
+  if (a.acc && wv == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * g + e;
+      yo[e] = (n < a.N && m < M) ? a.y[(int64_t)m * a.N + n] : 0.f;
+    }
+  }
+
   // fixed-order reduction over the waves' K partitions
   q2_f32x4* red = reinterpret_cast<q2_f32x4*>(smem);
   red[wv * 64 + lane] = acc;
@@ -1645,7 +1722,7 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 4 * g + e;
-        if (m < M) a.y[(int64_t)m * a.N + n] = s[e];
+        if (m < M) a.y[(int64_t)m * a.N + n] = a.acc ? s[e] + yo[e] : s[e];
       }
     }
   }

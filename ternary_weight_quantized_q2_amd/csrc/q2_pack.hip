@@ -1,5 +1,5 @@
-// q2_pack.hip - load-time Q2_0 packing with validation, and the exact decode
-// used by tests.
+// q2_pack.hip - load-time Q2_0 packing with validation, slicing of packed
+// weights, and the exact decode used by tests.
 //
 // Packing follows the Q2_0 layout of "We're Teaching Your Browser to Paint"
 // (aitherium.com), section "The lucky break that wasn't luck": four 2-bit
@@ -64,9 +64,30 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* packed, con
   }
 }
 
-__global__ __launch_bounds__(256) void zero_fill_kernel(float* y, int64_t count) {
+// Rows [n0, n0 + rows) and input columns [k0, k0 + ks) of a packed matrix
+// with K inputs per row (K, k0 and ks multiples of 128) into a dense packed
+// matrix of ks inputs per row.  Rows are independent byte runs and a block's
+// codes are 32 whole bytes, so this is a plain copy: one thread per 16 code
+// bytes (the source and destination offsets are multiples of 16), then one
+// per scale.
+__global__ __launch_bounds__(256) void slice_kernel(const uint8_t* packed, const uint16_t* s, int64_t K,
+                                                    int64_t n0, int64_t rows, int64_t k0, int64_t ks,
+                                                    uint8_t* out, uint16_t* out_s) {
+  const int64_t chunks = ks / 64;                 // 16-byte pieces per output row
+  const int64_t nb = ks / BLOCK_K;                // scales per output row
+  const int64_t code_work = rows * chunks;
+  const int64_t total = code_work + rows * nb;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    if (i < code_work) {
+      const int64_t row = i / chunks, c = i - row * chunks;
+      const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(packed + (n0 + row) * (K / 4) + k0 / 4 + 16 * c);
+      *reinterpret_cast<q2_u32x4*>(out + row * (ks / 4) + 16 * c) = v;
+    } else {
+      const int64_t j = i - code_work, row = j / nb, b = j - row * nb;
+      out_s[row * nb + b] = s[(n0 + row) * (K / BLOCK_K) + k0 / BLOCK_K + b];
+    }
+  }
 }
 
 static unsigned grid_for(int64_t work) {
@@ -94,8 +115,11 @@ hipError_t launch_dequant(const uint8_t* packed, const uint16_t* scales, float* 
   return hipGetLastError();
 }
 
-hipError_t launch_zero_fill(float* y, int64_t count, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_fill_kernel, dim3(grid_for(count)), dim3(256), 0, stream, y, count);
+hipError_t launch_slice(const uint8_t* packed, const uint16_t* scales, int64_t K, int64_t n0, int64_t rows,
+                        int64_t k0, int64_t ks, uint8_t* out, uint16_t* out_scales, hipStream_t stream) {
+  const int64_t work = rows * (ks / 64 + ks / BLOCK_K);
+  hipLaunchKernelGGL(slice_kernel, dim3(grid_for(work)), dim3(256), 0, stream, packed, scales, K, n0, rows, k0, ks,
+                     out, out_scales);
   return hipGetLastError();
 }
 

@@ -89,6 +89,44 @@ def test_lowrank_argument_errors(lib):
     assert LR(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 16, 8, 96, FAKE, need, None) == q2.Q2_ERR_SHAPE
 
 
+def test_linear_ex_argument_errors(lib):
+    E = lib.q2_linear_ex
+    need = lib.q2_lowrank_workspace_bytes(16, 8)
+    acc = q2.Q2_ACCUMULATE
+    # unknown flag bits, then the q2_linear / q2_linear_lowrank rules
+    assert E(FAKE, FAKE, FAKE, None, None, 0, FAKE, 16, 8, 128, None, 0, 2, None) == q2.Q2_ERR_ARG
+    assert b"flag" in lib.q2_last_error()
+    assert E(FAKE, FAKE, FAKE, None, None, 0, FAKE, 16, 8, 100, None, 0, acc, None) == q2.Q2_ERR_SHAPE
+    assert E(FAKE, FAKE, FAKE, None, None, 0, None, 16, 8, 128, None, 0, acc, None) == q2.Q2_ERR_ARG
+    assert E(FAKE, FAKE, FAKE, None, None, 0, FAKE + 2, 16, 8, 128, None, 0, acc, None) == q2.Q2_ERR_ALIGN
+    assert E(FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 16, 8, 128, FAKE, need, acc, None) == q2.Q2_ERR_ARG
+    assert E(FAKE, FAKE, FAKE, None, FAKE, 8, FAKE, 16, 8, 128, FAKE, need, acc, None) == q2.Q2_ERR_ARG
+    assert E(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 16, 8, 128, FAKE, need - 1, acc, None) == q2.Q2_ERR_WORKSPACE
+    assert E(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 16, 8, 128, FAKE + 16, need, acc, None) == q2.Q2_ERR_ALIGN
+    # r == 0 ignores A, B and the workspace; empty problems and an empty sum added touch nothing
+    assert E(None, FAKE, FAKE, None, None, 0, None, 0, 8, 128, None, 0, acc, None) == q2.Q2_OK
+    assert E(FAKE, None, None, None, None, 0, FAKE, 16, 8, 0, None, 0, acc, None) == q2.Q2_OK
+
+
+def test_slice_argument_errors(lib):
+    S = lib.q2_slice
+    assert S(FAKE, FAKE, 8, 512, 0, 9, 0, 128, FAKE, FAKE, None) == q2.Q2_ERR_ARG       # n1 > N
+    assert S(FAKE, FAKE, 8, 512, 5, 4, 0, 128, FAKE, FAKE, None) == q2.Q2_ERR_ARG       # n1 < n0
+    assert S(FAKE, FAKE, 8, 512, -1, 4, 0, 128, FAKE, FAKE, None) == q2.Q2_ERR_ARG
+    assert S(FAKE, FAKE, 8, 512, 0, 4, 256, 128, FAKE, FAKE, None) == q2.Q2_ERR_ARG     # k1 < k0
+    assert S(FAKE, FAKE, 8, 512, 0, 4, 0, 640, FAKE, FAKE, None) == q2.Q2_ERR_ARG       # k1 > K
+    assert S(FAKE, FAKE, 8, 512, 0, 4, 64, 256, FAKE, FAKE, None) == q2.Q2_ERR_SHAPE    # not on a block boundary
+    assert b"block" in lib.q2_last_error()
+    assert S(FAKE, FAKE, 8, 500, 0, 4, 0, 128, FAKE, FAKE, None) == q2.Q2_ERR_SHAPE     # K itself
+    assert S(FAKE, FAKE, 8, 512, 0, 4, 0, 128, FAKE + 4, FAKE, None) == q2.Q2_ERR_ALIGN
+    assert S(FAKE, FAKE, 8, 512, 0, 4, 0, 128, FAKE, FAKE + 1, None) == q2.Q2_ERR_ALIGN
+    assert S(FAKE, None, 8, 512, 0, 4, 0, 128, FAKE, FAKE, None) == q2.Q2_ERR_ARG
+    assert S(FAKE, FAKE, 8, 512, 0, 4, 0, 128, None, FAKE, None) == q2.Q2_ERR_ARG
+    # empty ranges do nothing, NULL pointers allowed
+    assert S(None, None, 8, 512, 3, 3, 0, 128, None, None, None) == q2.Q2_OK
+    assert S(None, None, 8, 512, 0, 8, 256, 256, None, None, None) == q2.Q2_OK
+
+
 def test_pack_argument_errors(lib):
     bad = ctypes.c_int64(123)
     P = lib.q2_pack

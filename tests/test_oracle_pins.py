@@ -220,6 +220,68 @@ def test_input_axis_split_is_sum_of_two_products():
     assert np.allclose(y1 + y2, y, rtol=1e-12, atol=1e-12)
 
 
+SLICE_CASES = [(0, 9, 0, 640), (2, 7, 128, 384), (8, 9, 512, 640), (0, 1, 0, 128), (3, 3, 0, 128),
+               (4, 6, 256, 256), (1, 8, 384, 640)]
+
+
+def check_slice(slice_fn):
+    """A slice decodes, element by element, to the matching part of the whole
+    matrix under the literal per-element decode (pinned by the bit-order and
+    closed-form checks), and its bytes are those of the sliced codes packed
+    afresh."""
+    n, k = 9, 640
+    codes = I.q2_codes(97, n, k)
+    scales = I.q2_scales(97, n, k)
+    packed, sc = O.pack_q2(codes, scales)
+    full = O.unpack_q2_scalar(packed, sc, n, k)
+    for n0, n1, k0, k1 in SLICE_CASES:
+        sp, ss = slice_fn(packed, sc, n0, n1, k0, k1)
+        assert sp.shape == (n1 - n0, (k1 - k0) // 4) and ss.shape == (n1 - n0, (k1 - k0) // 128)
+        if n1 > n0 and k1 > k0:
+            assert O.unpack_q2_scalar(sp, ss, n1 - n0, k1 - k0) == [row[k0:k1] for row in full[n0:n1]]
+            want_p, want_s = O.pack_q2(codes[n0:n1, k0:k1], scales[n0:n1, k0 // 128:k1 // 128])
+            assert np.array_equal(sp, want_p) and np.array_equal(ss, want_s)
+
+
+def test_slice_pins():
+    check_slice(O.slice_q2)
+    with pytest.raises(ValueError):
+        O.slice_q2(np.zeros((2, 64), np.uint8), np.zeros((2, 2), np.uint16), 0, 2, 64, 256)
+
+
+def check_split_sum(sum_fn):
+    """The fused output projection computed as two products over input slices
+    (low-rank A sliced the same way, B shared) plus an existing y0 equals y0
+    plus the whole product, against exact rationals built from the codes."""
+    m, k, n, k1, r = 2, 384, 5, 128, 3
+    codes = I.q2_codes(98, n, k)
+    packed, sc = O.pack_q2(codes, I.q2_scales(98, n, k))
+    xb = I.activations_bf16(98, m, k)
+    a, b = I.lowrank_factors(98, r, k, n, std=0.1)
+    y0 = np.random.default_rng(98).standard_normal((m, n))
+    parts = [(np.ascontiguousarray(xb[:, :k1]), np.ascontiguousarray(packed[:, :k1 // 4]),
+              np.ascontiguousarray(sc[:, :k1 // 128]), np.ascontiguousarray(a[:, :k1]), b),
+             (np.ascontiguousarray(xb[:, k1:]), np.ascontiguousarray(packed[:, k1 // 4:]),
+              np.ascontiguousarray(sc[:, k1 // 128:]), np.ascontiguousarray(a[:, k1:]), b)]
+    y = sum_fn(parts, y0)
+    xs = [[Fraction(O.bf16_decode_scalar(int(v))) for v in row] for row in xb]
+    ds = [[Fraction(O.f16_decode_scalar(int(v))) for v in row] for row in sc]
+    av = [[Fraction(O.f16_decode_scalar(int(v))) for v in row] for row in a]
+    bv = [[Fraction(O.f16_decode_scalar(int(v))) for v in row] for row in b]
+    for i in range(m):
+        t = [sum((xs[i][kk] * av[j][kk] for kk in range(k)), Fraction(0)) for j in range(r)]
+        for j in range(n):
+            w = sum((xs[i][kk] * (int(codes[j, kk]) - 1) * ds[j][kk // 128] for kk in range(k)), Fraction(0))
+            exact = Fraction(float(y0[i, j])) + w + sum((t[q] * bv[j][q] for q in range(r)), Fraction(0))
+            assert abs(float(Fraction(float(y[i, j])) - exact)) <= 1e-12 * (1.0 + abs(float(exact)))
+    # without y0 the sum starts from the first part
+    assert np.array_equal(sum_fn(parts[:1]), O.q2_linear_lowrank(*parts[0]))
+
+
+def test_split_sum_pins():
+    check_split_sum(O.q2_linear_sum)
+
+
 # ---------------------------------------------------------------------------
 # pack: scale round trip and code check
 # ---------------------------------------------------------------------------

@@ -60,7 +60,27 @@ def q4_zero_sign(xb, p4, s, z):              # (q + z) * s
     return O.bf16_to_f64(xb) @ w.T
 
 
+def slice_scales_at_input_column(packed, sc, n0, n1, k0, k1):     # scale index k0 instead of k0 / 128
+    sp, _ = O.slice_q2(packed, sc, n0, n1, k0, k1)
+    nb = (k1 - k0) // 128
+    cols = np.minimum(np.arange(k0, k0 + nb), np.asarray(sc).shape[1] - 1)
+    return sp, np.ascontiguousarray(np.asarray(sc)[n0:n1][:, cols])
+
+
+def slice_codes_at_byte_k0(packed, sc, n0, n1, k0, k1):           # byte offset k0 instead of k0 / 4
+    _, ss = O.slice_q2(packed, sc, n0, n1, k0, k1)
+    p = np.asarray(packed)
+    start = min(k0, p.shape[1] - (k1 - k0) // 4)
+    return np.ascontiguousarray(p[n0:n1, start:start + (k1 - k0) // 4]), ss
+
+
 MUTANTS = {
+    "slice scales at the input column": lambda: P.check_slice(slice_scales_at_input_column),
+    "slice codes at byte k0": lambda: P.check_slice(slice_codes_at_byte_k0),
+    "split sum drops y0": lambda: P.check_split_sum(lambda parts, y0=None: O.q2_linear_sum(parts)),
+    "split sum adds y0 twice": lambda: P.check_split_sum(
+        lambda parts, y0=None: O.q2_linear_sum(parts, y0) + (0 if y0 is None else y0)),
+    "split sum drops the second part": lambda: P.check_split_sum(lambda parts, y0=None: O.q2_linear_sum(parts[:1], y0)),
     "unpack MSB-first": lambda: P.check_q2_bit_order(O.pack_q2, unpack_msb_first, linear_with(unpack_msb_first)),
     "pack MSB-first": lambda: P.check_q2_bit_order(pack_msb_first, O.unpack_q2, O.q2_linear),
     "zero point 0": lambda: P.check_q2_closed_forms(linear_with(unpack_no_offset)),
@@ -86,3 +106,5 @@ def test_unmutated_checks_pass():
     P.check_q2_closed_forms(O.q2_linear)
     P.check_lowrank(O.q2_linear_lowrank)
     P.check_q4(O.q4_linear)
+    P.check_slice(O.slice_q2)
+    P.check_split_sum(O.q2_linear_sum)

@@ -1,0 +1,201 @@
+"""GPU parity of weight slicing and of the input-axis split with accumulation
+(q2_slice, q2_linear_ex with Q2_ACCUMULATE) against the CPU oracle.
+
+Bars: slices bit-exact (codes and scale bits); an accumulating call gives,
+bit for bit, y0 + v in fp32 where v is what the same call writes without the
+flag; the split product within the linear's tolerance of the oracle's whole
+product.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.q2_oracle as O
+import ternary_weight_quantized_q2_amd as q2
+from ternary_weight_quantized_q2_amd import inputs as I
+from tests.test_parity_gpu import DEV, acts, assert_close, dev_bits, host_bits, q2_weights, sample_cols
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU; they must not be skipped silently"
+    torch.cuda.set_device(0)
+    q2.load()
+    yield
+
+
+# ---------------------------------------------------------------------------
+# slicing
+# ---------------------------------------------------------------------------
+
+SLICES = [(0, 9, 0, 640), (2, 7, 128, 384), (8, 9, 512, 640), (0, 1, 0, 128), (3, 3, 0, 128), (4, 6, 256, 256),
+          (1, 8, 384, 640)]
+
+
+@pytest.mark.parametrize("n0,n1,k0,k1", SLICES)
+def test_slice_bitexact(n0, n1, k0, k1):
+    p_dev, s_dev, p_ref, s_ref = q2_weights(41, 9, 640)
+    sp, ss = q2.q2_slice(p_dev, s_dev, n0, n1, k0, k1)
+    torch.cuda.synchronize()
+    want_p, want_s = O.slice_q2(p_ref, s_ref, n0, n1, k0, k1)
+    assert np.array_equal(sp.cpu().numpy(), want_p)
+    assert np.array_equal(host_bits(ss), want_s)
+
+
+# Fused projection of a transformer block at hidden size 3072: Q, K, V and the
+# MLP input (4 x 3072) as one weight of 21504 rows.
+FUSED_PARTS = [(0, 3072), (3072, 6144), (6144, 9216), (9216, 21504)]
+
+
+def test_fused_weight_row_slices():
+    n, k, m = 21504, 3072, 96
+    p_dev, s_dev, p_ref, s_ref = q2_weights(42, n, k)
+    xb, x = acts(42, m, k)
+    for n0, n1 in FUSED_PARTS:
+        sp, ss = q2.q2_slice(p_dev, s_dev, n0, n1, 0, k)
+        torch.cuda.synchronize()
+        want_p, want_s = O.slice_q2(p_ref, s_ref, n0, n1, 0, k)
+        assert np.array_equal(sp.cpu().numpy(), want_p), (n0, n1)
+        assert np.array_equal(host_bits(ss), want_s), (n0, n1)
+        # a row range is also usable in place: rows are contiguous byte runs
+        y_copy = q2.q2_linear(x, sp, ss)
+        y_view = q2.q2_linear(x, p_dev[n0:n1], s_dev[n0:n1])
+        torch.cuda.synchronize()
+        assert torch.equal(y_copy, y_view)
+        cols = sample_cols(n1 - n0, 96, seed=n0)
+        ref = O.q2_linear_cols(xb, want_p, want_s, cols)
+        assert_close(y_copy.cpu().numpy()[:, cols], ref, f"fused rows [{n0}, {n1})")
+
+
+def test_slice_errors():
+    p_dev, s_dev, _, _ = q2_weights(43, 4, 256)
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_slice(p_dev, s_dev, 0, 4, 64, 256)
+    assert e.value.status == q2.Q2_ERR_SHAPE
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_slice(p_dev, s_dev, 0, 5, 0, 256)
+    assert e.value.status == q2.Q2_ERR_ARG
+
+
+# ---------------------------------------------------------------------------
+# accumulation: y0 + v, bit for bit, on every kernel configuration
+# ---------------------------------------------------------------------------
+
+GEMM_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
+             "kg2x1x4", "kg4x2x2", "kg2x1x2", "kg2x2x4", "kg2x2x2", "kg2x1x4r3", "kg6x3x2"]
+LR_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64"]
+
+
+def _set_path(monkeypatch, cfg):
+    monkeypatch.delenv("Q2_FORCE_PATH", raising=False)
+    monkeypatch.delenv("Q2_GEMM_TILE", raising=False)
+    if cfg == "gemv":
+        monkeypatch.setenv("Q2_FORCE_PATH", "gemv")
+    elif cfg != "auto":
+        monkeypatch.setenv("Q2_FORCE_PATH", "gemm")
+        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+
+
+def _acc_case(cfg, m, n, k, r, unaligned=False):
+    p, s, _, _ = q2_weights(44, n, k)
+    _, x = acts(44, m, k)
+    A = B = None
+    if r:
+        a, b = I.lowrank_factors(44, r, k, n, std=0.02)
+        A, B = dev_bits(a, torch.float16), dev_bits(b, torch.float16)
+    g = torch.Generator().manual_seed(45)
+    y0 = torch.randn((m, n), generator=g).to(DEV)
+    if unaligned:                       # y 4 bytes past a 16-byte boundary: the per-element stores
+        flat = torch.zeros(m * n + 4, device=DEV)
+        y = flat[1:1 + m * n].view(m, n)
+        assert y.data_ptr() % 16 == 4
+        y.copy_(y0)
+    else:
+        y = y0.clone()
+    v = q2.q2_linear_ex(x, p, s, A=A, B=B)
+    q2.q2_linear_ex(x, p, s, y=y, A=A, B=B, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0 + v), f"{cfg} M={m} N={n} K={k} r={r}"
+
+
+@pytest.mark.parametrize("cfg", ["auto", "gemv"] + GEMM_CFGS)
+def test_accumulate_is_y0_plus_result(cfg, monkeypatch):
+    _set_path(monkeypatch, cfg)
+    if cfg == "gemv":
+        _acc_case(cfg, 5, 333, 640, 0)
+        _acc_case(cfg, 16, 400, 1280, 0)
+    else:
+        _acc_case(cfg, 192, 400, 640, 0)                   # row-contiguous stores
+        _acc_case(cfg, 192, 333, 640, 0)                   # N not a multiple of 4: per-element stores
+        _acc_case(cfg, 192, 400, 640, 0, unaligned=True)
+
+
+@pytest.mark.parametrize("cfg", ["auto", "gemv"] + LR_CFGS)
+def test_accumulate_lowrank(cfg, monkeypatch):
+    _set_path(monkeypatch, cfg)
+    if cfg == "gemv":
+        _acc_case(cfg, 3, 300, 384, 32)
+    else:
+        _acc_case(cfg, 192, 400, 640, 32)
+        _acc_case(cfg, 192, 333, 640, 8)
+        if cfg != "kpair":                                 # ranks off the 8-multiple take the scalar epilogue
+            _acc_case(cfg, 192, 400, 640, 5)
+
+
+def test_accumulate_empty_sum_keeps_y():
+    m, n = 7, 40
+    y0 = torch.randn((m, n), device=DEV)
+    y = y0.clone()
+    x = torch.empty((m, 0), dtype=torch.bfloat16, device=DEV)
+    p = torch.empty((n, 0), dtype=torch.uint8, device=DEV)
+    s = torch.empty((n, 0), dtype=torch.float16, device=DEV)
+    q2.q2_linear_ex(x, p, s, y=y, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    assert torch.equal(q2.q2_linear_ex(x, p, s), torch.zeros_like(y0))
+
+
+# ---------------------------------------------------------------------------
+# the fused output projection as two products over input slices, summed
+# ---------------------------------------------------------------------------
+
+def _split(m, n, k1, k2, r, cols=None):
+    k = k1 + k2
+    p, s, p_ref, s_ref = q2_weights(46, n, k)
+    xb, _ = acts(46, m, k)
+    x1 = dev_bits(np.ascontiguousarray(xb[:, :k1]), torch.bfloat16)
+    x2 = dev_bits(np.ascontiguousarray(xb[:, k1:]), torch.bfloat16)
+    p1, s1 = q2.q2_slice(p, s, 0, n, 0, k1)
+    p2, s2 = q2.q2_slice(p, s, 0, n, k1, k)
+    A1 = A2 = B = None
+    if r:
+        a, b = I.lowrank_factors(46, r, k, n, std=0.02)
+        A1 = dev_bits(np.ascontiguousarray(a[:, :k1]), torch.float16)
+        A2 = dev_bits(np.ascontiguousarray(a[:, k1:]), torch.float16)
+        B = dev_bits(b, torch.float16)
+    y = q2.q2_linear_ex(x1, p1, s1, A=A1, B=B)
+    q2.q2_linear_ex(x2, p2, s2, y=y, A=A2, B=B, accumulate=True)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    if cols is None:
+        ref = O.q2_linear_lowrank(xb, p_ref, s_ref, a, b) if r else O.q2_linear(xb, p_ref, s_ref)
+    else:
+        ref = O.q2_linear_cols(xb, p_ref, s_ref, cols)
+        if r:
+            ref = ref + O.lowrank_t(xb, a) @ O.f16_to_f64(b[cols]).T
+        y = y[:, cols]
+    assert_close(y, ref, f"split M={m} N={n} K={k1}+{k2} r={r}")
+
+
+@pytest.mark.parametrize("m", [1, 5, 75, 200])
+@pytest.mark.parametrize("r", [0, 32])
+def test_split_projection(m, r):
+    _split(m, 333, 256, 384, r)
+
+
+@pytest.mark.parametrize("r", [0, 32])
+def test_split_projection_full_size(r):
+    # single-block output projection: attention output (3072) and MLP output (12288) side by side
+    _split(1536, 3072, 3072, 12288, r, cols=sample_cols(3072, 128, seed=7))
