@@ -166,30 +166,54 @@ def measure_split_projection(torch, q2, I, dev, reps=20):
     def whole():
         q2.q2_linear(x, p, s, y=y)
 
-    res = {}
-    for name, fn in (("split", split), ("whole", whole)):
-        fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(reps):
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        best = float("inf")
-        for _ in range(3):                  # best of three replays: the clocks settle after the layer list
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            best = min(best, e0.elapsed_time(e1) * 1e-3 / reps)
-        res[name] = best
-        del g
+    res = {name: _best_graph_time(torch, fn, reps) for name, fn in (("split", split), ("whole", whole))}
     flops = 2.0 * m * n * k
     return {"shape": f"M={m} K={k1}+{k2} N={n}", "us_split": round(res["split"] * 1e6, 3),
             "us_whole": round(res["whole"] * 1e6, 3), "tflops_split": round(flops / res["split"] / 1e12, 3),
             "frac_split": round(flops / res["split"] / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def _best_graph_time(torch, fn, reps):
+    """Seconds per call: fn captured reps times in one graph, best of three replays after a warm one."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3 / reps)
+    del g
+    return best
+
+
+def measure_quarter_step(torch, q2, I, dev, reps=20):
+    """The Q2_0 GEMMs of the quarter-size first step (256 image patches, 128
+    text rows): every GEMM shape at M = 384 (single blocks), 256 and 128 (the
+    image and text streams of joint blocks), in the automatic launch
+    configuration.  Reported beside the step, not part of it."""
+    out, tot_t, tot_f = {}, 0.0, 0.0
+    for k, n in I.GEMM_SHAPES:
+        p, s = q2.q2_pack(torch.from_numpy(I.q2_codes_fast(960, n, k)).to(dev),
+                          torch.from_numpy(I.q2_scales(960, n, k)).to(dev))
+        for m in I.QUARTER_M:
+            x = torch.from_numpy(I.activations_bf16(960 + m, m, k).view(np.int16)).to(dev).view(torch.bfloat16)
+            y = torch.empty((m, n), device=dev)
+            t = _best_graph_time(torch, lambda: q2.q2_linear(x, p, s, y=y), reps)
+            f = 2.0 * m * n * k
+            out[f"M={m} K={k} N={n}"] = {"us": round(t * 1e6, 3), "tflops": round(f / t / 1e12, 3)}
+            tot_t += t
+            tot_f += f
+    return {"tflops": round(tot_f / tot_t / 1e12, 3), "frac": round(tot_f / tot_t / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "calls": out}
 
 
 def main():
@@ -203,6 +227,7 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
                     "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref")
     ap.add_argument("--no-split", action="store_true", help="skip the split output projection measurement")
+    ap.add_argument("--no-quarter", action="store_true", help="skip the quarter-size first step measurement")
     ap.add_argument("--no-layer-list", action="store_true",
                     help="skip the 100-linear rank-32 layer list report")
     args = ap.parse_args()
@@ -348,6 +373,7 @@ def main():
 
     layer_list = None if (args.no_layer_list or args.only) else measure_layer_list(torch, q2, I, dev)
     split_proj = None if (args.no_split or args.only) else measure_split_projection(torch, q2, I, dev)
+    quarter = None if (args.no_quarter or args.only) else measure_quarter_step(torch, q2, I, dev)
 
     parts = {}
     fam_time, fam_flops, fam_bytes = {}, {}, {}
@@ -400,6 +426,8 @@ def main():
         out["layer_list"] = layer_list
     if split_proj is not None:
         out["split_projection"] = split_proj
+    if quarter is not None:
+        out["quarter_step"] = quarter
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

@@ -98,6 +98,16 @@ int forced_cfg() {
   return q2dev::gemm_config_id(v);
 }
 
+// Test-only override of the K split: Q2_GEMM_KSPLIT=1|2 (0 = automatic, -1
+// for anything else).
+int forced_ksplit() {
+  const char* v = std::getenv("Q2_GEMM_KSPLIT");
+  if (v == nullptr || *v == 0) return 0;
+  if (std::strcmp(v, "1") == 0) return 1;
+  if (std::strcmp(v, "2") == 0) return 2;
+  return -1;
+}
+
 int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* s, const uint16_t* z, float* y,
                   int64_t M, int64_t N, int64_t K, const uint16_t* lr_t, const uint16_t* lr_b, int64_t r,
                   bool accumulate, hipStream_t stream) {
@@ -110,7 +120,10 @@ int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* 
   if (path == 1 && M > 16) path = 0;
   const int cfg = forced_cfg();
   if (cfg < 0) return fail(Q2_ERR_ARG, "unknown Q2_GEMM_TILE configuration");
-  return hip_status(q2dev::launch_linear(a, fmt, path, cfg, stream), fmt == 0 ? "q2 linear launch" : "q4 linear launch");
+  const int ks = forced_ksplit();
+  if (ks < 0) return fail(Q2_ERR_ARG, "Q2_GEMM_KSPLIT must be 1 or 2");
+  return hip_status(q2dev::launch_linear(a, fmt, path, cfg, ks, stream),
+                    fmt == 0 ? "q2 linear launch" : "q4 linear launch");
 }
 
 // The Q2_0 linear entry points: y = x W^T (+ (x A^T) B^T when r > 0), written

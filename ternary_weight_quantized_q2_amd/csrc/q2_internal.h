@@ -23,8 +23,11 @@ struct LinearArgs {
 
 // Path selection for tests: force_path 0 = automatic, 1 = force GEMV, 2 = force
 // GEMM; force_cfg 0 = automatic GEMM configuration, else the number that
-// gemm_config_id gives for a configuration name (-1 for an unknown name).
-hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, int force_cfg, hipStream_t stream);
+// gemm_config_id gives for a configuration name (-1 for an unknown name);
+// force_ksplit 0 = automatic, 1 = whole K, 2 = K in two parts (K-group
+// configurations without accumulation only).
+hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, int force_cfg, int force_ksplit,
+                         hipStream_t stream);
 int gemm_config_id(const char* name);
 hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* t_limbs,
                             int64_t M, int64_t K, int r, hipStream_t stream);

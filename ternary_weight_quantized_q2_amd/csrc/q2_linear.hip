@@ -1094,7 +1094,7 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles) {
 // sums once its own copies have landed; one barrier per set publishes them.
 // Rows past M are clamped on the copy side and dropped at the store.
 template <int FMT, int MT, int NT, int KG, int NSET>
-__global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int tiles_m, int group_m) {
+__global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int tiles_m, int group_m, int kpart) {
   constexpr int W = 4 * KG;                                   // waves
   constexpr int BM = 16 * MT, BN = 64 * NT;
   constexpr int DW = WFmt<FMT>::LANE_DW;
@@ -1129,7 +1129,13 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   const int wn = wv & 3, kg = wv >> 2;
   const int c = lane & 15, g = lane >> 4;
   const int tiles_n = (int)((a.N + BN - 1) / BN);
-  const int tile = xcd_tile((int)blockIdx.x, tiles_m * tiles_n);
+  // With kpart > 0 the K blocks are split in two parts of kpart blocks: the
+  // two workgroups of a tile take one part each (adjacent numbers, so one XCD)
+  // and add their results into y, which the launcher has zeroed.
+  const int nparts = kpart > 0 ? 2 : 1;
+  int tile = xcd_tile((int)blockIdx.x, tiles_m * tiles_n * nparts);
+  const int part = tile & (nparts - 1);
+  tile = tile >> (nparts - 1);
   const int grp = tile / (group_m * tiles_n), gi = tile - grp * group_m * tiles_n;
   const int gm = min(group_m, tiles_m - grp * group_m);          // row tiles in this group
   const int tm = grp * group_m + gi % gm, tn = gi / gm;
@@ -1137,8 +1143,10 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   const int64_t nw = n0 + wn * (BN / 4);
   const int64_t M = a.M, N = a.N, K = a.K, KB = K / BLOCK_K;
   // Block and set indices in 32 bits (K <= 2^24): uniform 64-bit compares would run on the vector ALU.
-  const int kb = (int)KB;
-  const int NS = (kb + KG - 1) / KG;                          // sets
+  // This workgroup takes blocks kb0 .. kb - 1.
+  const int kb0 = part * kpart;
+  const int kb = kpart > 0 ? min((int)KB, kb0 + kpart) : (int)KB;
+  const int NS = kb > kb0 ? (kb - kb0 + KG - 1) / KG : 0;    // sets
   const int64_t row_bytes = (FMT == 0) ? K / 4 : K / 2;
   const NatConsts kc = (FMT == 0) ? q2_nat_consts() : q4_nat_consts();
 
@@ -1232,7 +1240,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   // 0 .. XUM-1 the activation copies of this wave's tasks, then the codes, the
   // scale words [and zero words].  Blocks past the end re-copy the last one.
   auto issue_unit = [&](int unit, int set, int slot) {
-    const int b0 = KG * set;
+    const int b0 = kb0 + KG * set;
     if (unit < XUM) {
       const int k2 = unit >> 2, kk = unit & 3;
       if (k2 < xtasks) {
@@ -1288,7 +1296,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
       if (k2 < xtasks) {
         const int task = wv + W * k2;
         const int q = task / MT, it = task - q * MT;
-        if (KG * set + q < kb) {
+        if (kb0 + KG * set + q < kb) {
           const uint8_t* st = smem + (slot * KG + q) * XSTAGE;
           q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1393,7 +1401,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   // copies are the last ones waited for (vmcnt(0) at its top barrier); with
   // NSET = 3 each wave has waited for all of set s's copies at the end of set
   // s - 1, leaving only the copies of set s + 1 in flight.
-  if (KB > 0) {
+  if (NS > 0) {
     issue_set(0, 0);
     if constexpr (NSET == 3) {
       if (NS > 1) issue_set(1, 1);
@@ -1408,7 +1416,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
       else stage_barrier<0>();
       const int cset = (s + NSET - 1 < NS) ? s + NSET - 1 : -1;       // the set copied during this one
       const int cslot = (slot + NSET - 1 >= NSET) ? slot - 1 : slot + NSET - 1;   // (s + NSET - 1) % NSET
-      const int bp = KG * s + kg;
+      const int bp = kb0 + KG * s + kg;
       if (bp < kb) {
         q2_u32x4 bf[NT][4];
         float dc[NT], zc[NT];
@@ -1433,8 +1441,11 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   __syncthreads();                        // and every wave is done reading the stages
 
   // Under accumulation the old y values of the row-major stores are loaded
-  // now, while the tile is reduced.
-  const bool rows16 = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
+  // now, while the tile is reduced.  A split tile adds its part into y with
+  // one atomic add per element, in the matrix-core layout (16 consecutive
+  // columns of a row per instruction and row group).
+  const bool split = kpart > 0;
+  const bool rows16 = !split && (N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
   constexpr int RP = (BM * (BN / 4) + 64 * W - 1) / (64 * W);
   q2_f32x4 yo4[RP];
   if (a.acc && rows16) {
@@ -1524,7 +1535,10 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
           v *= fin;
           if (a.acc) v += yo[i][j][e];
           const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (m < M && n < N) __builtin_nontemporal_store(v, &a.y[m * N + n]);
+          if (m < M && n < N) {
+            if (split) unsafeAtomicAdd(&a.y[m * N + n], v);
+            else __builtin_nontemporal_store(v, &a.y[m * N + n]);
+          }
         }
       }
     }
@@ -1889,10 +1903,10 @@ static hipError_t run_gemm_kpair(const LinearArgs& a, hipStream_t stream) {
 // rounds and its rows of x exceed ~2.5 MB, every round reads them again.  p is
 // the power of two (at most the row-tile count) with the least modelled sum.
 template <int FMT>
-static int kgroup_group_rows(const LinearArgs& a, int bm, int tiles_m, int tiles_n) {
+static int kgroup_group_rows(const LinearArgs& a, int bm, int tiles_m, int tiles_n, int nparts) {
   const double xrow = 2.0 * (double)std::min<int64_t>(bm, a.M) * (double)a.K;   // one row tile of x
   const double wb = (double)a.N * (double)a.K * (FMT == 0 ? 0.265625 : 0.53125);
-  const double rounds = std::max(1.0, std::ceil((double)tiles_m * tiles_n / 8.0 / 32.0));
+  const double rounds = std::max(1.0, std::ceil((double)tiles_m * tiles_n * nparts / 8.0 / 32.0));
   auto cost = [&](int p) {
     const int group = (tiles_m + p - 1) / p;
     const double xpart = group * xrow;
@@ -1904,14 +1918,37 @@ static int kgroup_group_rows(const LinearArgs& a, int bm, int tiles_m, int tiles
   return (tiles_m + best - 1) / best;
 }
 
+// y = 0 before a K-split GEMM adds its two parts into it.
+__global__ __launch_bounds__(256) void zero_y_kernel(float* y, int64_t count) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0.0f;
+}
+
+// ksplit 2: the K blocks in two parts, each tile's two workgroups adding
+// into y (zeroed first).  Two fp32 additions onto zero give the same result in
+// either order, so a split call is still run-to-run deterministic; it cannot
+// accumulate onto an existing y for the same reason.
 template <int FMT, int MT, int NT, int KG, int NSET>
-static hipError_t run_gemm_kgroup(const LinearArgs& a, hipStream_t stream) {
+static hipError_t run_gemm_kgroup(const LinearArgs& a, int ksplit, hipStream_t stream) {
   constexpr int BM = 16 * MT, BN = 64 * NT;
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t tiles = tiles_m * ((a.N + BN - 1) / BN);
-  if (tiles > 0x7fffffff || a.r > 0) return hipErrorInvalidValue;   // no low-rank epilogue here
-  hipLaunchKernelGGL((gemm_kgroup_kernel<FMT, MT, NT, KG, NSET>), dim3((unsigned)tiles), dim3(256 * KG), 0, stream,
-                     a, (int)tiles_m, kgroup_group_rows<FMT>(a, BM, (int)tiles_m, (int)((a.N + BN - 1) / BN)));
+  const int64_t KB = a.K / BLOCK_K;
+  if (a.r > 0 || (ksplit == 2 && a.acc) || (ksplit != 1 && ksplit != 2)) return hipErrorInvalidValue;
+  const int kpart = (ksplit == 2) ? (int)((KB + 1) / 2) : 0;
+  const int64_t grid = tiles * (kpart > 0 ? 2 : 1);
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (kpart > 0) {
+    const int64_t count = a.M * a.N;
+    const int64_t blocks = std::min<int64_t>((count + 255) / 256, 4096);
+    hipLaunchKernelGGL(zero_y_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.y, count);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gemm_kgroup_kernel<FMT, MT, NT, KG, NSET>), dim3((unsigned)grid), dim3(256 * KG), 0, stream,
+                     a, (int)tiles_m,
+                     kgroup_group_rows<FMT>(a, BM, (int)tiles_m, (int)((a.N + BN - 1) / BN), kpart > 0 ? 2 : 1),
+                     kpart);
   return hipGetLastError();
 }
 
@@ -1932,7 +1969,8 @@ int gemm_config_id(const char* name) {
 }
 
 template <int FMT>
-static hipError_t run_gemm_cfg(const LinearArgs& a, int cfg, hipStream_t stream) {
+static hipError_t run_gemm_cfg(const LinearArgs& a, int cfg, int ksplit, hipStream_t stream) {
+  if (cfg < CFG_KG2x1x4 && ksplit != 1) return hipErrorInvalidValue;   // only K-group tiles split K
   const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
   switch (cfg) {
     case CFG_KPAIR:   // whole 96-row tiles; the branch only in its LDS-staged form
@@ -1943,16 +1981,21 @@ static hipError_t run_gemm_cfg(const LinearArgs& a, int cfg, hipStream_t stream)
     case CFG_W64x128: return run_gemm<FMT, 64, 128>(a, stream);
     case CFG_W32x128: return run_gemm<FMT, 32, 128>(a, stream);
     case CFG_W32x64: return run_gemm<FMT, 32, 64>(a, stream);
-    case CFG_KG2x1x4: return run_gemm_kgroup<FMT, 2, 1, 4, 2>(a, stream);
-    case CFG_KG4x2x2: return run_gemm_kgroup<FMT, 4, 2, 2, 2>(a, stream);
-    case CFG_KG2x1x2: return run_gemm_kgroup<FMT, 2, 1, 2, 2>(a, stream);
-    case CFG_KG2x2x4: return run_gemm_kgroup<FMT, 2, 2, 4, 2>(a, stream);
-    case CFG_KG2x2x2: return run_gemm_kgroup<FMT, 2, 2, 2, 2>(a, stream);
-    case CFG_KG2x1x4R3: return run_gemm_kgroup<FMT, 2, 1, 4, 3>(a, stream);
-    case CFG_KG6x3x2: return run_gemm_kgroup<FMT, 6, 3, 2, 2>(a, stream);
+    case CFG_KG2x1x4: return run_gemm_kgroup<FMT, 2, 1, 4, 2>(a, ksplit, stream);
+    case CFG_KG4x2x2: return run_gemm_kgroup<FMT, 4, 2, 2, 2>(a, ksplit, stream);
+    case CFG_KG2x1x2: return run_gemm_kgroup<FMT, 2, 1, 2, 2>(a, ksplit, stream);
+    case CFG_KG2x2x4: return run_gemm_kgroup<FMT, 2, 2, 4, 2>(a, ksplit, stream);
+    case CFG_KG2x2x2: return run_gemm_kgroup<FMT, 2, 2, 2, 2>(a, ksplit, stream);
+    case CFG_KG2x1x4R3: return run_gemm_kgroup<FMT, 2, 1, 4, 3>(a, ksplit, stream);
+    case CFG_KG6x3x2: return run_gemm_kgroup<FMT, 6, 3, 2, 2>(a, ksplit, stream);
     default: return hipErrorInvalidValue;
   }
 }
+
+// A GEMM launch: kernel configuration and K parts (1 or 2).
+struct GemmChoice {
+  int cfg, ksplit;
+};
 
 template <int FMT>
 static int gemm_auto_cfg(const LinearArgs& a) {
@@ -1968,7 +2011,7 @@ static int gemm_auto_cfg(const LinearArgs& a) {
     if (a.M <= 64) return tiles(32, 128) >= 128 ? CFG_KG2x2x4 : narrow;
     if (a.M <= 128) return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : narrow;
     if (a.M <= 256) return tiles(32, 128) >= 400 ? (FMT == 0 ? CFG_KG2x2x2 : CFG_KG2x1x2) : CFG_KG2x2x4;
-    if (a.M % 96 == 0 && tiles(96, 192) >= 128) return CFG_KPAIR;
+    if (tiles(96, 192) >= 128) return CFG_KG6x3x2;     // 10 % ahead of the K-pair kernel at 384 rows
     return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : CFG_KG2x2x4;
   }
   if (a.r == 0) {
@@ -1996,15 +2039,39 @@ static int gemm_auto_cfg(const LinearArgs& a) {
   return CFG_W32x64;
 }
 
-hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, int force_cfg, hipStream_t stream) {
+// Long K over few tiles (K >= 8192, without the branch or accumulation): the
+// K blocks in two parts, so twice the workgroups share the chip.  Measured at
+// K = 9728 / 12288, N = 2560 / 3072: 20-27 % off at M <= 64, 7-8 % at
+// M = 128, 11-14 % for Q2_0 at 384 and 512 rows; at 256 rows, and for the
+// 4-bit format beyond 128 rows, no configuration gained enough to switch.
+template <int FMT>
+static GemmChoice gemm_auto_choice(const LinearArgs& a) {
+  auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  if (a.r == 0 && !a.acc && a.K / BLOCK_K >= 64) {
+    if (a.M <= 64 && tiles(32, 64) < 256) return {FMT == 0 ? CFG_KG2x1x4R3 : CFG_KG2x1x4, 2};
+    if (a.M <= 128 && tiles(32, 128) < 256) return {CFG_KG2x2x4, 2};
+    if (FMT == 0 && a.M > 256 && a.M <= 640 && tiles(96, 192) < 128) return {CFG_KG6x3x2, 2};
+  }
+  return {gemm_auto_cfg<FMT>(a), 1};
+}
+
+template <int FMT>
+static hipError_t run_gemm_auto(const LinearArgs& a, int force_cfg, int force_ksplit, hipStream_t stream) {
+  GemmChoice ch = force_cfg > 0 ? GemmChoice{force_cfg, 1} : gemm_auto_choice<FMT>(a);
+  if (force_ksplit > 0) ch.ksplit = force_ksplit;
+  return run_gemm_cfg<FMT>(a, ch.cfg, ch.ksplit, stream);
+}
+
+hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, int force_cfg, int force_ksplit,
+                         hipStream_t stream) {
   const bool gemv = force_path == 1 || (force_path == 0 && a.M <= 16);
   if (gemv && a.M > 16) return hipErrorInvalidValue;
-  if (fmt == 0) {
-    if (gemv) return run_gemv<0>(a, stream);
-    return run_gemm_cfg<0>(a, force_cfg > 0 ? force_cfg : gemm_auto_cfg<0>(a), stream);
+  if (gemv) {
+    if (force_ksplit > 1) return hipErrorInvalidValue;
+    return fmt == 0 ? run_gemv<0>(a, stream) : run_gemv<1>(a, stream);
   }
-  if (gemv) return run_gemv<1>(a, stream);
-  return run_gemm_cfg<1>(a, force_cfg > 0 ? force_cfg : gemm_auto_cfg<1>(a), stream);
+  return fmt == 0 ? run_gemm_auto<0>(a, force_cfg, force_ksplit, stream)
+                  : run_gemm_auto<1>(a, force_cfg, force_ksplit, stream);
 }
 
 hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* tl, int64_t M, int64_t K, int r,

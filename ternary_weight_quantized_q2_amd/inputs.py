@@ -102,5 +102,9 @@ GEMV_SHAPES = [(3072, 3072), (3072, 9216), (3072, 12288), (12288, 3072)]   # (K,
 GEMM_M = 1536                                                              # 1024 image + 512 text tokens
 GEMM_SHAPES = [(3072, 3072), (3072, 9216), (3072, 12288), (12288, 3072)]   # (K, N)
 LOWRANK = dict(M=1536, K=3072, N=9216, ranks=(4, 32, 64), linears=100, steps=4)
+# The quarter-size first step of the two-step schedule: 256 image patches and
+# 128 text rows; joint blocks run the two streams through their own weights
+# (M = 256 and M = 128), single blocks run them together (M = 384).
+QUARTER_M = (384, 256, 128)
 Q4_M = 128
 Q4_SHAPES = [(2560, 9728), (9728, 2560), (2560, 2560)]                     # (K, N)

@@ -245,6 +245,70 @@ def test_forced_gemm_config_errors(monkeypatch):
     assert e.value.status == q2.Q2_ERR_HIP
 
 
+KG_CFGS = [c for c in GEMM_CFGS if c.startswith("kg")]
+
+
+@pytest.mark.parametrize("cfg", KG_CFGS)
+@pytest.mark.parametrize("m,n,k", CFG_SHAPES + [(384, 3072, 12288)])
+def test_forced_k_split(cfg, m, n, k, monkeypatch):
+    # K in two parts added into a zeroed y; a single block (K = 128) leaves the second part empty
+    (x, p, s, ref), (x4, P, S, Z, ref4) = _cfg_case(m, n, k) if k <= 4096 else _k_split_big_case(m, n, k)
+    monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+    monkeypatch.setenv("Q2_GEMM_KSPLIT", "2")
+    y = torch.full((m, n), float("nan"), device=DEV)
+    q2.q2_linear(x, p, s, y)
+    y_again = q2.q2_linear(x, p, s)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_again), "a split call must be run-to-run deterministic"
+    yh = y.cpu().numpy()
+    if isinstance(ref, tuple):              # sampled columns of a full-size shape
+        cols, ref_cols = ref
+        assert_close(yh[:, cols], ref_cols, f"{cfg} split M={m} N={n} K={k} sampled")
+    else:
+        assert_close(yh, ref, f"{cfg} split M={m} N={n} K={k}")
+    if P is not None:
+        y4 = torch.full((m, n), float("nan"), device=DEV)
+        q2.q4_linear(x4, P, S, Z, y4)
+        torch.cuda.synchronize()
+        assert_close(y4.cpu().numpy(), ref4, f"q4 {cfg} split M={m} N={n} K={k}")
+
+
+_big = {}
+
+
+def _k_split_big_case(m, n, k):
+    if (m, n, k) not in _big:
+        p_dev, s_dev, p_ref, s_ref = q2_weights(23, n, k)
+        xb, x = acts(23, m, k)
+        cols = sample_cols(n, 96, seed=3)
+        _big[(m, n, k)] = ((x, p_dev, s_dev, (cols, O.q2_linear_cols(xb, p_ref, s_ref, cols))),
+                           (None, None, None, None, None))
+    return _big[(m, n, k)]
+
+
+def test_forced_k_split_errors(monkeypatch):
+    (x, p, s, _), _ = _cfg_case(75, 200, 1408)
+    monkeypatch.setenv("Q2_GEMM_KSPLIT", "3")
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_linear(x, p, s)
+    assert e.value.status == q2.Q2_ERR_ARG
+    monkeypatch.setenv("Q2_GEMM_KSPLIT", "2")
+    monkeypatch.setenv("Q2_GEMM_TILE", "w32x128")       # only K-group tiles split K
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_linear(x, p, s)
+    assert e.value.status == q2.Q2_ERR_HIP
+    monkeypatch.setenv("Q2_GEMM_TILE", "kg2x2x2")       # an accumulating call cannot split
+    y = torch.zeros((75, 200), device=DEV)
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_linear_ex(x, p, s, y=y, accumulate=True)
+    assert e.value.status == q2.Q2_ERR_HIP
+    monkeypatch.setenv("Q2_FORCE_PATH", "gemv")          # nor does the GEMV
+    xs = x[:8].contiguous()
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_linear(xs, p, s)
+    assert e.value.status == q2.Q2_ERR_HIP
+
+
 def _offset_f16(t):
     """The same values in a buffer whose first element sits 2 bytes past a 4-byte boundary."""
     flat = torch.empty(t.numel() + 1, dtype=torch.float16, device=t.device)
@@ -300,6 +364,17 @@ def test_gemm_full_shapes(k, n):
         assert_close(y, O.q2_linear(xb, p_ref, s_ref), "gemm full")
     cols = sample_cols(n)
     assert_close(y[:, cols], O.q2_linear_cols(xb, p_ref, s_ref, cols), f"gemm K={k} N={n} sampled")
+
+
+@pytest.mark.parametrize("m", I.QUARTER_M)
+@pytest.mark.parametrize("k,n", I.GEMM_SHAPES)
+def test_quarter_step_shapes(m, k, n):
+    # the rows of the quarter-size first step, in the launch configuration the automatic choice gives them
+    p_dev, s_dev, p_ref, s_ref = q2_weights(31, n, k)
+    xb, x = acts(31, m, k)
+    y = q2.q2_linear(x, p_dev, s_dev).cpu().numpy()
+    cols = sample_cols(n, seed=m)
+    assert_close(y[:, cols], O.q2_linear_cols(xb, p_ref, s_ref, cols), f"M={m} K={k} N={n} sampled")
 
 
 def test_determinism_and_guards():
