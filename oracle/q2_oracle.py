@@ -217,6 +217,86 @@ def q2_linear_sum(parts, y0=None) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Import of a transposed, group-quantised ternary weight (gemlite-int2 style)
+# ---------------------------------------------------------------------------
+# "We're Teaching Your Browser to Paint", section "The lucky break that wasn't
+# luck": the source stores codes {0,1,2} four per byte, least significant pair
+# first, along the input axis; it dequantises with a per-group scale and zero
+# point, and every zero equals minus its scale, so each weight is (q - 1) x
+# scale -- the Q2_0 formula.  Conversion is a transpose and a regroup with no
+# numeric change; the one rounding, the f32 -> f16 scale cast, must be exact or
+# the conversion stops.  Readings (the pages give no more of the layout): the
+# source is input-major -- bytes [K/4, N], byte j of column n holding codes
+# 4j..4j+3 of weight row n -- with f32 scales and zeros [K/G, N]; the zero is
+# a bias in weight units, w = q x scale + zero (with zero == -scale this is
+# (q - 1) x scale); the group length G divides 128 or is a multiple of it,
+# and a 128-weight block whose groups disagree has no Q2_0 form.
+
+class ImportError_(ValueError):
+    """Raised by import_gemlite.  kind is 'code', 'zero' or 'scale'; index is
+    the flat row-major index of the first offending code in the weight [N, K]
+    ('code'), or of the first offending group in the source's [K/G, N] arrays."""
+
+    def __init__(self, kind: str, index: int):
+        super().__init__(f"import: bad {kind} at flat index {index}")
+        self.kind = kind
+        self.index = index
+
+
+def gemlite_dequant(codes_t: np.ndarray, scales_t: np.ndarray, zeros_t: np.ndarray, group: int) -> np.ndarray:
+    """The source's own dequantisation, w[n, k] = q[n, k] x s[k // G, n] + z[k // G, n],
+    in float64 [N, K] (exact: q is 0, 1 or 2 and s, z are f32 values)."""
+    ct = np.asarray(codes_t, dtype=np.uint8)
+    kq, n = ct.shape
+    k = np.arange(kq * 4)
+    q = ((ct[k // 4, :] >> (2 * (k % 4))[:, None].astype(np.uint8)) & 3).T.astype(np.float64)   # [N, K]
+    s = np.asarray(scales_t, dtype=np.float32).astype(np.float64)[k // group, :].T
+    z = np.asarray(zeros_t, dtype=np.float32).astype(np.float64)[k // group, :].T
+    return q * s + z
+
+
+def import_gemlite(codes_t: np.ndarray, scales_t: np.ndarray, zeros_t: np.ndarray, group: int):
+    """Source (bytes [K/4, N], scales / zeros f32 [K/G, N]) -> Q2_0 (packed u8
+    [N, K/4], scale bits u16 [N, K/128]).  Checks, in this order, each
+    reporting its first flat index: codes <= 2; zero == -scale; the scale is a
+    finite exact f16 value; within a 128-weight block every group has the same
+    scale."""
+    ct = np.ascontiguousarray(codes_t, dtype=np.uint8)
+    st = np.ascontiguousarray(scales_t, dtype=np.float32)
+    zt = np.ascontiguousarray(zeros_t, dtype=np.float32)
+    kq, n = ct.shape
+    k = 4 * kq
+    if k % GROUP or group <= 0 or group % 4 or (GROUP % group and group % GROUP) or k % group:
+        raise ValueError("import: K must be a multiple of 128 and of G; G must divide 128 or be a multiple of it")
+    if st.shape != (k // group, n) or zt.shape != st.shape:
+        raise ValueError("import: scales and zeros must be [K/G, N]")
+    col = np.arange(k)
+    codes = ((ct[col // 4, :] >> (2 * (col % 4))[:, None].astype(np.uint8)) & 3).T      # [N, K]
+    bad = np.flatnonzero(codes > 2)
+    if bad.size:
+        raise ImportError_("code", int(bad[0]))
+    bad = np.flatnonzero(~(zt == -st))
+    if bad.size:
+        raise ImportError_("zero", int(bad[0]))
+    half = st.astype(np.float16)
+    bad = np.flatnonzero(~(np.isfinite(st) & (half.astype(np.float32) == st)))
+    if bad.size:
+        raise ImportError_("scale", int(bad[0]))
+    nb = k // GROUP
+    if group < GROUP:                          # every group of a block must carry the block's scale
+        per = GROUP // group
+        first = st.reshape(nb, per, n)[:, :1, :]
+        same = (st.reshape(nb, per, n) == first).reshape(k // group, n)
+        bad = np.flatnonzero(~same)
+        if bad.size:
+            raise ImportError_("scale", int(bad[0]))
+        block_s = st[::per, :]                  # [K/128, N]
+    else:
+        block_s = st[np.arange(nb) * GROUP // group, :]
+    return pack_codes_q2(codes), np.ascontiguousarray(block_s.T.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
 # Low-rank side branch  y = W x + B (A x)
 # ---------------------------------------------------------------------------
 

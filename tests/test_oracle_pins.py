@@ -282,6 +282,73 @@ def test_split_sum_pins():
     check_split_sum(O.q2_linear_sum)
 
 
+def import_source(seed, n, k, group):
+    """A valid source weight: input-major code bytes [K/4, N] of codes in
+    {0,1,2}, and per-group f32 scales (f16-exact, equal across the groups of a
+    128-weight block when G < 128) with zeros = -scales."""
+    rng = np.random.default_rng(seed)
+    codes = rng.choice(3, size=(n, k), p=[0.3, 0.4, 0.3]).astype(np.uint8)
+    c = codes.reshape(n, k // 4, 4).astype(np.uint32)
+    packed = (c[..., 0] | c[..., 1] << 2 | c[..., 2] << 4 | c[..., 3] << 6).astype(np.uint8)
+    blocks = np.abs(rng.standard_normal((k // 128, n))).astype(np.float16).astype(np.float32) * np.float32(0.02)
+    blocks = blocks.astype(np.float16).astype(np.float32)
+    scales = np.repeat(blocks, 128 // group, axis=0) if group < 128 else blocks[::group // 128]
+    if group > 128:                                    # a group spans several blocks: one scale for all
+        scales = np.ascontiguousarray(scales)
+    return codes, np.ascontiguousarray(packed.T), np.ascontiguousarray(scales), np.ascontiguousarray(-scales)
+
+
+def _expect_import_error(call, kind, index):
+    try:
+        call()
+    except O.ImportError_ as e:
+        assert (e.kind, e.index) == (kind, index), (e.kind, e.index)
+        return
+    raise AssertionError(f"conversion did not stop on the bad {kind}")
+
+
+def check_import(import_fn):
+    g = golden("import_transpose.json")
+    k, n = g["K"], g["N"]
+    ct = np.full((k // 4, n), g["source_rest"], np.uint8)
+    ct[:len(g["source_col0_head"]), 0] = g["source_col0_head"]
+    ct[:len(g["source_col1_head"]), 1] = g["source_col1_head"]
+    st = np.array([g["scales"]], np.float32)
+    zt = np.array([g["zeros"]], np.float32)
+    p, s = import_fn(ct, st, zt, g["G"])
+    assert list(p[0, :2]) == g["packed_row0_head"] and list(p[1, :3]) == g["packed_row1_head"]
+    assert list(s[:, 0]) == g["scale_f16_bits"]
+    w = O.unpack_q2(p, s)
+    assert list(w[0, :8]) == g["w_row0_head"] and list(w[1, :8]) == g["w_row1_head"]
+    # no numeric change: the Q2_0 weight equals the source's own dequantisation, element by element
+    for group in (32, 64, 128, 256):
+        n2, k2 = 37, 512
+        codes, ct2, st2, zt2 = import_source(group, n2, k2, group)
+        p2, s2 = import_fn(ct2, st2, zt2, group)
+        assert np.array_equal(O.codes_q2(p2), codes), group
+        assert np.array_equal(O.unpack_q2(p2, s2), O.gemlite_dequant(ct2, st2, zt2, group)), group
+    # the conversion stops, naming the first offending element, in the order codes, zeros, scales
+    codes, ct2, st2, zt2 = import_source(7, 6, 256, 64)
+    bad = ct2.copy()
+    bad[5, 3] |= 0x30                                   # weight row 3, k = 4 * 5 + 2 becomes code 3
+    _expect_import_error(lambda: import_fn(bad, st2, zt2, 64), "code", 3 * 256 + 22)
+    z = zt2.copy()
+    z[2, 4] = -z[2, 4]                                  # zero == +scale
+    _expect_import_error(lambda: import_fn(ct2, st2, z, 64), "zero", 2 * 6 + 4)
+    sc = st2.copy()
+    sc[1, 1] = np.float32(0.1)                          # not an f16 value (zero kept equal to -scale)
+    _expect_import_error(lambda: import_fn(ct2, sc, -sc, 64), "scale", 1 * 6 + 1)
+    sc2 = st2.copy()
+    sc2[3, 5] = sc2[3, 5] * 2                            # second group of block 1 disagrees with the first
+    _expect_import_error(lambda: import_fn(ct2, sc2, -sc2, 64), "scale", 3 * 6 + 5)
+
+
+def test_import_pins():
+    check_import(O.import_gemlite)
+    with pytest.raises(ValueError):
+        O.import_gemlite(np.zeros((32, 2), np.uint8), np.zeros((3, 2), np.float32), np.zeros((3, 2), np.float32), 48)
+
+
 # ---------------------------------------------------------------------------
 # pack: scale round trip and code check
 # ---------------------------------------------------------------------------

@@ -74,7 +74,29 @@ def slice_codes_at_byte_k0(packed, sc, n0, n1, k0, k1):           # byte offset 
     return np.ascontiguousarray(p[n0:n1, start:start + (k1 - k0) // 4]), ss
 
 
+def import_no_transpose(ct, st, zt, group):          # source bytes read as if already [N, K/4]
+    p, s = O.import_gemlite(ct, st, zt, group)
+    flat = np.ascontiguousarray(ct).reshape(-1)[:p.size]
+    return flat.reshape(p.shape).copy(), s
+
+
+def import_zero_plus_scale(ct, st, zt, group):      # accepts zero == +scale as well
+    zt = np.where(np.asarray(zt) == np.asarray(st), -np.asarray(st), zt)
+    return O.import_gemlite(ct, st, zt, group)
+
+
+def import_regroup_unchecked(ct, st, zt, group):    # takes each block's first group, never compares
+    if group < 128:
+        per = 128 // group
+        st = np.repeat(np.asarray(st)[::per], per, axis=0)
+        zt = -st
+    return O.import_gemlite(ct, st, zt, group)
+
+
 MUTANTS = {
+    "import without the transpose": lambda: P.check_import(import_no_transpose),
+    "import accepts zero == +scale": lambda: P.check_import(import_zero_plus_scale),
+    "import regroups without comparing": lambda: P.check_import(import_regroup_unchecked),
     "slice scales at the input column": lambda: P.check_slice(slice_scales_at_input_column),
     "slice codes at byte k0": lambda: P.check_slice(slice_codes_at_byte_k0),
     "split sum drops y0": lambda: P.check_split_sum(lambda parts, y0=None: O.q2_linear_sum(parts)),
@@ -108,3 +130,4 @@ def test_unmutated_checks_pass():
     P.check_q4(O.q4_linear)
     P.check_slice(O.slice_q2)
     P.check_split_sum(O.q2_linear_sum)
+    P.check_import(O.import_gemlite)
