@@ -60,7 +60,8 @@ typedef enum {
   Q2_ERR_SCALE = -5,     /* q2_pack: scale not exactly representable in f16, or NaN/inf */
   Q2_ERR_DEVICE = -6,    /* current device is not gfx950                            */
   Q2_ERR_HIP = -7,       /* HIP runtime or launch error                             */
-  Q2_ERR_WORKSPACE = -8  /* low-rank workspace too small                            */
+  Q2_ERR_WORKSPACE = -8, /* low-rank workspace too small                            */
+  Q2_ERR_FORMAT = -9     /* q2_import_gemlite: a zero point that is not -scale       */
 } q2_status;
 
 /*
@@ -81,6 +82,36 @@ typedef enum {
  */
 int q2_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K,
             uint8_t* packed, uint16_t* scales_f16, int64_t* bad_index, hipStream_t stream);
+
+/*
+ * q2_import_gemlite - load-time import of a transposed, group-quantised
+ * ternary weight (the gemlite-int2 kind) into Q2_0, with no numeric change.
+ * Source: We're Teaching Your Browser to Paint, section "The lucky break that
+ * wasn't luck": the source's codes are {0,1,2}, four per byte, least
+ * significant pair first, along the input axis; each group has a scale and a
+ * zero point, and every zero equals minus its scale, so each weight is
+ * (q - 1) * scale -- the Q2_0 formula.  The conversion is a transpose and a
+ * regroup; the f32 -> f16 scale cast must be exact or it stops.  The layout
+ * beyond that is this library's reading:
+ *   codes_t    u8  [K/4, N]: byte j of column n holds codes 4j..4j+3 of
+ *              weight row n (input-major)                             (in)
+ *   scales_t   f32 [K/G, N]; zeros_t f32 [K/G, N]: weight = q * scale + zero  (in)
+ *   G          group length: divides 128 or is a multiple of it, and divides
+ *              K (Q2_ERR_SHAPE otherwise)
+ *   packed     u8  [N, K/4], 16-byte aligned; scales_f16 u16 [N, K/128]  (out)
+ *   bad_index  host int64*, may be NULL: the first bad flat index (weight
+ *              index n * K + k for a code, group index g * N + n otherwise),
+ *              -1 on success.
+ * Checked, and reported in this order: a code 3 (Q2_ERR_CODE); a zero that
+ * is not exactly -scale (Q2_ERR_FORMAT); a scale that is not a finite exact
+ * f16 value, then a group whose scale differs from its block's first group
+ * when G < 128 (Q2_ERR_SCALE).  Synchronizes `stream`, and allocates and
+ * frees a 32-byte device buffer for the flags.  The outputs must not be used
+ * after an error.
+ */
+int q2_import_gemlite(const uint8_t* codes_t, const float* scales_t, const float* zeros_t,
+                      int64_t N, int64_t K, int64_t G, uint8_t* packed, uint16_t* scales_f16,
+                      int64_t* bad_index, hipStream_t stream);
 
 /*
  * q2_linear - y = x W^T with W[n, k] = (q[n, k] - 1) * d[n, k/128].

@@ -24,11 +24,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("Q2_LIB") or os.path.join(_HERE, "libq2.so")
 
 Q2_OK, Q2_ERR_ARG, Q2_ERR_SHAPE, Q2_ERR_ALIGN, Q2_ERR_CODE, Q2_ERR_SCALE, Q2_ERR_DEVICE, Q2_ERR_HIP, \
-    Q2_ERR_WORKSPACE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+    Q2_ERR_WORKSPACE, Q2_ERR_FORMAT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 Q2_ACCUMULATE = 0x1      # q2_linear_ex flag: y += result
 
-EXPORTS = ("q2_pack", "q2_linear", "q2_lowrank_workspace_bytes", "q2_linear_lowrank", "q2_linear_ex", "q2_slice",
+EXPORTS = ("q2_pack", "q2_import_gemlite", "q2_linear", "q2_lowrank_workspace_bytes", "q2_linear_lowrank", "q2_linear_ex", "q2_slice",
            "q4_linear", "q2_dequant", "q2_strerror", "q2_last_error")
 
 _lib = None
@@ -53,6 +53,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     p, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     sigs = {
         "q2_pack": ([p, p, i64, i64, p, p, ctypes.POINTER(ctypes.c_int64), p], ctypes.c_int),
+        "q2_import_gemlite": ([p, p, p, i64, i64, i64, p, p, ctypes.POINTER(ctypes.c_int64), p], ctypes.c_int),
         "q2_linear": ([p, p, p, p, i64, i64, i64, p], ctypes.c_int),
         "q2_lowrank_workspace_bytes": ([i64, i64], sz),
         "q2_linear_lowrank": ([p, p, p, p, p, i64, p, i64, i64, i64, p, sz, p], ctypes.c_int),
@@ -106,6 +107,28 @@ def q2_pack(codes: torch.Tensor, scales: torch.Tensor, packed=None, scales_f16=N
         scales_f16 = torch.empty((n, k // 128), dtype=torch.float16, device=dev)
     bad = ctypes.c_int64(-1)
     st = lib.q2_pack(_ptr(codes), _ptr(scales), n, k, _ptr(packed), _ptr(scales_f16), ctypes.byref(bad), _stream())
+    _check(st, bad.value)
+    return packed, scales_f16
+
+
+def q2_import_gemlite(codes_t, scales_t, zeros_t, group: int, packed=None, scales_f16=None):
+    """Transposed group-quantised ternary weight -> Q2_0: codes_t u8 [K/4, N] (input-major),
+    scales_t / zeros_t f32 [K/G, N] -> (packed u8 [N, K/4], scales f16 [N, K/128])."""
+    lib = load()
+    kq, n = codes_t.shape
+    k = kq * 4
+    _want(codes_t, torch.uint8, (kq, n), "codes_t")
+    g = max(int(group), 1)
+    _want(scales_t, torch.float32, (k // g, n), "scales_t")
+    _want(zeros_t, torch.float32, (k // g, n), "zeros_t")
+    dev = codes_t.device
+    if packed is None:
+        packed = torch.empty((n, kq), dtype=torch.uint8, device=dev)
+    if scales_f16 is None:
+        scales_f16 = torch.empty((n, k // 128), dtype=torch.float16, device=dev)
+    bad = ctypes.c_int64(-1)
+    st = lib.q2_import_gemlite(_ptr(codes_t), _ptr(scales_t), _ptr(zeros_t), n, k, int(group), _ptr(packed),
+                               _ptr(scales_f16), ctypes.byref(bad), _stream())
     _check(st, bad.value)
     return packed, scales_f16
 

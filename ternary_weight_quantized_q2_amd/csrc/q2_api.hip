@@ -176,6 +176,7 @@ const char* q2_strerror(int status) {
     case Q2_ERR_DEVICE: return "Q2_ERR_DEVICE: current device is not gfx950";
     case Q2_ERR_HIP: return "Q2_ERR_HIP: HIP runtime error";
     case Q2_ERR_WORKSPACE: return "Q2_ERR_WORKSPACE: workspace too small or misaligned";
+    case Q2_ERR_FORMAT: return "Q2_ERR_FORMAT: zero point is not minus the scale";
     default: return "unknown q2 status";
   }
 }
@@ -253,6 +254,54 @@ int q4_linear(const uint16_t* x_bf16, const uint8_t* packed4, const uint16_t* sc
   if (M == 0 || N == 0) return ok();
   if ((st = check_device())) return st;
   return linear_common(1, x_bf16, packed4, scale_f16, zero_f16, y, M, N, K, nullptr, nullptr, 0, false, stream);
+}
+
+int q2_import_gemlite(const uint8_t* codes_t, const float* scales_t, const float* zeros_t, int64_t N, int64_t K,
+                      int64_t G, uint8_t* packed, uint16_t* scales_f16, int64_t* bad_index, hipStream_t stream) {
+  if (bad_index) *bad_index = -1;
+  int st = check_sizes(0, N, K);
+  if (st) return st;
+  if (G <= 0 || G % 4 != 0 || (128 % G != 0 && G % 128 != 0) || K % G != 0)
+    return fail(Q2_ERR_SHAPE, "group length G=%lld must divide 128 or be a multiple of it, and divide K=%lld",
+                (long long)G, (long long)K);
+  const bool ne = N > 0 && K > 0;
+  if ((st = check_ptr(codes_t, ne, 1, "codes_t")) || (st = check_ptr(scales_t, ne, 4, "scales_t")) ||
+      (st = check_ptr(zeros_t, ne, 4, "zeros_t")) || (st = check_ptr(packed, ne, 16, "packed")) ||
+      (st = check_ptr(scales_f16, ne, 2, "scales_f16")))
+    return st;
+  if (!ne) return ok();
+  if ((st = check_device())) return st;
+
+  unsigned long long* flags = nullptr;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&flags), 4 * sizeof(unsigned long long));
+  if (e != hipSuccess) return hip_status(e, "hipMalloc(import flags)");
+  unsigned long long host[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+  e = hipMemsetAsync(flags, 0xFF, sizeof host, stream);
+  if (e == hipSuccess) e = q2dev::launch_import(codes_t, scales_t, zeros_t, N, K, G, packed, scales_f16, flags, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(host, flags, sizeof host, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  hipError_t ef = hipFree(flags);
+  if (e != hipSuccess) return hip_status(e, "q2_import_gemlite");
+  if (ef != hipSuccess) return hip_status(ef, "hipFree(import flags)");
+  // Reported in the order codes, zero points, scale values, block agreement.
+  if (host[0] != ~0ull) {
+    if (bad_index) *bad_index = (int64_t)host[0];
+    return fail(Q2_ERR_CODE, "code 3 at weight index %llu", host[0]);
+  }
+  if (host[1] != ~0ull) {
+    if (bad_index) *bad_index = (int64_t)host[1];
+    return fail(Q2_ERR_FORMAT, "zero point at group index %llu is not minus its scale", host[1]);
+  }
+  if (host[2] != ~0ull) {
+    if (bad_index) *bad_index = (int64_t)host[2];
+    return fail(Q2_ERR_SCALE, "scale at group index %llu is not an exact f16 value", host[2]);
+  }
+  if (host[3] != ~0ull) {
+    if (bad_index) *bad_index = (int64_t)host[3];
+    return fail(Q2_ERR_SCALE, "scale at group index %llu differs from its 128-weight block's first group",
+                host[3]);
+  }
+  return ok();
 }
 
 int q2_slice(const uint8_t* packed, const uint16_t* scales_f16, int64_t N, int64_t K, int64_t n0, int64_t n1,

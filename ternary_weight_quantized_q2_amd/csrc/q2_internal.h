@@ -36,6 +36,9 @@ hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t N, int
                        hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* packed, const uint16_t* scales, float* w,
                           int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_import(const uint8_t* codes_t, const float* scales_t, const float* zeros_t, int64_t N, int64_t K,
+                         int64_t G, uint8_t* packed, uint16_t* scales_f16, unsigned long long* flags,
+                         hipStream_t stream);
 hipError_t launch_slice(const uint8_t* packed, const uint16_t* scales, int64_t K, int64_t n0, int64_t rows,
                         int64_t k0, int64_t ks, uint8_t* out, uint16_t* out_scales, hipStream_t stream);
 

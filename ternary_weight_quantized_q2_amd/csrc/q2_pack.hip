@@ -1,5 +1,6 @@
-// q2_pack.hip - load-time Q2_0 packing with validation, slicing of packed
-// weights, and the exact decode used by tests.
+// q2_pack.hip - load-time Q2_0 packing with validation, import of a
+// transposed group-quantised ternary weight, slicing of packed weights, and
+// the exact decode used by tests.
 //
 // Packing follows the Q2_0 layout of "We're Teaching Your Browser to Paint"
 // (aitherium.com), section "The lucky break that wasn't luck": four 2-bit
@@ -90,6 +91,51 @@ __global__ __launch_bounds__(256) void slice_kernel(const uint8_t* packed, const
   }
 }
 
+// Import of a transposed group-quantised ternary weight (source bytes
+// [K/4, N], input-major; f32 scales and zeros [K/G, N]).  Its code bytes
+// already hold four codes each in the Q2_0 order, so the codes are a byte
+// transpose; one thread per source byte (reads coalesced along N).  A code 3
+// is flagged with the flat index n * K + k of the weight.
+__global__ __launch_bounds__(256) void import_codes_kernel(const uint8_t* src, uint8_t* packed, int64_t N,
+                                                           int64_t K, unsigned long long* flags) {
+  const int64_t total = N * (K / 4);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t j = i / N, n = i - j * N;
+    const uint32_t b = src[i];
+    packed[n * (K / 4) + j] = (uint8_t)b;
+    const uint32_t three = b & (b >> 1) & 0x55u;          // bit 2p set where code p is 3
+    if (three) atomicMin(&flags[0], (unsigned long long)(n * K + 4 * j + (__builtin_ctz(three) >> 1)));
+  }
+}
+
+// One thread per (block b, row n), along N: the groups that cover block b are
+// checked (zero == -scale, flag 1; finite exact f16 scale, flag 2; the same
+// scale as the block's first group, flag 3, indices g * N + n) and the block's
+// scale is written as f16.
+__global__ __launch_bounds__(256) void import_scales_kernel(const float* st, const float* zt, uint16_t* sh,
+                                                            int64_t N, int64_t K, int64_t G,
+                                                            unsigned long long* flags) {
+  const int64_t KB = K / BLOCK_K;
+  const int64_t total = N * KB;
+  const int64_t per = G < BLOCK_K ? BLOCK_K / G : 1;     // groups per block
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t b = i / N, n = i - b * N;
+    const int64_t g0 = G < BLOCK_K ? b * per : b * BLOCK_K / G;
+    const float s0 = st[g0 * N + n];
+    for (int64_t q = 0; q < per; ++q) {
+      const int64_t idx = (g0 + q) * N + n;
+      const float sv = st[idx], zv = zt[idx];
+      if (!(zv == -sv)) atomicMin(&flags[1], (unsigned long long)idx);
+      const _Float16 h = (_Float16)sv;
+      if (!__builtin_isfinite(sv) || (float)h != sv) atomicMin(&flags[2], (unsigned long long)idx);
+      if (sv != s0) atomicMin(&flags[3], (unsigned long long)idx);
+    }
+    sh[n * KB + b] = __builtin_bit_cast(uint16_t, (_Float16)s0);
+  }
+}
+
 static unsigned grid_for(int64_t work) {
   int64_t blocks = (work + 255) / 256;
   if (blocks > 4096) blocks = 4096;
@@ -106,6 +152,18 @@ hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t N, int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pack_scales_kernel, dim3(grid_for(ns)), dim3(256), 0, stream, scales, scales_f16, ns, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_import(const uint8_t* codes_t, const float* scales_t, const float* zeros_t, int64_t N, int64_t K,
+                         int64_t G, uint8_t* packed, uint16_t* scales_f16, unsigned long long* flags,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL(import_codes_kernel, dim3(grid_for(N * (K / 4))), dim3(256), 0, stream, codes_t, packed, N, K,
+                     flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(import_scales_kernel, dim3(grid_for(N * (K / BLOCK_K))), dim3(256), 0, stream, scales_t,
+                     zeros_t, scales_f16, N, K, G, flags);
   return hipGetLastError();
 }
 

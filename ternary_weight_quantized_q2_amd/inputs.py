@@ -17,7 +17,13 @@ and a 4-bit text-encoder linear):
 * low-rank factors A [r, K] and B [N, r] are N(0, std 0.01) rounded to f16;
 * 4-bit weights are uniform random bytes, i.e. two independent codes uniform on
   0..15 per byte; their group scales are |N(0,1)| * 0.02 and zero points
-  U(0, 15), both rounded to f16.
+  U(0, 15), both rounded to f16;
+* a transposed group-quantised ternary source (for the importer) has bytes
+  [K/4, N] drawn uniformly from the 81 byte values whose four 2-bit fields are
+  all below 3 (so every code is i.i.d. uniform on {0, 1, 2}, whatever order the
+  fields are read in), f32 group scales [K/G, N] that are f16-exact values of
+  |N(0,1)| * 0.02 and equal across the groups of a 128-weight block, and zero
+  points equal to minus the scales.
 """
 from __future__ import annotations
 
@@ -26,7 +32,7 @@ import numpy as np
 GROUP = 128  # weights per Q2_0 block / per 4-bit group
 
 # tensor ids inside a config's seed tuple
-T_CODES, T_SCALES, T_X, T_A, T_B, T_Q4, T_Q4S, T_Q4Z = range(8)
+T_CODES, T_SCALES, T_X, T_A, T_B, T_Q4, T_Q4S, T_Q4Z, T_SRC, T_SRCS = range(10)
 
 
 def stream(config_id: int, tensor_id: int, seed: int = 0) -> np.random.Generator:
@@ -108,3 +114,21 @@ LOWRANK = dict(M=1536, K=3072, N=9216, ranks=(4, 32, 64), linears=100, steps=4)
 QUARTER_M = (384, 256, 128)
 Q4_M = 128
 Q4_SHAPES = [(2560, 9728), (9728, 2560), (2560, 2560)]                     # (K, N)
+
+
+# Byte values whose four 2-bit fields are all in {0, 1, 2}.
+_TERNARY_BYTES = np.array([b for b in range(256) if all((b >> (2 * f)) & 3 != 3 for f in range(4))], np.uint8)
+
+
+def gemlite_source(config_id: int, n: int, k: int, group: int):
+    """(bytes u8 [k/4, n], scales f32 [k/group, n], zeros f32 [k/group, n]): a
+    valid transposed group-quantised ternary weight for the importer."""
+    b = _TERNARY_BYTES[stream(config_id, T_SRC).integers(0, len(_TERNARY_BYTES), size=(k // 4, n))]
+    blocks = np.abs(stream(config_id, T_SRCS).standard_normal((k // GROUP, n), dtype=np.float32)) * np.float32(0.02)
+    blocks = blocks.astype(np.float16).astype(np.float32)
+    if group < GROUP:
+        scales = np.repeat(blocks, GROUP // group, axis=0)
+    else:
+        scales = blocks[::group // GROUP]
+    scales = np.ascontiguousarray(scales)
+    return np.ascontiguousarray(b), scales, np.ascontiguousarray(-scales)

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_and_workspace_size(lib):
-    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert lib.q2_strerror(st)
     assert b"unknown" in lib.q2_strerror(-99)
     assert lib.q2_lowrank_workspace_bytes(0, 32) == 0
@@ -125,6 +125,22 @@ def test_slice_argument_errors(lib):
     # empty ranges do nothing, NULL pointers allowed
     assert S(None, None, 8, 512, 3, 3, 0, 128, None, None, None) == q2.Q2_OK
     assert S(None, None, 8, 512, 0, 8, 256, 256, None, None, None) == q2.Q2_OK
+
+
+def test_import_argument_errors(lib):
+    I_ = lib.q2_import_gemlite
+    bad = ctypes.c_int64(123)
+    assert I_(FAKE, FAKE, FAKE, 8, 512, 48, FAKE, FAKE, ctypes.byref(bad), None) == q2.Q2_ERR_SHAPE   # G
+    assert bad.value == -1
+    assert I_(FAKE, FAKE, FAKE, 8, 384, 256, FAKE, FAKE, None, None) == q2.Q2_ERR_SHAPE     # G does not divide K
+    assert I_(FAKE, FAKE, FAKE, 8, 500, 64, FAKE, FAKE, None, None) == q2.Q2_ERR_SHAPE      # K
+    assert I_(FAKE, FAKE, FAKE, 8, 512, 0, FAKE, FAKE, None, None) == q2.Q2_ERR_SHAPE
+    assert I_(FAKE, FAKE, FAKE, -1, 512, 64, FAKE, FAKE, None, None) == q2.Q2_ERR_ARG
+    assert I_(FAKE, FAKE + 2, FAKE, 8, 512, 64, FAKE, FAKE, None, None) == q2.Q2_ERR_ALIGN
+    assert I_(FAKE, FAKE, FAKE, 8, 512, 64, FAKE + 4, FAKE, None, None) == q2.Q2_ERR_ALIGN
+    assert I_(None, FAKE, FAKE, 8, 512, 64, FAKE, FAKE, None, None) == q2.Q2_ERR_ARG
+    assert I_(None, None, None, 0, 512, 64, None, None, None, None) == q2.Q2_OK
+    assert I_(None, None, None, 8, 0, 64, None, None, None, None) == q2.Q2_OK
 
 
 def test_pack_argument_errors(lib):

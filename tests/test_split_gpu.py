@@ -199,3 +199,52 @@ def test_split_projection(m, r):
 def test_split_projection_full_size(r):
     # single-block output projection: attention output (3072) and MLP output (12288) side by side
     _split(1536, 3072, 3072, 12288, r, cols=sample_cols(3072, 128, seed=7))
+
+
+# ---------------------------------------------------------------------------
+# import of a transposed group-quantised ternary weight
+# ---------------------------------------------------------------------------
+
+def _import_dev(ct, st, zt, group):
+    return q2.q2_import_gemlite(torch.from_numpy(ct).to(DEV), torch.from_numpy(st).to(DEV),
+                                torch.from_numpy(zt).to(DEV), group)
+
+
+@pytest.mark.parametrize("n,k,group", [(37, 512, 32), (64, 1280, 64), (1000, 384, 128), (300, 1024, 256),
+                                       (3, 1536, 512), (3072, 12288, 64)])
+def test_import_bitexact(n, k, group):
+    ct, st, zt = I.gemlite_source(group + n, n, k, group)
+    p, s = _import_dev(ct, st, zt, group)
+    torch.cuda.synchronize()
+    want_p, want_s = O.import_gemlite(ct, st, zt, group)
+    assert np.array_equal(p.cpu().numpy(), want_p)
+    assert np.array_equal(host_bits(s), want_s)
+
+
+def test_import_errors_match_the_oracle():
+    n, k, group = 6, 256, 64
+    ct, st, zt = I.gemlite_source(7, n, k, group)
+    cases = []
+    bad = ct.copy()
+    bad[5, 3] |= 0x30
+    bad[9, 1] |= 0x03                                  # a second code 3: the smaller weight index is reported
+    cases.append((bad, st, zt, q2.Q2_ERR_CODE))
+    z = zt.copy()
+    z[2, 4] = -z[2, 4]
+    z[3, 0] = 1.0
+    cases.append((ct, st, z, q2.Q2_ERR_FORMAT))
+    sc = st.copy()
+    sc[1, 1] = np.float32(0.1)
+    cases.append((ct, sc, -sc, q2.Q2_ERR_SCALE))
+    sc2 = st.copy()
+    sc2[3, 5] *= 2
+    cases.append((ct, sc2, -sc2, q2.Q2_ERR_SCALE))
+    both = bad.copy()
+    cases.append((both, sc, z, q2.Q2_ERR_CODE))            # codes are checked first
+    for ct_, st_, zt_, status in cases:
+        with pytest.raises(O.ImportError_) as ref:
+            O.import_gemlite(ct_, st_, zt_, group)
+        with pytest.raises(q2.Q2Error) as e:
+            _import_dev(ct_, st_, zt_, group)
+        assert e.value.status == status
+        assert e.value.bad_index == ref.value.index
