@@ -297,6 +297,37 @@ def import_gemlite(codes_t: np.ndarray, scales_t: np.ndarray, zeros_t: np.ndarra
 
 
 # ---------------------------------------------------------------------------
+# 8-bit activations
+# ---------------------------------------------------------------------------
+# "We're Teaching Your Browser to Paint", section "The GPU driver, and the bug
+# that looked like broken math": on the GPU path the activations run through
+# 8-bit quantization, which sets a few-percent error floor.  The page gives no
+# more.  Readings: per-row (per-token) symmetric absmax scaling, s = amax / 127
+# in float32; each code is x / s in float32, rounded to nearest even and
+# clamped to [-127, 127]; a row of zeros has s = 0 and all codes 0; the
+# product is y[m, n] = s[m] * sum_k xq[m, k] * w[n, k].  The codes are decided
+# in float32 with IEEE division (NumPy's float32 arithmetic), as the kernel
+# does.
+
+def quantize_rows_a8(x_bits: np.ndarray):
+    """bf16 bits [M, K] -> (codes int32 [M, K] in [-127, 127], scales float32 [M])."""
+    x = (np.asarray(x_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.rint((x / safe[:, None]).astype(np.float32))
+    q = np.clip(q, -127, 127).astype(np.int32)
+    q[s == 0, :] = 0
+    return q, s
+
+
+def q2_linear_a8(x_bits: np.ndarray, packed: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """y [M, N] = s[m] * (xq W^T) in float64, xq, s from quantize_rows_a8."""
+    q, s = quantize_rows_a8(x_bits)
+    return s.astype(np.float64)[:, None] * (q.astype(np.float64) @ unpack_q2(packed, scale_bits).T)
+
+
+# ---------------------------------------------------------------------------
 # Low-rank side branch  y = W x + B (A x)
 # ---------------------------------------------------------------------------
 

@@ -332,6 +332,57 @@ def test_import_pins():
         O.import_gemlite(np.zeros((32, 2), np.uint8), np.zeros((3, 2), np.float32), np.zeros((3, 2), np.float32), 48)
 
 
+def check_a8(quantize, linear_a8):
+    """8-bit activations: the hand-built row; every code within half a step of
+    x / s; the row maximum at +-127; one scale per row; a zero row; and the
+    product within the quantisation bound of the unquantised one."""
+    g = golden("a8_hand.json")
+    k = g["K"]
+    x = np.zeros((1, k), np.float32)
+    x[0, :len(g["x_head"])] = g["x_head"]
+    xb = I.f32_to_bf16_bits(x)
+    q, sc = quantize(xb)
+    assert list(q[0, :8]) == g["codes_head"] and not q[0, 8:].any()
+    assert int(np.asarray(sc, np.float32).view(np.uint32)[0]) == g["scale_f32_bits"]
+    codes = np.ones((1, k), np.uint8)
+    codes[0, :8] = g["w_codes_head"]
+    packed, scb = O.pack_q2(codes, np.ones((1, 1), np.float32))
+    y = linear_a8(xb, packed, scb)
+    s = float(np.asarray(sc, np.float32)[0])
+    assert y[0, 0] == g["code_sum"] * s
+    assert abs(y[0, 0] - g["y_unquantized"]) < 0.01 * g["y_unquantized"]
+    # random rows of different ranges, one of them all zeros
+    m, k2, n = 5, 384, 9
+    xr = I.activations_bf16(99, m, k2).copy()
+    xf = (xr.astype(np.uint32) << 16).view(np.float32).copy()
+    xf[1] *= 64.0
+    xf[3] = 0.0
+    xr = I.f32_to_bf16_bits(xf)
+    xf = (xr.astype(np.uint32) << 16).view(np.float32)
+    q, sc = quantize(xr)
+    sc = np.asarray(sc, np.float32)
+    amax = np.abs(xf).max(axis=1)
+    assert sc[3] == 0 and not q[3].any()
+    for r in (0, 1, 2, 4):
+        assert abs(float(sc[r]) - float(amax[r]) / 127) <= 2.0 ** -23 * float(amax[r]) / 127
+        assert np.abs(q[r]).max() == 127
+        err = np.abs(xf[r].astype(np.float64) / float(sc[r]) - q[r])
+        assert err.max() <= 0.5 + 1e-5
+    assert abs(float(sc[1]) / float(sc[0]) - float(amax[1]) / float(amax[0])) < 1e-6 * float(sc[1] / sc[0])
+    codes = I.q2_codes(99, n, k2)
+    packed, scb = O.pack_q2(codes, I.q2_scales(99, n, k2))
+    w = O.unpack_q2(packed, scb)
+    ya8 = linear_a8(xr, packed, scb)
+    yref = O.q2_linear(xr, packed, scb)
+    bound = (sc.astype(np.float64)[:, None] / 2) * (np.abs(w).sum(axis=1)[None, :]) * (1 + 1e-5)
+    assert np.all(np.abs(ya8 - yref) <= bound)
+    assert not ya8[3].any()
+
+
+def test_a8_pins():
+    check_a8(O.quantize_rows_a8, O.q2_linear_a8)
+
+
 # ---------------------------------------------------------------------------
 # pack: scale round trip and code check
 # ---------------------------------------------------------------------------

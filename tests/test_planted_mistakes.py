@@ -93,7 +93,41 @@ def import_regroup_unchecked(ct, st, zt, group):    # takes each block's first g
     return O.import_gemlite(ct, st, zt, group)
 
 
+def a8_truncating(xb):                              # codes truncated instead of rounded
+    x = (np.asarray(xb, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    _, s = O.quantize_rows_a8(xb)
+    safe = np.where(s > 0, s, np.float32(1)).astype(np.float32)
+    q = np.clip(np.trunc(x / safe[:, None]), -127, 127).astype(np.int32)
+    q[s == 0] = 0
+    return q, s
+
+
+def a8_per_tensor(xb):                              # one scale for the whole matrix
+    x = (np.asarray(xb, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    amax = np.float32(np.abs(x).max())
+    s = np.full(x.shape[0], amax / np.float32(127), np.float32)
+    q = np.clip(np.rint(x / s[:, None]), -127, 127).astype(np.int32)
+    return q, s
+
+
+def a8_unsigned_range(xb):                          # scale for 255 levels
+    q, s = O.quantize_rows_a8(xb)
+    x = (np.asarray(xb, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    s2 = (np.max(np.abs(x), axis=1) / np.float32(255)).astype(np.float32)
+    safe = np.where(s2 > 0, s2, np.float32(1)).astype(np.float32)
+    return np.clip(np.rint(x / safe[:, None]), -255, 255).astype(np.int32), s2
+
+
+def a8_scale_dropped(xb, p, s):                     # the row scale never applied
+    q, _ = O.quantize_rows_a8(xb)
+    return q.astype(np.float64) @ O.unpack_q2(p, s).T
+
+
 MUTANTS = {
+    "a8 truncating": lambda: P.check_a8(a8_truncating, O.q2_linear_a8),
+    "a8 per-tensor scale": lambda: P.check_a8(a8_per_tensor, O.q2_linear_a8),
+    "a8 255 levels": lambda: P.check_a8(a8_unsigned_range, O.q2_linear_a8),
+    "a8 row scale dropped": lambda: P.check_a8(O.quantize_rows_a8, a8_scale_dropped),
     "import without the transpose": lambda: P.check_import(import_no_transpose),
     "import accepts zero == +scale": lambda: P.check_import(import_zero_plus_scale),
     "import regroups without comparing": lambda: P.check_import(import_regroup_unchecked),
@@ -131,3 +165,4 @@ def test_unmutated_checks_pass():
     P.check_slice(O.slice_q2)
     P.check_split_sum(O.q2_linear_sum)
     P.check_import(O.import_gemlite)
+    P.check_a8(O.quantize_rows_a8, O.q2_linear_a8)
