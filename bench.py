@@ -216,6 +216,29 @@ def measure_quarter_step(torch, q2, I, dev, reps=20):
             "calls": out}
 
 
+def measure_a8(torch, q2, I, dev, reps=20):
+    """The 8-bit activation linear (per-row quantisation + the Q2_0 GEMM with a
+    row scale) on the four M = 1536 GEMM shapes, beside the bf16 linear on the
+    same inputs.  Reported beside the step, not part of it."""
+    m = I.GEMM_M
+    out, tot_t, tot_b, tot_f = {}, 0.0, 0.0, 0.0
+    for k, n in I.GEMM_SHAPES:
+        p, s = q2.q2_pack(torch.from_numpy(I.q2_codes_fast(970, n, k)).to(dev),
+                          torch.from_numpy(I.q2_scales(970, n, k)).to(dev))
+        x = torch.from_numpy(I.activations_bf16(970, m, k).view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((m, n), device=dev)
+        ws = torch.empty(q2.a8_workspace_bytes(m, k), dtype=torch.uint8, device=dev)
+        t8 = _best_graph_time(torch, lambda: q2.q2_linear_a8(x, p, s, y=y, workspace=ws), reps)
+        tb = _best_graph_time(torch, lambda: q2.q2_linear(x, p, s, y=y), reps)
+        f = 2.0 * m * n * k
+        out[f"K={k} N={n}"] = {"us_a8": round(t8 * 1e6, 3), "us_bf16": round(tb * 1e6, 3)}
+        tot_t += t8
+        tot_b += tb
+        tot_f += f
+    return {"shape": f"M={m}", "tflops_a8": round(tot_f / tot_t / 1e12, 3),
+            "tflops_bf16": round(tot_f / tot_b / 1e12, 3), "calls": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +251,7 @@ def main():
                     "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref")
     ap.add_argument("--no-split", action="store_true", help="skip the split output projection measurement")
     ap.add_argument("--no-quarter", action="store_true", help="skip the quarter-size first step measurement")
+    ap.add_argument("--no-a8", action="store_true", help="skip the 8-bit activation measurement")
     ap.add_argument("--no-layer-list", action="store_true",
                     help="skip the 100-linear rank-32 layer list report")
     args = ap.parse_args()
@@ -374,6 +398,7 @@ def main():
     layer_list = None if (args.no_layer_list or args.only) else measure_layer_list(torch, q2, I, dev)
     split_proj = None if (args.no_split or args.only) else measure_split_projection(torch, q2, I, dev)
     quarter = None if (args.no_quarter or args.only) else measure_quarter_step(torch, q2, I, dev)
+    a8 = None if (args.no_a8 or args.only) else measure_a8(torch, q2, I, dev)
 
     parts = {}
     fam_time, fam_flops, fam_bytes = {}, {}, {}
@@ -428,6 +453,8 @@ def main():
         out["split_projection"] = split_proj
     if quarter is not None:
         out["quarter_step"] = quarter
+    if a8 is not None:
+        out["a8_linear"] = a8
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

@@ -205,6 +205,35 @@ int q2_slice(const uint8_t* packed, const uint16_t* scales_f16, int64_t N, int64
              uint8_t* out_packed, uint16_t* out_scales, hipStream_t stream);
 
 /*
+ * q2_a8_workspace_bytes - device bytes q2_linear_a8 needs for M rows of K
+ * inputs: M * K * 2 rounded up to 256 (the codes), plus M * 4 rounded up to
+ * 256 (the row scales); 0 when M or K is 0 or negative.
+ */
+size_t q2_a8_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * q2_linear_a8 - the Q2_0 linear with 8-bit activations:
+ * y[m, n] = s[m] * sum_k c[m, k] * W[n, k], where per row m, s[m] = max_k
+ * |x[m, k]| / 127 and c[m, k] = round-half-even(x[m, k] / s[m]) clamped to
+ * [-127, 127] (float32, IEEE division; a row of zeros has s = 0, c = 0).
+ * Source: We're Teaching Your Browser to Paint, section "The GPU driver, and
+ * the bug that looked like broken math" (the GPU path quantizes activations
+ * to 8 bits, at a few-percent error floor); the per-row symmetric scheme and
+ * its rounding are this library's reading.
+ *   x_bf16, packed, scales_f16, y, M, N, K   as q2_linear (x finite)
+ *   workspace  device scratch of >= q2_a8_workspace_bytes(M, K) bytes,
+ *              256-byte aligned, owned by the caller.  After the call it holds
+ *              the codes as bf16 bit patterns [M, K] at offset 0 and the
+ *              scales f32 [M] at offset M * K * 2 rounded up to 256.
+ * The codes are exact in bf16, so the products stay exact and accumulate in
+ * fp32; the row scale is applied once per output.  Asynchronous; calls that
+ * share a workspace must be ordered on one stream.
+ */
+int q2_linear_a8(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
+                 float* y, int64_t M, int64_t N, int64_t K,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * q4_linear - 4-bit variant: y = x W^T with W[n, k] = (q[n, k] - z[n, k/128]) * s[n, k/128],
  * q[n, k] = (packed4[n, k/2] >> (4 * (k & 1))) & 15 (the low nibble holds the even k).
  * Source: You Can Now Just Ask for an Image (aitherium.com), section "The bug

@@ -29,6 +29,7 @@ Q2_OK, Q2_ERR_ARG, Q2_ERR_SHAPE, Q2_ERR_ALIGN, Q2_ERR_CODE, Q2_ERR_SCALE, Q2_ERR
 Q2_ACCUMULATE = 0x1      # q2_linear_ex flag: y += result
 
 EXPORTS = ("q2_pack", "q2_import_gemlite", "q2_linear", "q2_lowrank_workspace_bytes", "q2_linear_lowrank", "q2_linear_ex", "q2_slice",
+           "q2_a8_workspace_bytes", "q2_linear_a8",
            "q4_linear", "q2_dequant", "q2_strerror", "q2_last_error")
 
 _lib = None
@@ -59,6 +60,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "q2_linear_lowrank": ([p, p, p, p, p, i64, p, i64, i64, i64, p, sz, p], ctypes.c_int),
         "q2_linear_ex": ([p, p, p, p, p, i64, p, i64, i64, i64, p, sz, ctypes.c_uint32, p], ctypes.c_int),
         "q2_slice": ([p, p, i64, i64, i64, i64, i64, i64, p, p, p], ctypes.c_int),
+        "q2_a8_workspace_bytes": ([i64, i64], sz),
+        "q2_linear_a8": ([p, p, p, p, i64, i64, i64, p, sz, p], ctypes.c_int),
         "q4_linear": ([p, p, p, p, p, i64, i64, i64, p], ctypes.c_int),
         "q2_dequant": ([p, p, p, i64, i64, p], ctypes.c_int),
         "q2_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -225,6 +228,30 @@ def q2_slice(packed, scales, n0: int, n1: int, k0: int, k1: int, out=None, out_s
     _want(out_scales, torch.float16, (rows, ks // 128), "out_scales")
     _check(lib.q2_slice(_ptr(packed), _ptr(scales), n, k, n0, n1, k0, k1, _ptr(out), _ptr(out_scales), _stream()))
     return out, out_scales
+
+
+def a8_workspace_bytes(m: int, k: int) -> int:
+    return int(load().q2_a8_workspace_bytes(m, k))
+
+
+def q2_linear_a8(x, packed, scales, y=None, workspace=None) -> torch.Tensor:
+    """y = s * (c W^T) with x quantised per row to 8-bit codes c and scales s (the codes and scales are left
+    in the workspace: bf16 [M, K] at offset 0, f32 [M] after it, 256-byte aligned)."""
+    lib = load()
+    m, k = x.shape
+    n = packed.shape[0]
+    _want(x, torch.bfloat16, (m, k), "x")
+    _want(packed, torch.uint8, (n, k // 4), "packed")
+    _want(scales, torch.float16, (n, k // 128), "scales")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _want(y, torch.float32, (m, n), "y")
+    need = a8_workspace_bytes(m, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib.q2_linear_a8(_ptr(x), _ptr(packed), _ptr(scales), _ptr(y), m, n, k, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream()))
+    return y
 
 
 def q4_linear(x, packed4, scale, zero, y=None) -> torch.Tensor:

@@ -110,12 +110,13 @@ int forced_ksplit() {
 
 int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* s, const uint16_t* z, float* y,
                   int64_t M, int64_t N, int64_t K, const uint16_t* lr_t, const uint16_t* lr_b, int64_t r,
-                  bool accumulate, hipStream_t stream) {
+                  bool accumulate, hipStream_t stream, const float* row_scale = nullptr) {
   q2dev::LinearArgs a;
   a.x = x; a.w = w; a.s = s; a.z = z; a.y = y;
   a.M = M; a.N = N; a.K = K;
   a.lr_t = lr_t; a.lr_b = lr_b; a.r = (int)r;
   a.acc = accumulate ? 1 : 0;
+  a.row_scale = row_scale;
   int path = forced_path();
   if (path == 1 && M > 16) path = 0;
   const int cfg = forced_cfg();
@@ -182,6 +183,38 @@ const char* q2_strerror(int status) {
 }
 
 const char* q2_last_error(void) { return g_detail; }
+
+size_t q2_a8_workspace_bytes(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0 || M > ((int64_t)1 << 40) / K) return 0;
+  const size_t codes = ((size_t)M * (size_t)K * 2u + 255u) & ~(size_t)255u;
+  return codes + (((size_t)M * 4u + 255u) & ~(size_t)255u);
+}
+
+int q2_linear_a8(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16, float* y, int64_t M,
+                 int64_t N, int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_sizes(M, N, K);
+  if (st || (st = check_linear_k(K))) return st;
+  if ((st = check_ptr(x_bf16, M > 0 && K > 0, 16, "x")) ||
+      (st = check_ptr(packed, N > 0 && K > 0, 16, "packed")) ||
+      (st = check_ptr(scales_f16, N > 0 && K > 0, 2, "scales_f16")) ||
+      (st = check_ptr(y, M > 0 && N > 0, 4, "y")))
+    return st;
+  if (M == 0 || N == 0) return ok();
+  const size_t need = q2_a8_workspace_bytes(M, K);
+  if (workspace_bytes < need)
+    return fail(Q2_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (need > 0 && workspace == nullptr) return fail(Q2_ERR_ARG, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(Q2_ERR_ALIGN, "workspace is not 256-byte aligned");
+  if ((st = check_device())) return st;
+  if (K == 0) return linear_common(0, x_bf16, packed, scales_f16, nullptr, y, M, N, K, nullptr, nullptr, 0, false,
+                                   stream);
+  uint16_t* xq = static_cast<uint16_t*>(workspace);
+  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                       (((size_t)M * (size_t)K * 2u + 255u) & ~(size_t)255u));
+  if ((st = hip_status(q2dev::launch_quantize_rows(x_bf16, xq, rs, M, K, stream), "8-bit quantisation launch")))
+    return st;
+  return linear_common(0, xq, packed, scales_f16, nullptr, y, M, N, K, nullptr, nullptr, 0, false, stream, rs);
+}
 
 size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r) {
   if (M <= 0 || r <= 0) return 0;

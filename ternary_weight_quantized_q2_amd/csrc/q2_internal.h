@@ -19,6 +19,7 @@ struct LinearArgs {
   const uint16_t* lr_b;
   int r;
   int acc;               // 1: y += result (y is read), 0: y = result
+  const float* row_scale;  // non-null: output row m is multiplied by row_scale[m] (8-bit activations)
 };
 
 // Path selection for tests: force_path 0 = automatic, 1 = force GEMV, 2 = force
@@ -29,6 +30,8 @@ struct LinearArgs {
 hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, int force_cfg, int force_ksplit,
                          hipStream_t stream);
 int gemm_config_id(const char* name);
+hipError_t launch_quantize_rows(const uint16_t* x, uint16_t* xq, float* row_scale, int64_t M, int64_t K,
+                                hipStream_t stream);
 hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* t_limbs,
                             int64_t M, int64_t K, int r, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K,

@@ -563,6 +563,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
     }
   }
 
+  if (a.row_scale) {                      // 8-bit activations: the row's scale
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = m0 + 16 * i + 4 * g + e;
+        const float rs = m < M ? a.row_scale[m] : 0.f;
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j][e] *= rs;
+      }
+  }
   if (a.acc) {                            // every old value in flight at once, then added
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -1031,6 +1042,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       int row, q;
       if (row_piece<BM, BN, 512>(t, tid, m0, M, ncols, row, q)) {
         q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
+        if (a.row_scale) v *= a.row_scale[m0 + row];
         if (a.acc) v += yo4[t];
         __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
       }
@@ -1056,8 +1068,9 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float v = acc[i][j][e] + red[((i * NT + j) * 4 + e) * 64 + lane];
-          if (a.acc) v += yo[i][j][e];
           const int64_t m = m0 + 16 * i + 4 * g + e;
+          if (a.row_scale && m < M) v *= a.row_scale[m];
+          if (a.acc) v += yo[i][j][e];
           if (m < M && n < N) __builtin_nontemporal_store(v, &a.y[m * N + n]);
         }
       }
@@ -1505,6 +1518,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
       int row, q;
       if (row_piece<BM, BN, 64 * W>(t, tid, m0, M, ncols, row, q)) {
         q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
+        if (a.row_scale) v *= a.row_scale[m0 + row];
         if (a.acc) v += yo4[t];
         __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
       }
@@ -1533,8 +1547,9 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
 #pragma unroll
           for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
           v *= fin;
-          if (a.acc) v += yo[i][j][e];
           const int64_t m = m0 + 16 * i + 4 * g + e;
+          if (a.row_scale && m < M) v *= a.row_scale[m];
+          if (a.acc) v += yo[i][j][e];
           if (m < M && n < N) {
             if (split) unsafeAtomicAdd(&a.y[m * N + n], v);
             else __builtin_nontemporal_store(v, &a.y[m * N + n]);
@@ -1736,10 +1751,71 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 4 * g + e;
-        if (m < M) a.y[(int64_t)m * a.N + n] = a.acc ? s[e] + yo[e] : s[e];
+        if (m < M) {
+          const float v = a.row_scale ? s[e] * a.row_scale[m] : s[e];
+          a.y[(int64_t)m * a.N + n] = a.acc ? v + yo[e] : v;
+        }
       }
     }
   }
+}
+
+// ============================================================================
+// 8-bit activations: per-row symmetric quantisation
+// ============================================================================
+// One workgroup per row: s = max |x| / 127 and code = round-half-even(x / s),
+// clamped to [-127, 127], both with IEEE float32 division; a row of zeros has
+// s = 0 and codes 0.  The codes are stored as bf16 bit patterns (every integer
+// up to 256 in magnitude is exact in bf16), so the exact-product linear
+// kernels multiply them unchanged, and s goes to the epilogue's row scale.
+constexpr int QZ_THREADS = 256;
+
+__global__ __launch_bounds__(QZ_THREADS) void quantize_rows_kernel(const uint16_t* x, uint16_t* xq, float* row_scale,
+                                                                   int64_t K) {
+  __shared__ float wmax[QZ_THREADS / 64];
+  const int64_t m = blockIdx.x;
+  const uint16_t* xr = x + m * K;
+  uint16_t* qr = xq + m * K;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  float amax = 0.f;
+  for (int64_t k = 8 * (int64_t)tid; k < K; k += 8 * QZ_THREADS) {     // K is a multiple of 128
+    const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(xr + k);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[d] << 16)));
+      amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[d] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (lane == 0) wmax[wv] = amax;
+  __syncthreads();
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < QZ_THREADS / 64; ++w) amax = fmaxf(amax, wmax[w]);
+  const float sc = amax / 127.0f;
+  if (tid == 0) row_scale[m] = sc;
+  for (int64_t k = 8 * (int64_t)tid; k < K; k += 8 * QZ_THREADS) {
+    const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(xr + k);
+    q2_u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      float c0 = 0.f, c1 = 0.f;
+      if (sc > 0.f) {
+        c0 = fminf(fmaxf(__builtin_rintf(__builtin_bit_cast(float, v[d] << 16) / sc), -127.f), 127.f);
+        c1 = fminf(fmaxf(__builtin_rintf(__builtin_bit_cast(float, v[d] & 0xFFFF0000u) / sc), -127.f), 127.f);
+      }
+      o[d] = (__builtin_bit_cast(uint32_t, c0 + 0.0f) >> 16) | (__builtin_bit_cast(uint32_t, c1 + 0.0f) & 0xFFFF0000u);
+    }
+    *reinterpret_cast<q2_u32x4*>(qr + k) = o;
+  }
+}
+
+hipError_t launch_quantize_rows(const uint16_t* x, uint16_t* xq, float* row_scale, int64_t M, int64_t K,
+                                hipStream_t stream) {
+  if (M > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)M), dim3(QZ_THREADS), 0, stream, x, xq, row_scale, K);
+  return hipGetLastError();
 }
 
 // ============================================================================

@@ -1,0 +1,98 @@
+"""GPU parity of the 8-bit activation linear (q2_linear_a8) against the CPU
+oracle.  The codes and row scales, which float32 arithmetic decides, must be
+bit-exact (both sides divide in IEEE float32 and round half to even); the
+product is held to the linear's tolerance against the oracle's y = s * (c W^T).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.q2_oracle as O
+import ternary_weight_quantized_q2_amd as q2
+from ternary_weight_quantized_q2_amd import inputs as I
+from tests.test_parity_gpu import DEV, assert_close, dev_bits, q2_weights, sample_cols
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU; they must not be skipped silently"
+    torch.cuda.set_device(0)
+    q2.load()
+    yield
+
+
+def a8_inputs(cfg, m, k):
+    """bf16 activations with rows of different ranges, a row of zeros and a row with one large value."""
+    x = (I.activations_bf16(cfg, m, k).astype(np.uint32) << 16).view(np.float32).copy()
+    x[::3] *= 37.0
+    if m > 1:
+        x[1] = 0.0
+    if m > 2:
+        x[2, k // 2] = 900.0
+    return I.f32_to_bf16_bits(x)
+
+
+def run_a8(xb, p, s, n):
+    m, k = xb.shape
+    ws = torch.zeros(max(q2.a8_workspace_bytes(m, k), 1), dtype=torch.uint8, device=DEV)
+    y = q2.q2_linear_a8(dev_bits(xb, torch.bfloat16), p, s, workspace=ws)
+    torch.cuda.synchronize()
+    off = (m * k * 2 + 255) // 256 * 256
+    codes = ws[:m * k * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(m, k)
+    scales = ws[off:off + 4 * m].view(torch.float32).cpu().numpy()
+    return y.cpu().numpy(), codes, scales
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (5, 300, 640), (16, 257, 1280), (17, 100, 256), (75, 200, 1408),
+                                   (200, 333, 384)])
+def test_a8_codes_and_product(m, n, k):
+    p, s, p_ref, s_ref = q2_weights(61, n, k)
+    xb = a8_inputs(61, m, k)
+    y, codes, scales = run_a8(xb, p, s, n)
+    q_ref, s8_ref = O.quantize_rows_a8(xb)
+    got = (codes.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(got, q_ref.astype(np.float32)), "codes"
+    assert np.array_equal(scales.view(np.uint32), s8_ref.view(np.uint32)), "row scales"
+    assert_close(y, O.q2_linear_a8(xb, p_ref, s_ref), f"a8 M={m} N={n} K={k}")
+
+
+A8_CFGS = ["kpair", "w48x192", "w64x128", "w32x64", "kg2x1x4", "kg4x2x2", "kg2x2x2", "kg6x3x2"]
+
+
+A8_PATHS = [(c, "1") for c in A8_CFGS + ["gemv"]] + [(c, "2") for c in A8_CFGS if c.startswith("kg")]
+
+
+@pytest.mark.parametrize("cfg,split", A8_PATHS)
+def test_a8_every_path(cfg, split, monkeypatch):
+    m, n, k = (8, 333, 1280) if cfg == "gemv" else (192, 333, 1280)
+    monkeypatch.setenv("Q2_FORCE_PATH", "gemv" if cfg == "gemv" else "gemm")
+    if cfg != "gemv":
+        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+        monkeypatch.setenv("Q2_GEMM_KSPLIT", split)
+    p, s, p_ref, s_ref = q2_weights(62, n, k)
+    xb = a8_inputs(62, m, k)
+    y, _, _ = run_a8(xb, p, s, n)
+    assert_close(y, O.q2_linear_a8(xb, p_ref, s_ref), f"a8 {cfg} split={split}")
+
+
+@pytest.mark.parametrize("m,k,n", [(1536, 3072, 9216), (384, 12288, 3072)])
+def test_a8_full_size_sampled(m, k, n):
+    p, s, p_ref, s_ref = q2_weights(63, n, k)
+    xb = a8_inputs(63, m, k)
+    y, _, _ = run_a8(xb, p, s, n)
+    cols = sample_cols(n, 96, seed=5)
+    q, sc = O.quantize_rows_a8(xb)
+    ref = sc.astype(np.float64)[:, None] * (q.astype(np.float64) @ O.unpack_q2(p_ref[cols], s_ref[cols]).T)
+    assert_close(y[:, cols], ref, f"a8 M={m} K={k} N={n} sampled")
+
+
+def test_a8_workspace_errors():
+    m, n, k = 4, 64, 256
+    p, s, _, _ = q2_weights(64, n, k)
+    x = dev_bits(a8_inputs(64, m, k), torch.bfloat16)
+    small = torch.zeros(q2.a8_workspace_bytes(m, k) - 1, dtype=torch.uint8, device=DEV)
+    with pytest.raises(q2.Q2Error) as e:
+        q2.q2_linear_a8(x, p, s, workspace=small)
+    assert e.value.status == q2.Q2_ERR_WORKSPACE

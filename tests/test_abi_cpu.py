@@ -127,6 +127,21 @@ def test_slice_argument_errors(lib):
     assert S(None, None, 8, 512, 0, 8, 256, 256, None, None, None) == q2.Q2_OK
 
 
+def test_a8_argument_errors(lib):
+    A8 = lib.q2_linear_a8
+    assert lib.q2_a8_workspace_bytes(0, 128) == 0 and lib.q2_a8_workspace_bytes(4, 0) == 0
+    assert lib.q2_a8_workspace_bytes(3, 128) == 768 + 256
+    assert lib.q2_a8_workspace_bytes(1536, 3072) == 1536 * 3072 * 2 + 1536 * 4 + 0
+    need = lib.q2_a8_workspace_bytes(16, 256)
+    assert A8(FAKE, FAKE, FAKE, FAKE, 16, 8, 100, FAKE, need, None) == q2.Q2_ERR_SHAPE
+    assert A8(FAKE, FAKE, FAKE, FAKE, 16, 8, 256, FAKE, need - 1, None) == q2.Q2_ERR_WORKSPACE
+    assert A8(FAKE, FAKE, FAKE, FAKE, 16, 8, 256, None, need, None) == q2.Q2_ERR_ARG
+    assert A8(FAKE, FAKE, FAKE, FAKE, 16, 8, 256, FAKE + 16, need, None) == q2.Q2_ERR_ALIGN
+    assert A8(FAKE + 8, FAKE, FAKE, FAKE, 16, 8, 256, FAKE, need, None) == q2.Q2_ERR_ALIGN
+    assert A8(None, FAKE, FAKE, FAKE, 16, 8, 256, FAKE, need, None) == q2.Q2_ERR_ARG
+    assert A8(None, FAKE, FAKE, None, 0, 8, 256, None, 0, None) == q2.Q2_OK
+
+
 def test_import_argument_errors(lib):
     I_ = lib.q2_import_gemlite
     bad = ctypes.c_int64(123)
