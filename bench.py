@@ -249,9 +249,10 @@ def main():
                     "print only the wall time (no graph, no per-call events)")
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
                     "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref")
-    ap.add_argument("--no-split", action="store_true", help="skip the split output projection measurement")
-    ap.add_argument("--no-quarter", action="store_true", help="skip the quarter-size first step measurement")
-    ap.add_argument("--no-a8", action="store_true", help="skip the 8-bit activation measurement")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time the split output projection, the quarter-size first step and the 8-bit "
+                         "activation linear (they launch the step's GEMM kernel at other shapes, so they stay out "
+                         "of the default run whose kernel trace backs the roofline figure)")
     ap.add_argument("--no-layer-list", action="store_true",
                     help="skip the 100-linear rank-32 layer list report")
     args = ap.parse_args()
@@ -396,9 +397,10 @@ def main():
         del g
 
     layer_list = None if (args.no_layer_list or args.only) else measure_layer_list(torch, q2, I, dev)
-    split_proj = None if (args.no_split or args.only) else measure_split_projection(torch, q2, I, dev)
-    quarter = None if (args.no_quarter or args.only) else measure_quarter_step(torch, q2, I, dev)
-    a8 = None if (args.no_a8 or args.only) else measure_a8(torch, q2, I, dev)
+    extras = args.extras and not args.only
+    split_proj = measure_split_projection(torch, q2, I, dev) if extras else None
+    quarter = measure_quarter_step(torch, q2, I, dev) if extras else None
+    a8 = measure_a8(torch, q2, I, dev) if extras else None
 
     parts = {}
     fam_time, fam_flops, fam_bytes = {}, {}, {}

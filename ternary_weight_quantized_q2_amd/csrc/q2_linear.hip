@@ -1994,10 +1994,20 @@ static int kgroup_group_rows(const LinearArgs& a, int bm, int tiles_m, int tiles
   return (tiles_m + best - 1) / best;
 }
 
-// y = 0 before a K-split GEMM adds its two parts into it.
+// y = 0 before a K-split GEMM adds its two parts into it: 16-byte stores
+// from the first 16-byte boundary of y on, single floats before it and after
+// the last whole piece.
 __global__ __launch_bounds__(256) void zero_y_kernel(float* y, int64_t count) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) y[i] = 0.0f;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t head = (int64_t)(((16u - (uint32_t)(reinterpret_cast<uintptr_t>(y) & 15u)) & 15u) >> 2);
+  head = head < count ? head : count;
+  const int64_t pieces = (count - head) >> 2;
+  q2_f32x4* v = reinterpret_cast<q2_f32x4*>(y + head);
+  for (int64_t i = t0; i < pieces; i += stride) v[i] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t tail = head + 4 * pieces;
+  if (t0 < head) y[t0] = 0.0f;
+  if (t0 < count - tail) y[tail + t0] = 0.0f;
 }
 
 // ksplit 2: the K blocks in two parts, each tile's two workgroups adding
@@ -2016,7 +2026,7 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, int ksplit, hipStream_t s
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (kpart > 0) {
     const int64_t count = a.M * a.N;
-    const int64_t blocks = std::min<int64_t>((count + 255) / 256, 4096);
+    const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 4096);
     hipLaunchKernelGGL(zero_y_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.y, count);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

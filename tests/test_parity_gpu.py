@@ -286,6 +286,21 @@ def _k_split_big_case(m, n, k):
     return _big[(m, n, k)]
 
 
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_k_split_unaligned_y(offset, monkeypatch):
+    # the zero fill before a split call covers y from any 4-byte position and touches nothing around it
+    m, n, k = 75, 201, 1408
+    (x, p, s, ref), _ = _cfg_case(m, n, k)
+    monkeypatch.setenv("Q2_GEMM_TILE", "kg2x2x2")
+    monkeypatch.setenv("Q2_GEMM_KSPLIT", "2")
+    flat = torch.full((m * n + 8,), float("nan"), device=DEV)
+    y = flat[offset:offset + m * n].view(m, n)
+    q2.q2_linear(x, p, s, y)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy(), ref, f"split, y at +{4 * offset} bytes")
+    assert torch.isnan(flat[:offset]).all() and torch.isnan(flat[offset + m * n:]).all()
+
+
 def test_forced_k_split_errors(monkeypatch):
     (x, p, s, _), _ = _cfg_case(75, 200, 1408)
     monkeypatch.setenv("Q2_GEMM_KSPLIT", "3")
