@@ -409,6 +409,44 @@ def test_determinism_and_guards():
         assert torch.equal(y, y2), "not bitwise reproducible"
 
 
+def _guarded(m, n):
+    guard = 16384
+    buf = torch.full((2 * guard + m * n,), float("nan"), device=DEV)
+    buf[:guard] = 1234.5
+    buf[-guard:] = -4321.5
+    return buf, buf[guard:guard + m * n].view(m, n), guard
+
+
+@pytest.mark.parametrize("entry", ["lowrank", "q4_split", "a8", "q2_split"])
+def test_determinism_and_guards_other_entry_points(entry):
+    # every output element written, nothing outside it touched, and a second call bitwise equal
+    if entry == "lowrank":
+        m, k, n, r = 1536, 3072, 3072, 32
+        p, s, _, _, _, x, _, _, A, B = lowrank_case(41, m, k, n, r)
+        call = lambda y: q2.q2_linear_lowrank(x, p, s, A, B, y=y)
+    elif entry == "q4_split":                       # long K over few tiles: the two-part K split
+        m, k, n = 128, 9728, 2560
+        _, _, _, _, x, P, S, Z = q4_case(42, m, k, n)
+        call = lambda y: q2.q4_linear(x, P, S, Z, y)
+    elif entry == "a8":
+        m, k, n = 1536, 3072, 3072
+        p, s, _, _ = q2_weights(43, n, k)
+        _, x = acts(43, m, k)
+        call = lambda y: q2.q2_linear_a8(x, p, s, y=y)
+    else:
+        m, k, n = 384, 12288, 3072
+        p, s, _, _ = q2_weights(44, n, k)
+        _, x = acts(44, m, k)
+        call = lambda y: q2.q2_linear(x, p, s, y)
+    buf, y, guard = _guarded(m, n)
+    call(y)
+    y2 = call(torch.empty((m, n), device=DEV))
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any(), "output not fully written"
+    assert torch.all(buf[:guard] == 1234.5) and torch.all(buf[-guard:] == -4321.5), "write outside y"
+    assert torch.equal(y, y2), "not bitwise reproducible"
+
+
 # ---------------------------------------------------------------------------
 # low-rank branch
 # ---------------------------------------------------------------------------
