@@ -64,6 +64,8 @@ def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_quantized_q2_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f == "peaks.hip":                       # the benchmark's own measurement kernels
+            continue
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
@@ -237,6 +239,49 @@ def measure_a8(torch, q2, I, dev, reps=20):
         tot_f += f
     return {"shape": f"M={m}", "tflops_a8": round(tot_f / tot_t / 1e12, 3),
             "tflops_bf16": round(tot_f / tot_b / 1e12, 3), "calls": out}
+
+
+def measure_peaks(torch, dev):
+    """This GPU's measured ceilings, reported beside the published ones: a
+    back-to-back bf16 16x16x32 MFMA loop (eight independent accumulators per
+    wave, 2048 workgroups of four waves) and a streaming read of a 4 GiB
+    buffer (16-byte loads, four in flight per thread).  Best of three
+    launches each; the kernels are in libq2_peaks.so (built with the library)."""
+    import ctypes
+    path = os.path.join(ROOT, "ternary_weight_quantized_q2_amd", "libq2_peaks.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.q2peak_mfma.argtypes = [p, ctypes.c_int, ctypes.c_int, p]
+    lib.q2peak_read.argtypes = [p, i64, p, ctypes.c_int, p]
+    lib.q2peak_mfma_chains.restype = ctypes.c_int
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def best(launch):
+        launch()
+        torch.cuda.synchronize()
+        t = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            t = min(t, e0.elapsed_time(e1) * 1e-3)
+        return t
+
+    blocks, iters = 2048, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    t = best(lambda: lib.q2peak_mfma(out.data_ptr(), blocks, iters, stream))
+    mfma = blocks * 4 * iters * lib.q2peak_mfma_chains() * 16384.0 / t / 1e12
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rblocks = 4096
+    outw = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
+    t = best(lambda: lib.q2peak_read(buf.data_ptr(), nbytes, outw.data_ptr(), rblocks, stream))
+    del buf
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(nbytes / t / 1e9, 1)}
 
 
 def main():
@@ -418,6 +463,7 @@ def main():
     gemm_ach = fam_flops["gemm_m1536"] / fam_time["gemm_m1536"] / 1e12 if "gemm_m1536" in fam_time else 0.0
     gemv_ach = fam_bytes["gemv_m1"] / fam_time["gemv_m1"] / 1e9 if "gemv_m1" in fam_time else 0.0
     traffic = measured_traffic()
+    peaks = None if args.only else measure_peaks(torch, dev)
     out = {
         "metric": "Q2_0 linear eff. TFLOP/s (M=1536) + packed-weight GB/s (M=1), % roofline",
         "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
@@ -449,6 +495,11 @@ def main():
         "m1_weight_gbs": round(gemv_ach, 2),
         "parts": parts,
     }
+    if peaks is not None:
+        # the same achieved rates against this GPU's measured ceilings (the published peaks stay the reference)
+        out["measured_peaks"] = peaks
+        out["roofline"]["frac_measured"] = round(gemm_ach / peaks["mfma_bf16_tflops"], 4)
+        out["roofline_gemv"]["frac_measured"] = round(gemv_ach / peaks["hbm_read_gbs"], 4)
     if layer_list is not None:
         out["layer_list"] = layer_list
     if split_proj is not None:

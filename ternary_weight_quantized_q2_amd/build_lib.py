@@ -39,9 +39,13 @@ def _compile(src):
     return obj, out
 
 
+PEAKS_SRC = os.path.join(CSRC, "peaks.hip")          # benchmark-only measurement kernels
+PEAKS_LIB = os.path.join(PKG, "libq2_peaks.so")
+
+
 def build(verbose=True, out=LIB, srcs=None):
     os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = srcs or sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = srcs or sorted(s for s in glob.glob(os.path.join(CSRC, "*.hip")) if s != PEAKS_SRC)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(_compile, srcs))
     for _, log in results:
@@ -60,5 +64,11 @@ def build(verbose=True, out=LIB, srcs=None):
     return out
 
 
+def build_peaks(verbose=True):
+    """The benchmark's peak-measurement kernels, as a library of their own."""
+    return build(verbose=verbose, out=PEAKS_LIB, srcs=[PEAKS_SRC])
+
+
 if __name__ == "__main__":
     build()
+    build_peaks()
