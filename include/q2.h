@@ -132,7 +132,8 @@ int q2_linear(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* sca
 /*
  * q2_lowrank_workspace_bytes - device bytes q2_linear_lowrank needs for M
  * rows and rank r: M * r * 4 rounded up to a multiple of 256 (0 when M or r
- * is 0).  Negative arguments give 0.
+ * is 0).  Negative arguments, and M or r beyond what the linear accepts
+ * (M > 2^46, r > 65535), give 0.
  */
 size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r);
 

@@ -217,7 +217,7 @@ int q2_linear_a8(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* 
 }
 
 size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r) {
-  if (M <= 0 || r <= 0) return 0;
+  if (M <= 0 || r <= 0 || M > ((int64_t)1 << 46) || r > 65535) return 0;   // outside what the linear accepts
   const size_t b = (size_t)M * (size_t)r * 4u;
   return (b + 255u) & ~(size_t)255u;
 }
