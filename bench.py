@@ -60,12 +60,13 @@ def _code_only(text):
     return " ".join("".join(out).split())
 
 
+KERNEL_SOURCES = ("q2_device.h", "q2_internal.h", "q2_linear.hip")   # the linear kernels and what they include
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_weight_quantized_q2_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f == "peaks.hip":                       # the benchmark's own measurement kernels
-            continue
+    for f in KERNEL_SOURCES:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
