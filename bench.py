@@ -285,6 +285,21 @@ def measure_peaks(torch, dev):
     return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(nbytes / t / 1e9, 1)}
 
 
+def measure_gemv_hot(torch, q2, I, dev, reps=200):
+    """The M = 1 GEMV on one weight copy called back to back, so the weights
+    come from the 256 MB Infinity Cache after the first call: a hot-cache
+    figure, labelled as such, beside the step's cold (rotated) one."""
+    out = {}
+    for k, n in I.GEMV_SHAPES:
+        p, s = q2.q2_pack(torch.from_numpy(I.q2_codes_fast(980, n, k)).to(dev),
+                          torch.from_numpy(I.q2_scales(980, n, k)).to(dev))
+        x = torch.from_numpy(I.activations_bf16(980, 1, k).view(np.int16)).to(dev).view(torch.bfloat16)
+        y = torch.empty((1, n), device=dev)
+        t = _best_graph_time(torch, lambda: q2.q2_linear(x, p, s, y=y), reps)
+        out[f"K={k} N={n}"] = {"us": round(t * 1e6, 3), "weight_gbs": round(Q2_BYTES_PER_WEIGHT * n * k / t / 1e9, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,9 +311,10 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
                     "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref")
     ap.add_argument("--extras", action="store_true",
-                    help="also time the split output projection, the quarter-size first step and the 8-bit "
-                         "activation linear (they launch the step's GEMM kernel at other shapes, so they stay out "
-                         "of the default run whose kernel trace backs the roofline figure)")
+                    help="also time the split output projection, the quarter-size first step, the 8-bit "
+                         "activation linear and the hot-cache GEMV (they launch the step's kernels at other shapes "
+                         "or on cached weights, so they stay out of the default run whose kernel trace backs the "
+                         "roofline figures)")
     ap.add_argument("--no-layer-list", action="store_true",
                     help="skip the 100-linear rank-32 layer list report")
     args = ap.parse_args()
@@ -447,6 +463,7 @@ def main():
     split_proj = measure_split_projection(torch, q2, I, dev) if extras else None
     quarter = measure_quarter_step(torch, q2, I, dev) if extras else None
     a8 = measure_a8(torch, q2, I, dev) if extras else None
+    gemv_hot = measure_gemv_hot(torch, q2, I, dev) if extras else None
 
     parts = {}
     fam_time, fam_flops, fam_bytes = {}, {}, {}
@@ -509,6 +526,8 @@ def main():
         out["quarter_step"] = quarter
     if a8 is not None:
         out["a8_linear"] = a8
+    if gemv_hot is not None:
+        out["gemv_m1_hot_cache"] = gemv_hot
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
