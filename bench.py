@@ -320,7 +320,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(sharding is described in DESIGN.md, not built).", file=sys.stderr)
+              "(how the linear would shard across GPUs is a design note only).", file=sys.stderr)
         sys.exit(2)
 
     import torch
