@@ -29,9 +29,8 @@ Sources (web pages on ternary-weight image models):
 * mindview-t2i-turbo model card, section "One step": the side branch is
   y = W x + B (A x).
 
-Readings where the pages leave a step open (each also listed in the design
-notes): consecutive codes share a byte (code k sits in bits 2(k%4)..2(k%4)+1
-of byte k//4); scales are a separate array [N, K/128] (structure-of-arrays);
+Readings where the pages leave a step open: consecutive codes share a byte
+(code k sits in bits 2(k%4)..2(k%4)+1 of byte k//4); scales are a separate array [N, K/128] (structure-of-arrays);
 code 3 is rejected by the packer; f32 -> f16 rounds to nearest even and
 non-finite scales are rejected; the 4-bit group is 128 with an f16 zero point
 in code units; the low-rank branch has no extra scale factor; outputs are
