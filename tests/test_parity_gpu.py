@@ -344,6 +344,48 @@ def test_scales_at_odd_halfword(m, n, k):
     assert_close(y4, O.q4_linear(xb4, p4, s4, z4), f"odd q4 scales M={m} N={n} K={k}")
 
 
+def _edge_weight(n, k, regime):
+    """Hand-made Q2_0 bytes and f16 scale bits: codes including 3 (outside the
+    format, decoded by the same formula) and scales of both signs in one of
+    three regimes: "mixed" (ordinary scales with zeros, subnormals and the
+    largest finite values interspersed), "subnormal" (every scale an f16
+    subnormal, so a flush to zero would show) and "large" (every scale within
+    a factor 2 of the largest finite f16)."""
+    codes = I.q2_codes(21, n, k)
+    codes[0, :40] = 3
+    codes[n - 1, k - 130:] = 3
+    c = codes.reshape(n, k // 4, 4).astype(np.uint32)
+    packed = (c[..., 0] | c[..., 1] << 2 | c[..., 2] << 4 | c[..., 3] << 6).astype(np.uint8)
+    rng = np.random.default_rng(23)
+    if regime == "subnormal":
+        sbits = rng.integers(1, 0x400, size=(n, k // 128)).astype(np.uint16)
+    elif regime == "large":
+        sbits = rng.integers(0x7800, 0x7C00, size=(n, k // 128)).astype(np.uint16)
+    else:
+        sbits = I.f32_to_f16_bits(I.q2_scales(21, n, k))
+        special = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x0400, 0x7BFF, 0xFBFF], np.uint16)
+        sbits.reshape(-1)[::7] = np.resize(special, sbits.reshape(-1)[::7].shape)
+    sbits[1::2] ^= 0x8000                                  # every other row of the opposite sign
+    return packed, sbits
+
+
+@pytest.mark.parametrize("regime", ["mixed", "subnormal", "large"])
+@pytest.mark.parametrize("cfg,m", [("gemv", 1), ("gemv", 13), ("auto", 96), ("kpair", 192), ("kg6x3x2", 100),
+                                   ("kg2x1x4r3", 40), ("w48x192", 75), ("kg2x2x4", 33)])
+def test_linear_scale_and_code_extremes(cfg, m, regime, monkeypatch):
+    n, k = 333, 1408
+    packed, sbits = _edge_weight(n, k, regime)
+    if cfg == "gemv":
+        monkeypatch.setenv("Q2_FORCE_PATH", "gemv")
+    elif cfg != "auto":
+        monkeypatch.setenv("Q2_FORCE_PATH", "gemm")
+        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+    xb, x = acts(22, m, k)
+    y = q2.q2_linear(x, dev_u8(packed), dev_bits(sbits, torch.float16)).cpu().numpy()
+    assert np.all(np.isfinite(y))
+    assert_close(y, O.q2_linear(xb, packed, sbits), f"{regime} scales and code 3, {cfg} M={m}")
+
+
 def test_linear_empty_and_k_zero():
     n = 40
     x = torch.empty((5, 0), dtype=torch.bfloat16, device=DEV)
