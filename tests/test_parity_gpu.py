@@ -601,3 +601,30 @@ def test_q4_full_shapes(k, n):
         assert_close(y, O.q4_linear(xb, p4, s, z), "q4 full")
     cols = sample_cols(n)
     assert_close(y[:, cols], O.q4_linear_cols(xb, p4, s, z, cols), f"q4 K={k} N={n} sampled")
+
+
+@pytest.mark.parametrize("regime", ["mixed", "subnormal", "large"])
+@pytest.mark.parametrize("cfg,m", [("gemv", 1), ("gemv", 11), ("auto", 128), ("kg4x2x2", 70), ("kg2x2x4", 33),
+                                   ("w48x192", 96)])
+def test_q4_scale_and_zero_extremes(cfg, m, regime, monkeypatch):
+    """4-bit weights with scales of both signs in the three regimes of the Q2_0
+    case, and zero points that are zero, negative, non-integer, f16
+    subnormals or far outside the code range (the accumulator start
+    -(1 + z/16) S then dominates the block sum)."""
+    n, k = 257, 1408
+    p4, _, _ = I.q4_weights(24, n, k)
+    _, sbits = _edge_weight(n, k, regime)
+    rng = np.random.default_rng(25)
+    z = rng.uniform(-16.0, 31.0, size=(n, k // 128)).astype(np.float32)
+    zbits = I.f32_to_f16_bits(z)
+    special = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x7BFF, 0xFBFF, 0x3C00, 0x4B80], np.uint16)
+    zbits.reshape(-1)[::5] = np.resize(special, zbits.reshape(-1)[::5].shape)
+    if cfg == "gemv":
+        monkeypatch.setenv("Q2_FORCE_PATH", "gemv")
+    elif cfg != "auto":
+        monkeypatch.setenv("Q2_FORCE_PATH", "gemm")
+        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+    xb, x = acts(26, m, k)
+    y = q2.q4_linear(x, dev_u8(p4), dev_bits(sbits, torch.float16), dev_bits(zbits, torch.float16)).cpu().numpy()
+    assert np.all(np.isfinite(y))
+    assert_close(y, O.q4_linear(xb, p4, sbits, zbits), f"4-bit {regime} scales, extreme zeros, {cfg} M={m}")
