@@ -628,3 +628,47 @@ def test_q4_scale_and_zero_extremes(cfg, m, regime, monkeypatch):
     y = q2.q4_linear(x, dev_u8(p4), dev_bits(sbits, torch.float16), dev_bits(zbits, torch.float16)).cpu().numpy()
     assert np.all(np.isfinite(y))
     assert_close(y, O.q4_linear(xb, p4, sbits, zbits), f"4-bit {regime} scales, extreme zeros, {cfg} M={m}")
+
+
+def _lowrank_regime(shape, regime, seed):
+    """f16 bits of one low-rank factor, with random signs: ordinary
+    N(0, 0.02) values, all f16 subnormals, or magnitudes in [32768, 65504],
+    within a factor 2 of the largest finite f16 (the branch then reaches
+    ~1e12, well inside fp32)."""
+    rng = np.random.default_rng(seed)
+    if regime == "subnormal":
+        b = rng.integers(1, 0x400, size=shape).astype(np.uint16)
+    elif regime == "large":
+        b = rng.integers(0x7800, 0x7C00, size=shape).astype(np.uint16)
+    else:
+        b = I.f32_to_f16_bits((rng.standard_normal(shape) * 0.02).astype(np.float32))
+    return b ^ (rng.integers(0, 2, size=shape).astype(np.uint16) << 15)
+
+
+@pytest.mark.parametrize("regime", ["ordinary", "subnormal", "large"])
+@pytest.mark.parametrize("cfg,m,r", [("gemv", 3, 32), ("gemv", 16, 5), ("auto", 192, 32), ("kpair", 96, 64),
+                                     ("w48x192", 75, 32), ("w64x128", 40, 8), ("w32x64", 33, 5)])
+def test_lowrank_branch_alone_extremes(cfg, m, r, regime, monkeypatch):
+    """Zero block scales, so W = 0 exactly and y is the branch (x A^T) B^T
+    alone, with the factors in the three regimes; the branch's bf16 limb
+    arithmetic is then the whole result.  (All codes 1 would not isolate it:
+    the kernels' block sums of x (1 + 1/4) and their start value -1.25 S
+    round in different orders, which leaves fp32 noise of the size of x d,
+    above the subnormal-regime branch.)"""
+    n, k = 300, 640
+    codes = I.q2_codes(27, n, k)
+    scales = np.zeros((n, k // 128), np.float32)
+    p = q2.q2_pack(dev_u8(codes), torch.from_numpy(scales).to(DEV))
+    p_ref, s_ref = O.pack_q2(codes, scales)
+    a = _lowrank_regime((r, k), regime, 28)
+    b = _lowrank_regime((n, r), regime, 29)
+    if cfg == "gemv":
+        monkeypatch.setenv("Q2_FORCE_PATH", "gemv")
+    elif cfg != "auto":
+        monkeypatch.setenv("Q2_FORCE_PATH", "gemm")
+        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+    xb, x = acts(30, m, k)
+    y = q2.q2_linear_lowrank(x, p[0], p[1], dev_bits(a, torch.float16), dev_bits(b, torch.float16)).cpu().numpy()
+    ref = O.q2_linear_lowrank(xb, p_ref, s_ref, a, b)
+    assert np.all(np.isfinite(y)) and np.any(ref != 0)
+    assert_close(y, ref, f"low-rank branch alone, {regime} factors, {cfg} M={m} r={r}")
