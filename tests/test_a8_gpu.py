@@ -96,3 +96,41 @@ def test_a8_workspace_errors():
     with pytest.raises(q2.Q2Error) as e:
         q2.q2_linear_a8(x, p, s, workspace=small)
     assert e.value.status == q2.Q2_ERR_WORKSPACE
+
+
+def _extreme_rows(k):
+    """bf16 rows at the ends of the 8-bit quantiser's range: ordinary values,
+    a row scaled by 1e-30, bf16 subnormals only (the row scale is then an
+    fp32 subnormal), values near the bf16 maximum, halves that land exactly on
+    rounding ties once divided by s = 1, a constant row and a zero row."""
+    g = np.random.default_rng(31)
+    x = np.zeros((7, k), np.float32)
+    x[0] = g.standard_normal(k)
+    x[1] = g.standard_normal(k) * np.float32(1e-30)
+    sub = g.integers(0, 128, size=k).astype(np.uint32) | (g.integers(0, 2, size=k).astype(np.uint32) << 15)
+    x[2] = (sub << 16).view(np.float32)                     # bf16 subnormals: exponent field 0, random signs
+    x[3] = g.standard_normal(k) * np.float32(1e37)
+    x[4] = g.integers(-254, 255, size=k).astype(np.float32) / 2
+    x[4, 0] = 127.0                                          # amax 127, so s = 1 and x / s keeps the halves
+    x[5] = 3.0
+    return I.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("cfg", ["gemv", "gemm"])
+def test_a8_extreme_rows(cfg, monkeypatch):
+    n, k = 200, 640
+    monkeypatch.setenv("Q2_FORCE_PATH", cfg)
+    if cfg == "gemm":
+        monkeypatch.setenv("Q2_GEMM_TILE", "kg2x1x4")
+    p, s, p_ref, s_ref = q2_weights(65, n, k)
+    xb = _extreme_rows(k)
+    y, codes, scales = run_a8(xb, p, s, n)
+    q_ref, s8_ref = O.quantize_rows_a8(xb)
+    assert s8_ref[2] > 0 and s8_ref[2] < np.finfo(np.float32).tiny      # the subnormal-scale row is exercised
+    got = (codes.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(got, q_ref.astype(np.float32)), "codes"
+    assert np.array_equal(scales.view(np.uint32), s8_ref.view(np.uint32)), "row scales"
+    ref = O.q2_linear_a8(xb, p_ref, s_ref)
+    rows = [0, 1, 3, 4, 5, 6]                                # row 2's outputs are fp32 subnormals
+    assert_close(y[rows], ref[rows], f"a8 extreme rows {cfg}")
+    assert not y[6].any()
