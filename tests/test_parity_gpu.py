@@ -672,3 +672,18 @@ def test_lowrank_branch_alone_extremes(cfg, m, r, regime, monkeypatch):
     ref = O.q2_linear_lowrank(xb, p_ref, s_ref, a, b)
     assert np.all(np.isfinite(y)) and np.any(ref != 0)
     assert_close(y, ref, f"low-rank branch alone, {regime} factors, {cfg} M={m} r={r}")
+
+
+@pytest.mark.parametrize("m,n,k", [(65536, 64, 128), (1, 1 << 20, 128), (40, 300000, 256), (3000, 7, 384)])
+def test_large_grids(m, n, k):
+    """Far more workgroups than the benchmark shapes launch: many row tiles
+    with few columns, 2^16 GEMV workgroups, 2^14 column tiles; Q2_0 and
+    4-bit, sampled columns where N is large."""
+    p_dev, s_dev, p_ref, s_ref = q2_weights(33, n, k)
+    xb, x = acts(33, m, k)
+    y = q2.q2_linear(x, p_dev, s_dev).cpu().numpy()
+    cols = sample_cols(n, 256, seed=3) if n > 4096 else np.arange(n)
+    assert_close(y[:, cols], O.q2_linear_cols(xb, p_ref, s_ref, cols), f"Q2_0 M={m} N={n} K={k}")
+    p4, s4, z4, xb4, x4, P, S, Z = q4_case(34, m, k, n)
+    y4 = q2.q4_linear(x4, P, S, Z).cpu().numpy()
+    assert_close(y4[:, cols], O.q4_linear_cols(xb4, p4, s4, z4, cols), f"4-bit M={m} N={n} K={k}")
