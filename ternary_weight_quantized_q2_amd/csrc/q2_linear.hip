@@ -5,12 +5,14 @@
 // magic-number OR, and 16x16x32 bf16 MFMAs accumulate each 128-wide block
 // from a start value of -1.25 (or -(1 + z/16)) times the block's row sums,
 // after which one FMA per output applies the block's f16 scale.
-//  * gemm_kpair_kernel (M a multiple of 96, enough 96 x 192 tiles): eight
-//    waves, the two on each SIMD taking alternate K blocks of the same output
-//    columns; partial sums added once at the end.  Also carries the rank-r
-//    branch in its epilogue.
-//  * gemm_kgroup_kernel (smaller and ragged M): the same idea for KG groups of
-//    four waves and 16 MT x 64 NT tiles.
+//  * gemm_kpair_kernel (the rank-r branch at M a multiple of 96 with enough
+//    96 x 192 tiles): eight waves, the two on each SIMD taking alternate K
+//    blocks of the same output columns; partial sums added once at the end,
+//    the branch in its epilogue.
+//  * gemm_kgroup_kernel (the linear without the branch, from a few rows to the
+//    largest M, any raggedness): the same idea for KG groups of four waves and
+//    16 MT x 64 NT tiles, in XCD-contiguous tile order, optionally with the K
+//    blocks split over two workgroups.
 //  * gemm_kernel (the low-rank branch outside the K-pair kernel's reach, narrow
 //    mid-size outputs): four waves splitting N, one block per barrier.
 //  * gemv_kernel (M <= 16): a workgroup owns 16 weight rows; its waves split
