@@ -2113,11 +2113,9 @@ static int gemm_auto_cfg(const LinearArgs& a) {
   }
   // Otherwise prefer the largest tile that still gives a few waves of
   // workgroups over the 256 compute units.
-#ifndef Q2_NO_KPAIR
   // Eight-wave 96 x 192 tiles when they fill the chip and M is a whole number
   // of tiles (the low-rank branch only in its LDS-staged form).
   if (a.M % 96 == 0 && tiles(96, 192) >= 256 && (a.r == 0 || lr_lds)) return CFG_KPAIR;
-#endif
   // 48 x 192 tiles run two workgroups (eight waves) per CU; with the low-rank
   // operands staged in LDS the tile no longer fits twice, so that case keeps 96 x 192.
   if (!lr_lds && a.M >= 48 && tiles(48, 192) >= 512) return CFG_W48x192;
