@@ -248,3 +248,44 @@ def test_import_errors_match_the_oracle():
             _import_dev(ct_, st_, zt_, group)
         assert e.value.status == status
         assert e.value.bad_index == ref.value.index
+
+
+# ---------------------------------------------------------------------------
+# every entry point runs on the caller's stream
+# ---------------------------------------------------------------------------
+
+def test_calls_run_on_the_callers_stream():
+    """A side stream is kept busy, then the input is written on it and each
+    entry point is called on it: a launch on any other stream would read the
+    input before it is written.  Results equal the same calls on the default
+    stream, bit for bit (every call is deterministic)."""
+    k, n = 1280, 333
+    p, s, _, _ = q2_weights(47, n, k)
+    p4, s4, z4 = I.q4_weights(47, n, k)
+    P4 = torch.from_numpy(p4).to(DEV)
+    S4, Z4 = dev_bits(s4, torch.float16), dev_bits(z4, torch.float16)
+    a, b = I.lowrank_factors(47, 32, k, n, std=0.02)
+    A, B = dev_bits(a, torch.float16), dev_bits(b, torch.float16)
+    calls = {
+        "gemm": lambda x: q2.q2_linear(x, p, s),
+        "lowrank": lambda x: q2.q2_linear_lowrank(x, p, s, A, B),
+        "q4": lambda x: q2.q4_linear(x, P4, S4, Z4),
+        "a8": lambda x: q2.q2_linear_a8(x, p, s),
+        "accumulate": lambda x: q2.q2_linear_ex(x, p, s, y=torch.ones((x.shape[0], n), device=DEV), accumulate=True),
+    }
+    side = torch.cuda.Stream()
+    for m in (200, 5):                                   # the GEMM and the GEMV paths
+        _, x = acts(48, m, k)
+        refs = {name: fn(x) for name, fn in calls.items()}
+        torch.cuda.synchronize()
+        for name, fn in calls.items():
+            x_late = torch.zeros_like(x)
+            busy = torch.randn(2048, 2048, device=DEV)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(side):
+                for _ in range(30):
+                    busy = (busy @ busy) * 1e-3
+                x_late.copy_(x)
+                y = fn(x_late)
+            side.synchronize()
+            assert torch.equal(y, refs[name]), f"{name} M={m}"
