@@ -289,3 +289,59 @@ def test_calls_run_on_the_callers_stream():
                 y = fn(x_late)
             side.synchronize()
             assert torch.equal(y, refs[name]), f"{name} M={m}"
+
+
+# ---------------------------------------------------------------------------
+# captured in a HIP graph, replayed with eager work in between
+# ---------------------------------------------------------------------------
+
+def test_graph_replays_match_eager():
+    """Each entry point is captured once into a graph (static input, output
+    and workspace buffers) and replayed three times; before each replay new
+    activations are written eagerly, and after it the replay's output must
+    equal an eager call on the same input, bit for bit.  The split case
+    captures the zero fill and the two atomic parts of the K split."""
+    def q2w(cfg, n, k):
+        p, s, _, _ = q2_weights(cfg, n, k)
+        return p, s
+
+    cases = []
+    p, s = q2w(51, 384, 12288)                          # long K over few tiles: K split
+    cases.append(("split", 128, 12288, 384, lambda x, y, ws: q2.q2_linear(x, p, s, y), 0))
+    p2, s2 = q2w(52, 333, 1280)
+    cases.append(("gemm", 200, 1280, 333, lambda x, y, ws: q2.q2_linear(x, p2, s2, y), 0))
+    cases.append(("gemv", 3, 1280, 333, lambda x, y, ws: q2.q2_linear(x, p2, s2, y), 0))
+    a, b = I.lowrank_factors(53, 32, 1280, 333, std=0.02)
+    A, B = dev_bits(a, torch.float16), dev_bits(b, torch.float16)
+    cases.append(("lowrank", 192, 1280, 333,
+                  lambda x, y, ws: q2.q2_linear_lowrank(x, p2, s2, A, B, y=y, workspace=ws),
+                  q2.lowrank_workspace_bytes(192, 32)))
+    cases.append(("a8", 100, 1280, 333, lambda x, y, ws: q2.q2_linear_a8(x, p2, s2, y=y, workspace=ws),
+                  q2.a8_workspace_bytes(100, 1280)))
+    p4, s4, z4 = I.q4_weights(54, 333, 1280)
+    P4, S4, Z4 = torch.from_numpy(p4).to(DEV), dev_bits(s4, torch.float16), dev_bits(z4, torch.float16)
+    cases.append(("q4", 64, 1280, 333, lambda x, y, ws: q2.q4_linear(x, P4, S4, Z4, y), 0))
+
+    for name, m, k, n, fn, wsb in cases:
+        x = torch.empty((m, k), dtype=torch.bfloat16, device=DEV)
+        y = torch.empty((m, n), device=DEV)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+        _, x0 = acts(55, m, k)
+        x.copy_(x0)
+        fn(x, y, ws)                                       # warm-up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(x, y, ws)
+        torch.cuda.synchronize()
+        y_e = torch.empty_like(y)
+        ws_e = torch.empty_like(ws)
+        for rep in range(3):
+            _, xr = acts(56 + rep, m, k)
+            x.copy_(xr)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            fn(x, y_e, ws_e)
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_e), f"{name} replay {rep}"
