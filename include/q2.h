@@ -20,9 +20,10 @@
  *    zeros (an empty sum), or leaves y as it is under Q2_ACCUMULATE.
  *    Pointers to buffers of zero bytes may be NULL.
  *  - All array pointers are device pointers; all arrays are dense row-major.
- *    The caller owns every buffer; the library keeps no state between calls
- *    except a per-device architecture check, and is safe to call from several
- *    host threads.
+ *    The caller owns every buffer and the library allocates no device memory.
+ *    It keeps no state between calls except a per-device architecture check,
+ *    the load-time error flags (see q2_pack) and the test control of
+ *    q2_set_dispatch, and is safe to call from several host threads.
  *  - x, the packed codes, the q2_pack codes and the low-rank factor A must be
  *    16-byte aligned; every other array must be aligned to its element size;
  *    the low-rank workspace to 256 bytes.
@@ -76,9 +77,11 @@ typedef enum {
  *   scales_f16 u16 [N, K/128]: f16 bits of scales, nearest-even  (out)
  *   bad_index  host int64*, may be NULL: on Q2_ERR_CODE / Q2_ERR_SCALE, the
  *              flat row-major index of the first bad code / scale; -1 on success.
- * Codes are checked before scales.  Synchronizes `stream`, and allocates and
- * frees a 16-byte device buffer for the two error flags.  The outputs are
- * fully written even when an error is returned, but must not be used then.
+ * Codes are checked before scales.  Synchronizes `stream`.  Allocates
+ * nothing: the error flags live in a small file-scope device array (one per
+ * device), so q2_pack and q2_import_gemlite calls of one process run one at
+ * a time (a host lock).  The outputs are fully written even when an error is
+ * returned, but must not be used then.
  */
 int q2_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K,
             uint8_t* packed, uint16_t* scales_f16, int64_t* bad_index, hipStream_t stream);
@@ -105,9 +108,9 @@ int q2_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K,
  * Checked, and reported in this order: a code 3 (Q2_ERR_CODE); a zero that
  * is not exactly -scale (Q2_ERR_FORMAT); a scale that is not a finite exact
  * f16 value, then a group whose scale differs from its block's first group
- * when G < 128 (Q2_ERR_SCALE).  Synchronizes `stream`, and allocates and
- * frees a 32-byte device buffer for the flags.  The outputs must not be used
- * after an error.
+ * when G < 128 (Q2_ERR_SCALE).  Synchronizes `stream`; allocates nothing
+ * and shares q2_pack's device flags and host lock.  The outputs must not be
+ * used after an error.
  */
 int q2_import_gemlite(const uint8_t* codes_t, const float* scales_t, const float* zeros_t,
                       int64_t N, int64_t K, int64_t G, uint8_t* packed, uint16_t* scales_f16,
@@ -254,6 +257,24 @@ int q4_linear(const uint16_t* x_bf16, const uint8_t* packed4, const uint16_t* sc
  */
 int q2_dequant(const uint8_t* packed, const uint16_t* scales_f16, float* w,
                int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * q2_set_dispatch - test and profiling control of the launch choice, for the
+ * whole process; not needed for correct use.  path: NULL, "" or "auto"
+ * (M <= 16 runs the GEMV, larger M the GEMM), "gemv" (the GEMV whenever
+ * M <= 16) or "gemm" (always the GEMM).  tile: NULL or "" for the automatic
+ * GEMM configuration, else a configuration name (kpair, w48x192, w96x192,
+ * w64x128, w32x128, w32x64, kg2x1x4, kg4x2x2, kg2x1x2, kg2x2x4, kg2x2x2,
+ * kg2x1x4r3, kg6x3x2); a forced configuration that cannot take a call's
+ * shape makes that call fail with Q2_ERR_HIP.  ksplit: 0 automatic, 1 the
+ * whole K in one workgroup, 2 the K blocks in two parts (K-group
+ * configurations of non-accumulating calls only, else Q2_ERR_HIP at the
+ * call).  An unknown name or value gives Q2_ERR_ARG and changes nothing.
+ * The environment variables Q2_FORCE_PATH, Q2_GEMM_TILE and Q2_GEMM_KSPLIT
+ * (same values) are read once, at the first linear call, as the initial
+ * setting.  Results never depend on it beyond fp32 summation order.
+ */
+int q2_set_dispatch(const char* path, const char* tile, int ksplit);
 
 /* q2_strerror - static name of a status code; never NULL. */
 const char* q2_strerror(int status);

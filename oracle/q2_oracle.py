@@ -6,7 +6,7 @@ definition of what the HIP library computes.  Only the test suite, the smoke
 check and the CPU-baseline leg of the benchmark may import it; the library and
 its Python binding never do, and the two share no code.
 
-Everything is NumPy float64 (or exact Python integers/fractions in the scalar
+Everything is NumPy float64 (or exact Python integers in the scalar
 helpers).  Every decoded value below is exact in float64: bf16 and f16 values
 are exact, a bf16 x f16 product has at most 8 + 11 significant bits, and the
 4-bit dequantised weight (q - z) * s is computed exactly from f16 inputs.  The
@@ -39,7 +39,6 @@ float32 on the GPU and float64 here.
 from __future__ import annotations
 
 import math
-from fractions import Fraction
 
 import numpy as np
 
@@ -372,17 +371,6 @@ def q4_linear(x_bits, packed4, scale_bits, zero_bits) -> np.ndarray:
 def q4_linear_cols(x_bits, packed4, scale_bits, zero_bits, cols) -> np.ndarray:
     cols = np.asarray(cols)
     return bf16_to_f64(x_bits) @ unpack_q4(packed4[cols], scale_bits[cols], zero_bits[cols]).T
-
-
-# ---------------------------------------------------------------------------
-# Exact rational evaluation (brute force for tiny inputs)
-# ---------------------------------------------------------------------------
-
-def exact_linear(x_rows, w_rows):
-    """y[m][n] = sum_k x[m][k] * w[n][k] with Fractions (inputs are floats)."""
-    xs = [[Fraction(v) for v in row] for row in x_rows]
-    ws = [[Fraction(v) for v in row] for row in w_rows]
-    return [[sum((a * b for a, b in zip(xr, wr)), Fraction(0)) for wr in ws] for xr in xs]
 
 
 # ---------------------------------------------------------------------------

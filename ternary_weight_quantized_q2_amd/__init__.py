@@ -30,7 +30,7 @@ Q2_ACCUMULATE = 0x1      # q2_linear_ex flag: y += result
 
 EXPORTS = ("q2_pack", "q2_import_gemlite", "q2_linear", "q2_lowrank_workspace_bytes", "q2_linear_lowrank", "q2_linear_ex", "q2_slice",
            "q2_a8_workspace_bytes", "q2_linear_a8",
-           "q4_linear", "q2_dequant", "q2_strerror", "q2_last_error")
+           "q4_linear", "q2_dequant", "q2_set_dispatch", "q2_strerror", "q2_last_error")
 
 _lib = None
 
@@ -64,6 +64,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "q2_linear_a8": ([p, p, p, p, i64, i64, i64, p, sz, p], ctypes.c_int),
         "q4_linear": ([p, p, p, p, p, i64, i64, i64, p], ctypes.c_int),
         "q2_dequant": ([p, p, p, i64, i64, p], ctypes.c_int),
+        "q2_set_dispatch": ([ctypes.c_char_p, ctypes.c_char_p, ctypes.c_int], ctypes.c_int),
         "q2_strerror": ([ctypes.c_int], ctypes.c_char_p),
         "q2_last_error": ([], ctypes.c_char_p),
     }
@@ -281,3 +282,11 @@ def q2_dequant(packed, scales, w=None) -> torch.Tensor:
         w = torch.empty((n, k), dtype=torch.float32, device=packed.device)
     _check(lib.q2_dequant(_ptr(packed), _ptr(scales), _ptr(w), n, k, _stream()))
     return w
+
+
+def set_dispatch(path: str | None = None, tile: str | None = None, ksplit: int = 0) -> None:
+    """Test / profiling control of the launch choice for the whole process (q2_set_dispatch): path None,
+    "auto", "gemv" or "gemm"; tile None or a GEMM configuration name; ksplit 0 (automatic), 1 or 2."""
+    lib = load()
+    _check(lib.q2_set_dispatch(None if path is None else path.encode(), None if tile is None else tile.encode(),
+                               int(ksplit)))

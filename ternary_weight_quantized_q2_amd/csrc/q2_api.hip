@@ -2,6 +2,7 @@
 // Every argument check runs before the first HIP call, so a host without a GPU
 // still gets argument, shape and alignment errors.
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -56,6 +57,7 @@ int check_linear_k(int64_t K) {
 }
 
 std::atomic<int> g_arch_ok[64];
+std::mutex g_check_lock;              // q2_pack and q2_import_gemlite share the device's error flags
 
 int check_device() {
   int dev = 0;
@@ -81,31 +83,44 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// Test-only override of the M <= 16 dispatch: Q2_FORCE_PATH=gemv|gemm.
-int forced_path() {
-  const char* v = std::getenv("Q2_FORCE_PATH");
-  if (v == nullptr) return 0;
+// Test and profiling control of the launch choice: the path (0 automatic,
+// 1 GEMV, 2 GEMM), a GEMM configuration (0 automatic, else its number, -1 an
+// unknown name) and the K split (0 automatic, 1 or 2, -1 anything else).  The
+// environment (Q2_FORCE_PATH=gemv|gemm, Q2_GEMM_TILE=<name>,
+// Q2_GEMM_KSPLIT=1|2) is read once per process, at the first linear call;
+// q2_set_dispatch replaces it.  The hot path only loads three integers.
+struct Dispatch {
+  std::atomic<int> path{0}, cfg{0}, ksplit{0};
+};
+Dispatch g_dispatch;
+std::once_flag g_dispatch_env;
+
+int parse_path(const char* v) {
+  if (v == nullptr || *v == 0 || std::strcmp(v, "auto") == 0) return 0;
   if (std::strcmp(v, "gemv") == 0) return 1;
   if (std::strcmp(v, "gemm") == 0) return 2;
-  return 0;
+  return -1;
 }
 
-// Test-only override of the GEMM kernel configuration: Q2_GEMM_TILE=<name>
-// (-1 for an unknown name).
-int forced_cfg() {
-  const char* v = std::getenv("Q2_GEMM_TILE");
+int parse_cfg(const char* v) {
   if (v == nullptr || *v == 0) return 0;
   return q2dev::gemm_config_id(v);
 }
 
-// Test-only override of the K split: Q2_GEMM_KSPLIT=1|2 (0 = automatic, -1
-// for anything else).
-int forced_ksplit() {
-  const char* v = std::getenv("Q2_GEMM_KSPLIT");
+int parse_ksplit(const char* v) {
   if (v == nullptr || *v == 0) return 0;
   if (std::strcmp(v, "1") == 0) return 1;
   if (std::strcmp(v, "2") == 0) return 2;
   return -1;
+}
+
+void read_dispatch_env() {
+  std::call_once(g_dispatch_env, [] {
+    const int p = parse_path(std::getenv("Q2_FORCE_PATH"));
+    g_dispatch.path.store(p < 0 ? 0 : p);
+    g_dispatch.cfg.store(parse_cfg(std::getenv("Q2_GEMM_TILE")));
+    g_dispatch.ksplit.store(parse_ksplit(std::getenv("Q2_GEMM_KSPLIT")));
+  });
 }
 
 int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* s, const uint16_t* z, float* y,
@@ -117,11 +132,12 @@ int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* 
   a.lr_t = lr_t; a.lr_b = lr_b; a.r = (int)r;
   a.acc = accumulate ? 1 : 0;
   a.row_scale = row_scale;
-  int path = forced_path();
+  read_dispatch_env();
+  int path = g_dispatch.path.load(std::memory_order_relaxed);
   if (path == 1 && M > 16) path = 0;
-  const int cfg = forced_cfg();
+  const int cfg = g_dispatch.cfg.load(std::memory_order_relaxed);
   if (cfg < 0) return fail(Q2_ERR_ARG, "unknown Q2_GEMM_TILE configuration");
-  const int ks = forced_ksplit();
+  const int ks = g_dispatch.ksplit.load(std::memory_order_relaxed);
   if (ks < 0) return fail(Q2_ERR_ARG, "Q2_GEMM_KSPLIT must be 1 or 2");
   return hip_status(q2dev::launch_linear(a, fmt, path, cfg, ks, stream),
                     fmt == 0 ? "q2 linear launch" : "q4 linear launch");
@@ -184,6 +200,18 @@ const char* q2_strerror(int status) {
 
 const char* q2_last_error(void) { return g_detail; }
 
+int q2_set_dispatch(const char* path, const char* tile, int ksplit) {
+  read_dispatch_env();
+  const int p = parse_path(path), c = parse_cfg(tile);
+  if (p < 0) return fail(Q2_ERR_ARG, "path must be NULL, \"auto\", \"gemv\" or \"gemm\"");
+  if (c < 0) return fail(Q2_ERR_ARG, "unknown GEMM configuration \"%s\"", tile);
+  if (ksplit < 0 || ksplit > 2) return fail(Q2_ERR_ARG, "ksplit must be 0 (automatic), 1 or 2");
+  g_dispatch.path.store(p);
+  g_dispatch.cfg.store(c);
+  g_dispatch.ksplit.store(ksplit);
+  return ok();
+}
+
 size_t q2_a8_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || M > ((int64_t)1 << 40) / K) return 0;
   const size_t codes = ((size_t)M * (size_t)K * 2u + 255u) & ~(size_t)255u;
@@ -234,17 +262,17 @@ int q2_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K, uin
   if (!ne) return ok();
   if ((st = check_device())) return st;
 
+  // One pack or import at a time per process: they share the device's flags.
+  std::lock_guard<std::mutex> serial(g_check_lock);
   unsigned long long* flags = nullptr;
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&flags), 2 * sizeof(unsigned long long));
-  if (e != hipSuccess) return hip_status(e, "hipMalloc(pack flags)");
+  hipError_t e = q2dev::check_flags(&flags);
+  if (e != hipSuccess) return hip_status(e, "q2_pack flags");
   unsigned long long host[2] = {~0ull, ~0ull};
   e = hipMemsetAsync(flags, 0xFF, sizeof host, stream);
   if (e == hipSuccess) e = q2dev::launch_pack(codes, scales, N, K, packed, scales_f16, flags, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(host, flags, sizeof host, hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  hipError_t ef = hipFree(flags);
   if (e != hipSuccess) return hip_status(e, "q2_pack");
-  if (ef != hipSuccess) return hip_status(ef, "hipFree(pack flags)");
   if (host[0] != ~0ull) {
     if (bad_index) *bad_index = (int64_t)host[0];
     return fail(Q2_ERR_CODE, "code above 2 at flat index %llu", host[0]);
@@ -305,17 +333,16 @@ int q2_import_gemlite(const uint8_t* codes_t, const float* scales_t, const float
   if (!ne) return ok();
   if ((st = check_device())) return st;
 
+  std::lock_guard<std::mutex> serial(g_check_lock);
   unsigned long long* flags = nullptr;
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&flags), 4 * sizeof(unsigned long long));
-  if (e != hipSuccess) return hip_status(e, "hipMalloc(import flags)");
+  hipError_t e = q2dev::check_flags(&flags);
+  if (e != hipSuccess) return hip_status(e, "q2_import_gemlite flags");
   unsigned long long host[4] = {~0ull, ~0ull, ~0ull, ~0ull};
   e = hipMemsetAsync(flags, 0xFF, sizeof host, stream);
   if (e == hipSuccess) e = q2dev::launch_import(codes_t, scales_t, zeros_t, N, K, G, packed, scales_f16, flags, stream);
   if (e == hipSuccess) e = hipMemcpyAsync(host, flags, sizeof host, hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  hipError_t ef = hipFree(flags);
   if (e != hipSuccess) return hip_status(e, "q2_import_gemlite");
-  if (ef != hipSuccess) return hip_status(ef, "hipFree(import flags)");
   // Reported in the order codes, zero points, scale values, block agreement.
   if (host[0] != ~0ull) {
     if (bad_index) *bad_index = (int64_t)host[0];

@@ -17,6 +17,13 @@
 // sum x (q - 1) / 4 exactly in real arithmetic; the 4-bit path starts it at
 // -(1 + z/16) * sum(x) and ends at sum x (q - z) / 16.
 //
+// The offset start is exact in real arithmetic but not in fp32: the two sums
+// round in different orders, so a block whose weights are all zero would leave
+// rounding noise of the size of ulp(1.25 |S|).  Every kernel therefore tests
+// each (weight row, block) for an all-zero block -- every 2-bit code equal to
+// 1, or every 4-bit code equal to an integer zero point -- and applies a scale
+// of 0 to it, so such a block adds exactly nothing (column_all below).
+//
 // Two pair orders are used.  Strided pairs (GEMV): because a dword's two
 // halves are 16 bits apart, one shift and one and-or make a 2-bit pair of codes
 // (j, j+8) of the dword's 16 codes, or a 4-bit pair of codes (j, j+4) of its 8;
@@ -224,6 +231,51 @@ __device__ __forceinline__ float bf16_sum16(const uint32_t nx[8]) {
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// ---- all-zero blocks ---------------------------------------------------------
+// In the matrix-core layout the four lanes c, c + 16, c + 32, c + 48 hold the
+// codes of one weight row (column c) of a 128-weight block between them.  The
+// lane verdicts below are wave masks (one bit per lane, straight from the
+// vector compares); column_all turns one into the mask whose bit l is set when
+// all four lanes of column l % 16 said yes.  The folding runs on the scalar
+// unit; the caller applies the mask with one v_cndmask per value.
+__device__ __forceinline__ uint64_t column_all(uint64_t b) {
+  uint64_t f = b & (b >> 16);
+  f &= f >> 32;                        // bit c: lanes c, c+16, c+32, c+48 all set
+  f &= 0xFFFFull;
+  f |= f << 16;
+  f |= f << 32;                        // replicated to every lane group
+  return f;
+}
+
+// Lanes whose part of the block is all zero weights.  2-bit: every code is 1
+// (bytes 0x55).  4-bit: every nibble equals the zero point z, which then has to
+// be an integer in 0..15 (a zero point that is not an integer leaves no
+// weight of the block at zero).
+template <int DW>
+__device__ __forceinline__ uint64_t q2_part_zero(const uint32_t (&w)[DW]) {
+  uint64_t m = __builtin_amdgcn_ballot_w64(w[0] == 0x55555555u);
+#pragma unroll
+  for (int i = 1; i < DW; ++i) m &= __builtin_amdgcn_ballot_w64(w[i] == 0x55555555u);
+  return m;
+}
+template <int DW>
+__device__ __forceinline__ uint64_t q4_part_zero(const uint32_t (&w)[DW], float z) {
+  // v = z when z is an integer in 0..15 (NaN clamps to 0 and then fails the compare).
+  const uint32_t v = (uint32_t)__builtin_fminf(__builtin_fmaxf(z, 0.f), 15.f);
+  const uint32_t pat = __builtin_amdgcn_perm(0u, v | (v << 4), 0x00000000u);   // the nibble in all eight places
+  uint64_t m = __builtin_amdgcn_ballot_w64((float)v == z);
+#pragma unroll
+  for (int i = 0; i < DW; ++i) m &= __builtin_amdgcn_ballot_w64(w[i] == pat);
+  return m;
+}
+
+// v with the lanes of `mask` set to 0 (bits of a float or of an f16 word).
+__device__ __forceinline__ uint32_t zero_where(uint32_t v, uint64_t mask) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, 0, %2" : "=v"(r) : "v"(v), "s"(mask));
+  return r;
 }
 
 // Exact split of an f16 value into bf16 hi + lo (8 + at most 3 significant bits).

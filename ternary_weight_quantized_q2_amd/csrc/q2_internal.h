@@ -34,6 +34,9 @@ hipError_t launch_quantize_rows(const uint16_t* x, uint16_t* xq, float* row_scal
                                 hipStream_t stream);
 hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* t_limbs,
                             int64_t M, int64_t K, int r, hipStream_t stream);
+// The current device's four 64-bit error flags for the load-time checks (a
+// file-scope device array; the address is looked up once per device).
+hipError_t check_flags(unsigned long long** flags);
 hipError_t launch_pack(const uint8_t* codes, const float* scales, int64_t N, int64_t K,
                        uint8_t* packed, uint16_t* scales_f16, unsigned long long* flags,
                        hipStream_t stream);

@@ -69,6 +69,21 @@ __device__ __forceinline__ q2_f32x4 block_cinit(q2_f32x4 s4, float zp) {
   }
 }
 
+// Scale d (and zero point z) of one (weight row, block) of the matrix-core
+// layout from the bits that hold them (in the low half), with d = 0 when every
+// weight of the block is zero: such a block then adds exactly nothing, where
+// its offset-started sum would leave rounding noise.  w is this lane's part of
+// the block's codes; all lanes of the wave must call this together.
+template <int FMT>
+__device__ __forceinline__ void block_scale(const uint32_t (&w)[WFmt<FMT>::LANE_DW], uint32_t sbits,
+                                            uint32_t zbits, float& dc, float& zc) {
+  zc = (FMT == 1) ? f16_to_f32((uint16_t)zbits) : 0.f;
+  uint64_t pz;
+  if constexpr (FMT == 0) pz = q2_part_zero(w);
+  else pz = q4_part_zero(w, zc);
+  dc = f16_to_f32((uint16_t)zero_where(sbits, column_all(pz)));
+}
+
 template <int FMT>
 __device__ __forceinline__ void stage_pairs(const uint32_t (&nx)[8], uint32_t (&pr)[8]) {
   if constexpr (FMT == 0) q2_xpairs(nx, pr);
@@ -393,13 +408,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
       }
       decode_block_nat<FMT>(w, bf[j], kc);
       const uint32_t sw = *reinterpret_cast<const uint32_t*>(wst + CODE_BYTES + (col0 + c) * 4);
-      dc[j] = f16_to_f32((uint16_t)(sw >> ((((shalf ^ par) >> j) & 1) * 16)));
+      uint32_t zb = 0;
       if constexpr (FMT == 1) {
         const uint32_t zw = *reinterpret_cast<const uint32_t*>(wst + CODE_BYTES + 1024 + (col0 + c) * 4);
-        zc[j] = f16_to_f32((uint16_t)(zw >> ((((zhalf ^ par) >> j) & 1) * 16)));
-      } else {
-        zc[j] = 0.f;
+        zb = zw >> ((((zhalf ^ par) >> j) & 1) * 16);
       }
+      block_scale<FMT>(w, sw >> ((((shalf ^ par) >> j) & 1) * 16), zb, dc[j], zc[j]);
     }
     // A fragments of tile i+1 are read from LDS while tile i's MFMAs run;
     // tile i's MFMAs are issued before tile i-1's rescale so the FMAs run in
@@ -837,13 +851,12 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       }
       decode_block_nat<FMT>(w, bf[j], kc);
       const uint32_t sw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + (col0 + c) * 4);
-      dc[j] = f16_to_f32((uint16_t)(sw >> ((((shalf ^ pmask) >> j) & 1) * 16)));
+      uint32_t zb = 0;
       if constexpr (FMT == 1) {
         const uint32_t zw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + 1024 + (col0 + c) * 4);
-        zc[j] = f16_to_f32((uint16_t)(zw >> ((((zhalf ^ pmask) >> j) & 1) * 16)));
-      } else {
-        zc[j] = 0.f;
+        zb = zw >> ((((zhalf ^ pmask) >> j) & 1) * 16);
       }
+      block_scale<FMT>(w, sw >> ((((shalf ^ pmask) >> j) & 1) * 16), zb, dc[j], zc[j]);
     }
   };
   // MFMAs of one block over the staged activations `st`, row sums `sb`.
@@ -1359,13 +1372,12 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
       }
       decode_block_nat<FMT>(w, bf[j], kc);
       const uint32_t sw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + (col0 + c) * 4);
-      dc[j] = f16_to_f32((uint16_t)(sw >> ((((shalf ^ pmask) >> j) & 1) * 16)));
+      uint32_t zb = 0;
       if constexpr (FMT == 1) {
         const uint32_t zw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + SWORDS + (col0 + c) * 4);
-        zc[j] = f16_to_f32((uint16_t)(zw >> ((((zhalf ^ pmask) >> j) & 1) * 16)));
-      } else {
-        zc[j] = 0.f;
+        zb = zw >> ((((zhalf ^ pmask) >> j) & 1) * 16);
       }
+      block_scale<FMT>(w, sw >> ((((shalf ^ pmask) >> j) & 1) * 16), zb, dc[j], zc[j]);
     }
   };
   // MFMAs of one block over the staged activations `st`, row sums `sb`; the
@@ -1707,8 +1719,8 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
               const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(t + (c * 4 + b4) * 16 + 4 * g);
               w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
             }
-            const float dsc = f16_to_f32(st[c * 4 + b4]);
-            const float zp = (FMT == 1) ? f16_to_f32(st[64 + c * 4 + b4]) : 0.f;
+            float dsc, zp;
+            block_scale<FMT>(w, st[c * 4 + b4], (FMT == 1) ? st[64 + c * 4 + b4] : 0u, dsc, zp);
             q2_u32x4 bf[4];
             decode_block<FMT>(w, bf, kc);
             const q2_f32x4 s4 = *reinterpret_cast<const q2_f32x4*>(&ss[bl * 16 + 4 * g]);

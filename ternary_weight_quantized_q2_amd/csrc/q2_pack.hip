@@ -9,10 +9,36 @@
 // is the f32 -> f16 scale cast and it must round-trip exactly.  Bad inputs are
 // reported through two 64-bit device flags that hold the smallest offending
 // flat index (atomicMin, so the reported index is independent of scheduling).
+#include <mutex>
+
 #include "q2_device.h"
 #include "q2_internal.h"
 
 namespace q2dev {
+
+// The error flags of q2_pack (two) and q2_import_gemlite (four), one set per
+// device in a file-scope array, so neither call allocates.  Both calls reset
+// the flags, wait for their kernels and read the flags back under one host
+// lock, so they never overlap on a device.
+static __device__ __align__(16) unsigned long long g_check_flags[4];
+
+hipError_t check_flags(unsigned long long** flags) {
+  static std::mutex lock;
+  static unsigned long long* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(lock);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_check_flags));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<unsigned long long*>(p);
+  }
+  *flags = addr[dev];
+  return hipSuccess;
+}
 
 // One thread per 16 codes (16 bytes in, one packed dword out).
 __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* codes, uint32_t* packed, int64_t n16,

@@ -14,6 +14,8 @@ and a 4-bit text-encoder linear):
 * Q2_0 block scales are |N(0, 1)| * 0.02, rounded to the nearest f16 value and
   handed over as float32 (so the pack step's exact-roundtrip check passes);
 * activations are N(0, 1) float32 rounded to bf16 (round to nearest even);
+  the parity tests add four regimes that stress fp32 accumulation: N(8, 1),
+  one channel at 2^12, and rows scaled by 2^100 or 2^116;
 * low-rank factors A [r, K] and B [N, r] are N(0, std 0.01) rounded to f16;
 * 4-bit weights are uniform random bytes, i.e. two independent codes uniform on
   0..15 per byte; their group scales are |N(0,1)| * 0.02 and zero points
@@ -80,6 +82,29 @@ def activations_bf16(config_id: int, m: int, k: int) -> np.ndarray:
     """u16 [m, k] bf16 bit patterns of N(0, 1) float32 samples."""
     g = stream(config_id, T_X)
     return f32_to_bf16_bits(g.standard_normal((m, k), dtype=np.float32))
+
+
+ACT_REGIMES = ("mean8", "outlier", "huge", "near_limit")
+
+
+def activations_regime_bf16(config_id: int, m: int, k: int, regime: str) -> np.ndarray:
+    """u16 [m, k] bf16 bit patterns of activations that stress the fp32 sums:
+    "mean8" N(8, 1) (a large common offset in every row); "outlier" N(0, 1)
+    with channel k // 3 set to 2^12 in every row; "huge" N(0, 1) * 2^100;
+    "near_limit" N(0, 1) * 2^116 (about 2^119 at the largest, block sums
+    of |x| near 2^123)."""
+    x = stream(config_id, T_X).standard_normal((m, k), dtype=np.float32)
+    if regime == "mean8":
+        x = x + np.float32(8.0)
+    elif regime == "outlier":
+        x[:, k // 3] = np.float32(4096.0)
+    elif regime == "huge":
+        x = x * np.float32(2.0 ** 100)
+    elif regime == "near_limit":
+        x = x * np.float32(2.0 ** 116)
+    else:
+        raise ValueError(f"unknown activation regime {regime}")
+    return f32_to_bf16_bits(x)
 
 
 def lowrank_factors(config_id: int, r: int, k: int, n: int, std: float = 0.01):

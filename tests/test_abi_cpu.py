@@ -45,6 +45,16 @@ def test_strerror_and_workspace_size(lib):
     assert lib.q2_lowrank_workspace_bytes(3, 5) == 256
 
 
+def test_set_dispatch_arguments(lib):
+    # no HIP call is involved: names are checked and stored on the host
+    assert lib.q2_set_dispatch(b"gemv", b"kg6x3x2", 2) == q2.Q2_OK
+    assert lib.q2_set_dispatch(b"bogus", None, 0) == q2.Q2_ERR_ARG
+    assert lib.q2_set_dispatch(None, b"no-such-tile", 0) == q2.Q2_ERR_ARG
+    assert lib.q2_set_dispatch(None, None, 3) == q2.Q2_ERR_ARG
+    assert lib.q2_set_dispatch(b"auto", b"", 0) == q2.Q2_OK
+    assert lib.q2_set_dispatch(None, None, 0) == q2.Q2_OK
+
+
 FAKE = 1 << 20          # 16-byte aligned fake device address (never dereferenced)
 
 

@@ -291,6 +291,16 @@ def _expect_import_error(call, kind, index):
     raise AssertionError(f"conversion did not stop on the bad {kind}")
 
 
+def _source_codes_literal(ct):
+    """Codes [N, K] of a transposed source, one 2-bit field at a time."""
+    kq, n = ct.shape
+    out = np.zeros((n, 4 * kq), np.uint8)
+    for j in range(kq):
+        for i in range(4):
+            out[:, 4 * j + i] = (ct[j, :] >> (2 * i)) & 3
+    return out
+
+
 def check_import(import_fn):
     g = golden("import_transpose.json")
     k, n = g["K"], g["N"]
@@ -310,6 +320,13 @@ def check_import(import_fn):
         ct2, st2, zt2 = I.gemlite_source(group, n2, k2, group)
         p2, s2 = import_fn(ct2, st2, zt2, group)
         assert np.array_equal(O.unpack_q2(p2, s2), O.gemlite_dequant(ct2, st2, zt2, group)), group
+        # and, independently of both oracle decoders: the codes read field by
+        # field from the source bytes (byte j of column n holds codes 4j..4j+3
+        # of row n, least significant pair first), and each block's scale is
+        # the source scale of the group holding the block's first weight
+        assert np.array_equal(O.codes_q2(p2), _source_codes_literal(ct2)), group
+        first_group = (np.arange(k2 // 128) * 128) // group
+        assert np.array_equal(np.asarray(s2).view(np.float16).astype(np.float32), st2[first_group, :].T), group
     # the conversion stops, naming the first offending element, in the order codes, zeros, scales
     ct2, st2, zt2 = I.gemlite_source(7, 6, 256, 64)
     bad = ct2.copy()
@@ -516,6 +533,24 @@ def check_q4(q4_linear):
 
 def test_q4_pins():
     check_q4(O.q4_linear)
+
+
+def check_q4_cols(cols_fn):
+    """The sampled-column 4-bit product equals the columns of the whole
+    (pinned) 4-bit product, for single, scattered, repeated-order and all
+    columns, with zero points that are not integers."""
+    m, k, n = 3, 384, 29
+    p4, s, z = I.q4_weights(96, n, k)
+    xb = I.activations_bf16(96, m, k)
+    full = O.q4_linear(xb, p4, s, z)
+    for cols in (np.array([0]), np.array([n - 1]), np.array([17, 2, 9]), np.arange(n)):
+        got = cols_fn(xb, p4, s, z, cols)
+        assert got.shape == (m, len(cols))
+        assert np.allclose(got, full[:, cols], rtol=1e-13, atol=1e-13), cols
+
+
+def test_q4_cols_pins():
+    check_q4_cols(O.q4_linear_cols)
 
 
 def test_q4_exact_bruteforce():

@@ -67,12 +67,12 @@ def sample_cols(n, count=128, seed=0):
 
 
 @pytest.fixture
-def path(request, monkeypatch):
+def path(request, force):
     p = request.param
     if p != "auto":
-        monkeypatch.setenv("Q2_FORCE_PATH", p)
+        force(path=p)
     else:
-        monkeypatch.delenv("Q2_FORCE_PATH", raising=False)
+        force(path=None)
     return p
 
 
@@ -203,11 +203,11 @@ def _cfg_case(m, n, k):
 
 @pytest.mark.parametrize("cfg", GEMM_CFGS)
 @pytest.mark.parametrize("m,n,k", CFG_SHAPES)
-def test_forced_gemm_configs(cfg, m, n, k, monkeypatch):
+def test_forced_gemm_configs(cfg, m, n, k, force):
     if cfg == "kpair":
         m = 96 * ((m + 95) // 96)          # this configuration takes whole 96-row tiles only
     (x, p, s, ref), (x4, P, S, Z, ref4) = _cfg_case(m, n, k)
-    monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+    force(tile=cfg)
     y = torch.full((m, n), float("nan"), device=DEV)
     q2.q2_linear(x, p, s, y)
     torch.cuda.synchronize()
@@ -219,11 +219,11 @@ def test_forced_gemm_configs(cfg, m, n, k, monkeypatch):
 
 
 @pytest.mark.parametrize("cfg", ["kpair", "kg6x3x2", "w48x192"])
-def test_output_not_16_byte_aligned(cfg, monkeypatch):
+def test_output_not_16_byte_aligned(cfg, force):
     """y 4 bytes past a 16-byte boundary takes the per-element store path."""
     m, n, k = 192, 400, 640
     (x, p, s, ref), _ = _cfg_case(m, n, k)
-    monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+    force(tile=cfg)
     flat = torch.full((m * n + 4,), float("nan"), device=DEV)
     y = flat[1:1 + m * n].view(m, n)
     assert y.data_ptr() % 16 == 4
@@ -233,13 +233,14 @@ def test_output_not_16_byte_aligned(cfg, monkeypatch):
     assert torch.isnan(flat[0]) and torch.isnan(flat[1 + m * n:]).all()
 
 
-def test_forced_gemm_config_errors(monkeypatch):
+def test_forced_gemm_config_errors(force):
     (x, p, s, _), _ = _cfg_case(75, 200, 1408)
-    monkeypatch.setenv("Q2_GEMM_TILE", "no-such-tile")
     with pytest.raises(q2.Q2Error) as e:
-        q2.q2_linear(x, p, s)
+        force(tile="no-such-tile")
     assert e.value.status == q2.Q2_ERR_ARG
-    monkeypatch.setenv("Q2_GEMM_TILE", "kpair")          # 75 rows are not whole 96-row tiles
+    force(tile=None)                # the refused name changed nothing; the call runs
+    q2.q2_linear(x, p, s)
+    force(tile="kpair")          # 75 rows are not whole 96-row tiles
     with pytest.raises(q2.Q2Error) as e:
         q2.q2_linear(x, p, s)
     assert e.value.status == q2.Q2_ERR_HIP
@@ -250,11 +251,11 @@ KG_CFGS = [c for c in GEMM_CFGS if c.startswith("kg")]
 
 @pytest.mark.parametrize("cfg", KG_CFGS)
 @pytest.mark.parametrize("m,n,k", CFG_SHAPES + [(384, 3072, 12288)])
-def test_forced_k_split(cfg, m, n, k, monkeypatch):
+def test_forced_k_split(cfg, m, n, k, force):
     # K in two parts added into a zeroed y; a single block (K = 128) leaves the second part empty
     (x, p, s, ref), (x4, P, S, Z, ref4) = _cfg_case(m, n, k) if k <= 4096 else _k_split_big_case(m, n, k)
-    monkeypatch.setenv("Q2_GEMM_TILE", cfg)
-    monkeypatch.setenv("Q2_GEMM_KSPLIT", "2")
+    force(tile=cfg)
+    force(ksplit=2)
     y = torch.full((m, n), float("nan"), device=DEV)
     q2.q2_linear(x, p, s, y)
     y_again = q2.q2_linear(x, p, s)
@@ -287,12 +288,12 @@ def _k_split_big_case(m, n, k):
 
 
 @pytest.mark.parametrize("offset", [1, 2, 3])
-def test_k_split_unaligned_y(offset, monkeypatch):
+def test_k_split_unaligned_y(offset, force):
     # the zero fill before a split call covers y from any 4-byte position and touches nothing around it
     m, n, k = 75, 201, 1408
     (x, p, s, ref), _ = _cfg_case(m, n, k)
-    monkeypatch.setenv("Q2_GEMM_TILE", "kg2x2x2")
-    monkeypatch.setenv("Q2_GEMM_KSPLIT", "2")
+    force(tile="kg2x2x2")
+    force(ksplit=2)
     flat = torch.full((m * n + 8,), float("nan"), device=DEV)
     y = flat[offset:offset + m * n].view(m, n)
     q2.q2_linear(x, p, s, y)
@@ -301,23 +302,22 @@ def test_k_split_unaligned_y(offset, monkeypatch):
     assert torch.isnan(flat[:offset]).all() and torch.isnan(flat[offset + m * n:]).all()
 
 
-def test_forced_k_split_errors(monkeypatch):
+def test_forced_k_split_errors(force):
     (x, p, s, _), _ = _cfg_case(75, 200, 1408)
-    monkeypatch.setenv("Q2_GEMM_KSPLIT", "3")
     with pytest.raises(q2.Q2Error) as e:
-        q2.q2_linear(x, p, s)
+        force(ksplit=3)
     assert e.value.status == q2.Q2_ERR_ARG
-    monkeypatch.setenv("Q2_GEMM_KSPLIT", "2")
-    monkeypatch.setenv("Q2_GEMM_TILE", "w32x128")       # only K-group tiles split K
+    force(ksplit=2)
+    force(tile="w32x128")       # only K-group tiles split K
     with pytest.raises(q2.Q2Error) as e:
         q2.q2_linear(x, p, s)
     assert e.value.status == q2.Q2_ERR_HIP
-    monkeypatch.setenv("Q2_GEMM_TILE", "kg2x2x2")       # an accumulating call cannot split
+    force(tile="kg2x2x2")       # an accumulating call cannot split
     y = torch.zeros((75, 200), device=DEV)
     with pytest.raises(q2.Q2Error) as e:
         q2.q2_linear_ex(x, p, s, y=y, accumulate=True)
     assert e.value.status == q2.Q2_ERR_HIP
-    monkeypatch.setenv("Q2_FORCE_PATH", "gemv")          # nor does the GEMV
+    force(path="gemv")          # nor does the GEMV
     xs = x[:8].contiguous()
     with pytest.raises(q2.Q2Error) as e:
         q2.q2_linear(xs, p, s)
@@ -372,14 +372,14 @@ def _edge_weight(n, k, regime):
 @pytest.mark.parametrize("regime", ["mixed", "subnormal", "large"])
 @pytest.mark.parametrize("cfg,m", [("gemv", 1), ("gemv", 13), ("auto", 96), ("kpair", 192), ("kg6x3x2", 100),
                                    ("kg2x1x4r3", 40), ("w48x192", 75), ("kg2x2x4", 33)])
-def test_linear_scale_and_code_extremes(cfg, m, regime, monkeypatch):
+def test_linear_scale_and_code_extremes(cfg, m, regime, force):
     n, k = 333, 1408
     packed, sbits = _edge_weight(n, k, regime)
     if cfg == "gemv":
-        monkeypatch.setenv("Q2_FORCE_PATH", "gemv")
+        force(path="gemv")
     elif cfg != "auto":
-        monkeypatch.setenv("Q2_FORCE_PATH", "gemm")
-        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+        force(path="gemm")
+        force(tile=cfg)
     xb, x = acts(22, m, k)
     y = q2.q2_linear(x, dev_u8(packed), dev_bits(sbits, torch.float16)).cpu().numpy()
     assert np.all(np.isfinite(y))
@@ -606,7 +606,7 @@ def test_q4_full_shapes(k, n):
 @pytest.mark.parametrize("regime", ["mixed", "subnormal", "large"])
 @pytest.mark.parametrize("cfg,m", [("gemv", 1), ("gemv", 11), ("auto", 128), ("kg4x2x2", 70), ("kg2x2x4", 33),
                                    ("w48x192", 96)])
-def test_q4_scale_and_zero_extremes(cfg, m, regime, monkeypatch):
+def test_q4_scale_and_zero_extremes(cfg, m, regime, force):
     """4-bit weights with scales of both signs in the three regimes of the Q2_0
     case, and zero points that are zero, negative, non-integer, f16
     subnormals or far outside the code range (the accumulator start
@@ -620,10 +620,10 @@ def test_q4_scale_and_zero_extremes(cfg, m, regime, monkeypatch):
     special = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x7BFF, 0xFBFF, 0x3C00, 0x4B80], np.uint16)
     zbits.reshape(-1)[::5] = np.resize(special, zbits.reshape(-1)[::5].shape)
     if cfg == "gemv":
-        monkeypatch.setenv("Q2_FORCE_PATH", "gemv")
+        force(path="gemv")
     elif cfg != "auto":
-        monkeypatch.setenv("Q2_FORCE_PATH", "gemm")
-        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+        force(path="gemm")
+        force(tile=cfg)
     xb, x = acts(26, m, k)
     y = q2.q4_linear(x, dev_u8(p4), dev_bits(sbits, torch.float16), dev_bits(zbits, torch.float16)).cpu().numpy()
     assert np.all(np.isfinite(y))
@@ -648,25 +648,25 @@ def _lowrank_regime(shape, regime, seed):
 @pytest.mark.parametrize("regime", ["ordinary", "subnormal", "large"])
 @pytest.mark.parametrize("cfg,m,r", [("gemv", 3, 32), ("gemv", 16, 5), ("auto", 192, 32), ("kpair", 96, 64),
                                      ("w48x192", 75, 32), ("w64x128", 40, 8), ("w32x64", 33, 5)])
-def test_lowrank_branch_alone_extremes(cfg, m, r, regime, monkeypatch):
-    """Zero block scales, so W = 0 exactly and y is the branch (x A^T) B^T
-    alone, with the factors in the three regimes; the branch's bf16 limb
-    arithmetic is then the whole result.  (All codes 1 would not isolate it:
-    the kernels' block sums of x (1 + 1/4) and their start value -1.25 S
-    round in different orders, which leaves fp32 noise of the size of x d,
-    above the subnormal-regime branch.)"""
+def test_lowrank_branch_alone_extremes(cfg, m, r, regime, force):
+    """Every code 1, so W = 0 exactly whatever the (non-zero) block scales and
+    y is the branch (x A^T) B^T alone, with the factors in the three
+    regimes; the branch's bf16 limb arithmetic is then the whole result.  This
+    needs the kernels to add exactly nothing for an all-zero block (their
+    offset-started block sums would otherwise leave fp32 noise of the size of
+    x d, above the subnormal-regime branch)."""
     n, k = 300, 640
-    codes = I.q2_codes(27, n, k)
-    scales = np.zeros((n, k // 128), np.float32)
+    codes = np.ones((n, k), np.uint8)
+    scales = (I.q2_scales(27, n, k) + np.float32(0.5)).astype(np.float16).astype(np.float32)
     p = q2.q2_pack(dev_u8(codes), torch.from_numpy(scales).to(DEV))
     p_ref, s_ref = O.pack_q2(codes, scales)
     a = _lowrank_regime((r, k), regime, 28)
     b = _lowrank_regime((n, r), regime, 29)
     if cfg == "gemv":
-        monkeypatch.setenv("Q2_FORCE_PATH", "gemv")
+        force(path="gemv")
     elif cfg != "auto":
-        monkeypatch.setenv("Q2_FORCE_PATH", "gemm")
-        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+        force(path="gemm")
+        force(tile=cfg)
     xb, x = acts(30, m, k)
     y = q2.q2_linear_lowrank(x, p[0], p[1], dev_bits(a, torch.float16), dev_bits(b, torch.float16)).cpu().numpy()
     ref = O.q2_linear_lowrank(xb, p_ref, s_ref, a, b)

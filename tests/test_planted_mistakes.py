@@ -123,7 +123,26 @@ def a8_scale_dropped(xb, p, s):                     # the row scale never applie
     return q.astype(np.float64) @ O.unpack_q2(p, s).T
 
 
+def q4_cols_shifted(xb, p4, s, z, cols):           # the neighbouring weight rows
+    c = (np.asarray(cols) + 1) % np.asarray(p4).shape[0]
+    return O.q4_linear(xb, p4[c], s[c], z[c])
+
+
+def q4_cols_no_zero(xb, p4, s, z, cols):           # q * s: the zero point dropped
+    c = np.asarray(cols)
+    return O.q4_linear(xb, p4[c], s[c], np.zeros_like(np.asarray(z)[c]))
+
+
+def import_codes_reversed(ct, st, zt, g):          # codes of each byte taken MSB-first
+    p, s = O.import_gemlite(ct, st, zt, g)
+    c = O.codes_q2(p).reshape(p.shape[0], -1, 4)[..., ::-1].reshape(p.shape[0], -1)
+    return O.pack_codes_q2(c), s
+
+
 MUTANTS = {
+    "q4 columns shifted": lambda: P.check_q4_cols(q4_cols_shifted),
+    "q4 columns without zero point": lambda: P.check_q4_cols(q4_cols_no_zero),
+    "import codes reversed in each byte": lambda: P.check_import(import_codes_reversed),
     "a8 truncating": lambda: P.check_a8(a8_truncating, O.q2_linear_a8),
     "a8 per-tensor scale": lambda: P.check_a8(a8_per_tensor, O.q2_linear_a8),
     "a8 255 levels": lambda: P.check_a8(a8_unsigned_range, O.q2_linear_a8),
@@ -162,6 +181,7 @@ def test_unmutated_checks_pass():
     P.check_q2_closed_forms(O.q2_linear)
     P.check_lowrank(O.q2_linear_lowrank)
     P.check_q4(O.q4_linear)
+    P.check_q4_cols(O.q4_linear_cols)
     P.check_slice(O.slice_q2)
     P.check_split_sum(O.q2_linear_sum)
     P.check_import(O.import_gemlite)

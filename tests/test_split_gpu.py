@@ -88,14 +88,14 @@ GEMM_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
 LR_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64"]
 
 
-def _set_path(monkeypatch, cfg):
-    monkeypatch.delenv("Q2_FORCE_PATH", raising=False)
-    monkeypatch.delenv("Q2_GEMM_TILE", raising=False)
+def _set_path(force, cfg):
+    force(path=None)
+    force(tile=None)
     if cfg == "gemv":
-        monkeypatch.setenv("Q2_FORCE_PATH", "gemv")
+        force(path="gemv")
     elif cfg != "auto":
-        monkeypatch.setenv("Q2_FORCE_PATH", "gemm")
-        monkeypatch.setenv("Q2_GEMM_TILE", cfg)
+        force(path="gemm")
+        force(tile=cfg)
 
 
 def _acc_case(cfg, m, n, k, r, unaligned=False):
@@ -121,8 +121,8 @@ def _acc_case(cfg, m, n, k, r, unaligned=False):
 
 
 @pytest.mark.parametrize("cfg", ["auto", "gemv"] + GEMM_CFGS)
-def test_accumulate_is_y0_plus_result(cfg, monkeypatch):
-    _set_path(monkeypatch, cfg)
+def test_accumulate_is_y0_plus_result(cfg, force):
+    _set_path(force, cfg)
     if cfg == "gemv":
         _acc_case(cfg, 5, 333, 640, 0)
         _acc_case(cfg, 16, 400, 1280, 0)
@@ -133,8 +133,8 @@ def test_accumulate_is_y0_plus_result(cfg, monkeypatch):
 
 
 @pytest.mark.parametrize("cfg", ["auto", "gemv"] + LR_CFGS)
-def test_accumulate_lowrank(cfg, monkeypatch):
-    _set_path(monkeypatch, cfg)
+def test_accumulate_lowrank(cfg, force):
+    _set_path(force, cfg)
     if cfg == "gemv":
         _acc_case(cfg, 3, 300, 384, 32)
     else:
