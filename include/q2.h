@@ -159,6 +159,27 @@ int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint1
                       float* y, int64_t M, int64_t N, int64_t K,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * q2_linear_lowrank_noalloc - q2_linear_lowrank without a workspace argument
+ * and without any allocation, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The x A^T scratch lives in a file-scope device array of
+ * Q2_NOALLOC_SCRATCH_BYTES (8 MiB) per device, held until the process ends:
+ * calls with q2_lowrank_workspace_bytes(M, r) above that size are refused
+ * with Q2_ERR_WORKSPACE.  The array's device address is looked up once per
+ * device, at the first call made with that device current.  Every call on a
+ * device shares that device's array and overwrites it entirely (nothing in it
+ * needs to start at zero), so calls that overlap on one device -- on
+ * different streams, or from different host threads without ordering -- race
+ * and must not be issued; calls ordered on one stream are safe.  Every other
+ * argument, the result (bit for bit) and the errors are those of
+ * q2_linear_lowrank.  Asynchronous.
+ */
+#define Q2_NOALLOC_SCRATCH_BYTES 8388608u
+int q2_linear_lowrank_noalloc(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
+                              const uint16_t* A_f16, const uint16_t* B_f16, int64_t r,
+                              float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* Flags of q2_linear_ex. */
 #define Q2_ACCUMULATE 0x1u  /* y += result: y is read, the result added in fp32 once */
 

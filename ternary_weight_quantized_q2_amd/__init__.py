@@ -28,7 +28,8 @@ Q2_OK, Q2_ERR_ARG, Q2_ERR_SHAPE, Q2_ERR_ALIGN, Q2_ERR_CODE, Q2_ERR_SCALE, Q2_ERR
 
 Q2_ACCUMULATE = 0x1      # q2_linear_ex flag: y += result
 
-EXPORTS = ("q2_pack", "q2_import_gemlite", "q2_linear", "q2_lowrank_workspace_bytes", "q2_linear_lowrank", "q2_linear_ex", "q2_slice",
+EXPORTS = ("q2_pack", "q2_import_gemlite", "q2_linear", "q2_lowrank_workspace_bytes", "q2_linear_lowrank", "q2_linear_lowrank_noalloc",
+           "q2_linear_ex", "q2_slice",
            "q2_a8_workspace_bytes", "q2_linear_a8",
            "q4_linear", "q2_dequant", "q2_set_dispatch", "q2_strerror", "q2_last_error")
 
@@ -58,6 +59,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "q2_linear": ([p, p, p, p, i64, i64, i64, p], ctypes.c_int),
         "q2_lowrank_workspace_bytes": ([i64, i64], sz),
         "q2_linear_lowrank": ([p, p, p, p, p, i64, p, i64, i64, i64, p, sz, p], ctypes.c_int),
+        "q2_linear_lowrank_noalloc": ([p, p, p, p, p, i64, p, i64, i64, i64, p], ctypes.c_int),
         "q2_linear_ex": ([p, p, p, p, p, i64, p, i64, i64, i64, p, sz, ctypes.c_uint32, p], ctypes.c_int),
         "q2_slice": ([p, p, i64, i64, i64, i64, i64, i64, p, p, p], ctypes.c_int),
         "q2_a8_workspace_bytes": ([i64, i64], sz),
@@ -176,6 +178,29 @@ def q2_linear_lowrank(x, packed, scales, A, B, y=None, workspace=None) -> torch.
     st = lib.q2_linear_lowrank(_ptr(x), _ptr(packed), _ptr(scales), _ptr(A), _ptr(B), r, _ptr(y), m, n, k,
                                _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
     _check(st)
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 8388608      # Q2_NOALLOC_SCRATCH_BYTES
+
+
+def q2_linear_lowrank_noalloc(x, packed, scales, A, B, y=None) -> torch.Tensor:
+    """q2_linear_lowrank with the library's per-device scratch instead of a workspace (no allocation in the
+    library; y is allocated here only when not given)."""
+    lib = load()
+    m, k = x.shape
+    n = packed.shape[0]
+    r = A.shape[0]
+    _want(x, torch.bfloat16, (m, k), "x")
+    _want(packed, torch.uint8, (n, k // 4), "packed")
+    _want(scales, torch.float16, (n, k // 128), "scales")
+    _want(A, torch.float16, (r, k), "A")
+    _want(B, torch.float16, (n, r), "B")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _want(y, torch.float32, (m, n), "y")
+    _check(lib.q2_linear_lowrank_noalloc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(A), _ptr(B), r, _ptr(y), m, n, k,
+                                         _stream()))
     return y
 
 

@@ -147,7 +147,7 @@ int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* 
 // or, with Q2_ACCUMULATE, added to y.
 int linear_entry(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16, const uint16_t* A_f16,
                  const uint16_t* B_f16, int64_t r, float* y, int64_t M, int64_t N, int64_t K, void* workspace,
-                 size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
+                 size_t workspace_bytes, uint32_t flags, hipStream_t stream, bool validate_only = false) {
   int st = check_sizes(M, N, K);
   if (st || (st = check_linear_k(K))) return st;
   if (flags & ~(uint32_t)Q2_ACCUMULATE) return fail(Q2_ERR_ARG, "unknown flag bits 0x%x", flags & ~Q2_ACCUMULATE);
@@ -162,6 +162,7 @@ int linear_entry(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* 
   if (M == 0 || N == 0) return ok();
   const bool accumulate = (flags & Q2_ACCUMULATE) != 0;
   if (accumulate && K == 0) return ok();           // an empty sum added: y stays as it is
+  if (validate_only) return ok();
   uint16_t* tl = nullptr;
   if (r > 0) {
     const size_t need = q2_lowrank_workspace_bytes(M, r);
@@ -176,6 +177,31 @@ int linear_entry(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* 
       (st = hip_status(q2dev::launch_lowrank_t(x_bf16, A_f16, tl, M, K, (int)r, stream), "low-rank x A^T launch")))
     return st;
   return linear_common(0, x_bf16, packed, scales_f16, nullptr, y, M, N, K, tl, B_f16, r, accumulate, stream);
+}
+
+// Scratch of q2_linear_lowrank_noalloc: the x A^T limbs live in this
+// file-scope device array instead of a caller workspace.  Each device holds its
+// own copy; its address is looked up once per device (with that device
+// current) and kept, and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)Q2_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(void** out) {
+  static std::mutex lock;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(Q2_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(Q2_ERR_DEVICE, "device %d out of range", dev);
+  std::lock_guard<std::mutex> g(lock);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(Q2_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return Q2_OK;
 }
 
 }  // namespace
@@ -293,6 +319,29 @@ int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint1
                       const uint16_t* A_f16, const uint16_t* B_f16, int64_t r, float* y, int64_t M, int64_t N,
                       int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return linear_entry(x_bf16, packed, scales_f16, A_f16, B_f16, r, y, M, N, K, workspace, workspace_bytes, 0u,
+                      stream);
+}
+
+int q2_linear_lowrank_noalloc(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
+                              const uint16_t* A_f16, const uint16_t* B_f16, int64_t r, float* y, int64_t M, int64_t N,
+                              int64_t K, hipStream_t stream) {
+  int st = check_sizes(M, N, K);
+  if (st) return st;
+  if (r < 0 || r > 65535) return linear_entry(x_bf16, packed, scales_f16, A_f16, B_f16, r, y, M, N, K, nullptr, 0, 0u,
+                                              stream);                  // the same argument error
+  const size_t need = (r > 0 && M > 0) ? q2_lowrank_workspace_bytes(M, r) : 0;
+  if (need > kNoAllocScratchBytes)
+    return fail(Q2_ERR_WORKSPACE, "M=%lld r=%lld needs %zu bytes of scratch; this entry point holds %zu",
+                (long long)M, (long long)r, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    // Arguments first (as for q2_linear_lowrank), so argument errors never touch the device.
+    if ((st = linear_entry(x_bf16, packed, scales_f16, A_f16, B_f16, r, y, M, N, K, nullptr, 0, 0u, nullptr,
+                           /*validate_only=*/true)))
+      return st;
+    if (M > 0 && N > 0 && ((st = check_device()) || (st = noalloc_scratch(&ws)))) return st;
+  }
+  return linear_entry(x_bf16, packed, scales_f16, A_f16, B_f16, r, y, M, N, K, ws, ws ? kNoAllocScratchBytes : 0, 0u,
                       stream);
 }
 

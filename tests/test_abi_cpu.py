@@ -45,6 +45,17 @@ def test_strerror_and_workspace_size(lib):
     assert lib.q2_lowrank_workspace_bytes(3, 5) == 256
 
 
+def test_noalloc_argument_errors(lib):
+    # checked before any HIP call: sizes beyond the fixed scratch, then the usual argument errors
+    st = lib.q2_linear_lowrank_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 65536, 128, 128, None)
+    assert st == q2.Q2_ERR_WORKSPACE
+    assert lib.q2_linear_lowrank_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 4, 128, 128, None) == q2.Q2_ERR_ARG
+    assert lib.q2_linear_lowrank_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, 128, 100, None) == q2.Q2_ERR_SHAPE
+    assert lib.q2_linear_lowrank_noalloc(None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, 128, 128, None) == q2.Q2_ERR_ARG
+    assert lib.q2_linear_lowrank_noalloc(FAKE + 8, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, 128, 128, None) == q2.Q2_ERR_ALIGN
+    assert lib.q2_linear_lowrank_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 128, 128, None) == q2.Q2_OK
+
+
 def test_set_dispatch_arguments(lib):
     # no HIP call is involved: names are checked and stored on the host
     assert lib.q2_set_dispatch(b"gemv", b"kg6x3x2", 2) == q2.Q2_OK
