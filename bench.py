@@ -86,64 +86,118 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline():
-    """The CPU oracle (float64 NumPy + BLAS) on a bounded sample: the Q2_0
-    linear at M = 1536, K = N = 3072, repeated for about 10 s."""
-    from threadpoolctl import threadpool_info
+def cpu_baseline(step_calls):
+    """The CPU oracle (float64 NumPy + BLAS) on bounded samples of every
+    workload family, with the BLAS pool pinned to the cores this process may
+    use: each family's calls are timed once or more (about 1.5 s each), the
+    100-linear x 4-step layer list as one rank-32 linear x 400 (extrapolated).
+    value = the effective TFLOP/s of one whole step (every call of the GPU
+    step, at the oracle's per-call times)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import q2_oracle as O
     from ternary_weight_quantized_q2_amd import inputs as I
 
-    m, k, n = 1536, 3072, 3072
-    packed, sc = O.pack_q2(I.q2_codes(30, n, k), I.q2_scales(30, n, k))
-    xb = I.activations_bf16(30, m, k)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        O.q2_linear(xb, packed, sc)
-        reps += 1
-        if time.perf_counter() - t0 > 10.0:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": round(2.0 * m * n * k * reps / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{reps} x Q2_0 linear M={m} K={k} N={n} (unpack + float64 dgemm), {dt:.1f} s"}
+    cores = len(os.sched_getaffinity(0))
+    per_config, t_call = {}, {}
+
+    def timed(fn, budget=1.5):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 > budget:
+                break
+        return (time.perf_counter() - t0) / reps, reps
+
+    with threadpool_limits(limits=cores):
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        c = I.CONFIG_TINY
+        p, s = O.pack_q2(I.q2_codes(40, c["N"], c["K"]), I.q2_scales(40, c["N"], c["K"]))
+        xb = I.activations_bf16(40, c["M"], c["K"])
+        t, reps = timed(lambda: O.q2_linear(xb, p, s), 0.5)
+        per_config["tiny M=4 K=256 N=64"] = {"us": round(t * 1e6, 1), "reps": reps}
+        for k, n in I.GEMV_SHAPES:
+            p, s = O.pack_q2(I.q2_codes_fast(41, n, k), I.q2_scales(41, n, k))
+            xb = I.activations_bf16(41, 1, k)
+            t, reps = timed(lambda: O.q2_linear(xb, p, s))
+            t_call[("gemv_m1", k, n)] = t
+            per_config[f"gemv M=1 K={k} N={n}"] = {"ms": round(t * 1e3, 2), "weight_gbs":
+                                                   round(Q2_BYTES_PER_WEIGHT * n * k / t / 1e9, 3), "reps": reps}
+        m = I.GEMM_M
+        for k, n in I.GEMM_SHAPES:
+            p, s = O.pack_q2(I.q2_codes_fast(42, n, k), I.q2_scales(42, n, k))
+            xb = I.activations_bf16(42, m, k)
+            t, reps = timed(lambda: O.q2_linear(xb, p, s))
+            t_call[("gemm_m1536", k, n)] = t
+            per_config[f"gemm M={m} K={k} N={n}"] = {"ms": round(t * 1e3, 1),
+                                                     "tflops": round(2.0 * m * n * k / t / 1e12, 4), "reps": reps}
+        lr = I.LOWRANK
+        p, s = O.pack_q2(I.q2_codes_fast(43, lr["N"], lr["K"]), I.q2_scales(43, lr["N"], lr["K"]))
+        xb = I.activations_bf16(43, lr["M"], lr["K"])
+        a, b = I.lowrank_factors(43, 32, lr["K"], lr["N"])
+        t, reps = timed(lambda: O.q2_linear_lowrank(xb, p, s, a, b))
+        t_call[("lowrank_r32",)] = t
+        calls = lr["linears"] * lr["steps"]
+        per_config[f"layer list r=32 M={lr['M']} K={lr['K']} N={lr['N']}"] = {
+            "ms_per_linear": round(t * 1e3, 1), "s_for_list_extrapolated": round(t * calls, 1),
+            "note": f"one linear timed, x{calls} (extrapolated)", "reps": reps}
+        for k, n in I.Q4_SHAPES:
+            p4, s4, z4 = I.q4_weights(44, n, k)
+            xb = I.activations_bf16(44, I.Q4_M, k)
+            t, reps = timed(lambda: O.q4_linear(xb, p4, s4, z4))
+            t_call[("q4_m128", k, n)] = t
+            per_config[f"q4 M={I.Q4_M} K={k} N={n}"] = {"ms": round(t * 1e3, 1),
+                                                         "tflops": round(2.0 * I.Q4_M * n * k / t / 1e12, 4),
+                                                         "reps": reps}
+    step_t = sum(t_call[key] for key in step_calls)
+    step_f = sum(f for _, f in step_calls.items())
+    return {"value": round(step_f / step_t / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "blas_threads": threads,
+            "sample": "every call of one step, each timed on its own for about 1.5 s (unpack + float64 BLAS); "
+                      "value = step flops / sum of the per-call times",
+            "per_config": per_config}
 
 
-def measure_layer_list(torch, q2, I, dev):
-    """The low-rank layer list: LOWRANK["linears"] distinct rank-32 linears
-    (own W, A, B) on one shared x, LOWRANK["steps"] passes in one graph.  The
-    weights (about 0.9 GB) exceed the 256 MB Infinity Cache, so every call
-    reads its weights from HBM.  Reported beside the step, not part of it."""
+def measure_layer_list(torch, q2, I, dev, ranks=(4, 32, 64)):
+    """The low-rank layer list: LOWRANK["linears"] distinct linears (own W,
+    A, B) on one shared x, LOWRANK["steps"] passes in one graph, at each rank
+    of `ranks`.  The weights (0.76-0.91 GB) exceed the 256 MB Infinity Cache,
+    so every call reads its weights from HBM.  Reported beside the step."""
     c = I.LOWRANK
-    m, k, n, r, layers, steps = c["M"], c["K"], c["N"], 32, c["linears"], c["steps"]
+    m, k, n, layers, steps = c["M"], c["K"], c["N"], c["linears"], c["steps"]
     x = torch.from_numpy(I.activations_bf16(900, m, k).view(np.int16)).to(dev).view(torch.bfloat16)
-    ws = torch.empty(q2.lowrank_workspace_bytes(m, r), dtype=torch.uint8, device=dev)
     y = torch.empty((m, n), device=dev)
-    weights = []
+    packed = []
     for i in range(layers):
-        p, s = q2.q2_pack(torch.from_numpy(I.q2_codes_fast(1000 * r + i, n, k)).to(dev),
-                          torch.from_numpy(I.q2_scales(1000 * r + i, n, k)).to(dev))
-        a, b = I.lowrank_factors(1000 * r + i, r, k, n)
-        weights.append((p, s, torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16),
-                        torch.from_numpy(b.view(np.int16)).to(dev).view(torch.float16)))
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(steps):
-            for p, s, A, B in weights:
-                q2.q2_linear_lowrank(x, p, s, A, B, y=y, workspace=ws)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / (steps * layers)
-    flops = 2.0 * m * n * k + 2.0 * m * r * (k + n)
-    return {"linears": layers, "steps": steps, "r": r, "shape": f"M={m} K={k} N={n}",
-            "us_per_call": round(t * 1e6, 3), "tflops": round(flops / t / 1e12, 3),
-            "frac": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "weight_bytes": int(layers * (Q2_BYTES_PER_WEIGHT * n * k + 2 * r * (k + n) * 2))}
+        packed.append(q2.q2_pack(torch.from_numpy(I.q2_codes_fast(1000 + i, n, k)).to(dev),
+                                 torch.from_numpy(I.q2_scales(1000 + i, n, k)).to(dev)))
+    out = {}
+    for r in ranks:
+        ws = torch.empty(q2.lowrank_workspace_bytes(m, r), dtype=torch.uint8, device=dev)
+        weights = []
+        for i, (p, s) in enumerate(packed):
+            a, b = I.lowrank_factors(1000 * r + i, r, k, n)
+            weights.append((p, s, torch.from_numpy(a.view(np.int16)).to(dev).view(torch.float16),
+                            torch.from_numpy(b.view(np.int16)).to(dev).view(torch.float16)))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                for p, s, A, B in weights:
+                    q2.q2_linear_lowrank(x, p, s, A, B, y=y, workspace=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / (steps * layers)
+        flops = 2.0 * m * n * k + 2.0 * m * r * (k + n)
+        out[f"r={r}"] = {"us_per_call": round(t * 1e6, 3), "tflops": round(flops / t / 1e12, 3),
+                         "frac": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "weight_bytes": int(layers * (Q2_BYTES_PER_WEIGHT * n * k + 2 * r * (k + n) * 2))}
+        del g, weights
+    return {"linears": layers, "steps": steps, "shape": f"M={m} K={k} N={n}", "ranks": out}
 
 
 def measure_split_projection(torch, q2, I, dev, reps=20):
@@ -283,6 +337,75 @@ def measure_peaks(torch, dev):
     t = best(lambda: lib.q2peak_read(buf.data_ptr(), nbytes, outw.data_ptr(), rblocks, stream))
     del buf
     return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(nbytes / t / 1e9, 1)}
+
+
+def _peaks_lib(torch):
+    import ctypes
+    path = os.path.join(ROOT, "ternary_weight_quantized_q2_amd", "libq2_peaks.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.q2peak_read.argtypes = [p, i64, p, ctypes.c_int, p]
+    lib.q2peak_empty.argtypes = [ctypes.c_int, p]
+    return lib
+
+
+def measure_read_ceiling(torch, dev, shapes, steps):
+    """The streaming-read ceiling at the M = 1 GEMV's own sizes: a plain read
+    (16-byte loads, every byte used) of exactly one call's packed weight bytes
+    (codes and scales, 0.265625 N K), over distinct copies that rotate through
+    >= 1 GiB like the GEMV's, launched back to back in a graph and timed per
+    launch with HIP events as the GEMV is.  Best over 256-2048 workgroups.
+    Also the fixed cost of a launch: back-to-back launches of an empty kernel
+    (256 and 2048 workgroups).  These say how close a single call of these
+    sizes can come to the 8 TB/s line."""
+    lib = _peaks_lib(torch)
+    if lib is None:
+        return None
+
+    def stream():          # the capturing stream while a graph is captured
+        return torch.cuda.current_stream().cuda_stream
+
+    def per_launch(fn, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3 / reps)
+        del g
+        return best
+
+    out = {}
+    outw = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    for k, n in shapes:
+        nbytes = int(np.ceil(Q2_BYTES_PER_WEIGHT * n * k / 16.0)) * 16
+        stride = (nbytes + 4095) // 4096 * 4096
+        ncopies = int(np.ceil(ROTATE_BYTES / nbytes))
+        buf = torch.empty(stride * ncopies, dtype=torch.uint8, device=dev)
+        base = buf.data_ptr()
+        reps = max(steps, ncopies)
+        best, best_blocks = float("inf"), 0
+        for blocks in (256, 512, 1024, 2048):
+            t = per_launch(lambda i, b=blocks: lib.q2peak_read(base + (i % ncopies) * stride, nbytes, outw.data_ptr(),
+                                                               b, stream()), reps)
+            if t < best:
+                best, best_blocks = t, blocks
+        out[f"K={k} N={n}"] = {"bytes": nbytes, "us": round(best * 1e6, 3), "gbs": round(nbytes / best / 1e9, 1),
+                               "workgroups": best_blocks, "copies": ncopies}
+        del buf
+    launch = {f"{b} workgroups": round(per_launch(lambda i, b=b: lib.q2peak_empty(b, stream()), 200) * 1e6, 3)
+              for b in (256, 2048)}
+    return {"read": out, "empty_launch_us": launch}
 
 
 def measure_gemv_hot(torch, q2, I, dev, reps=200):
@@ -482,6 +605,7 @@ def main():
     gemv_ach = fam_bytes["gemv_m1"] / fam_time["gemv_m1"] / 1e9 if "gemv_m1" in fam_time else 0.0
     traffic = measured_traffic()
     peaks = None if args.only else measure_peaks(torch, dev)
+    read_ceiling = None if args.only else measure_read_ceiling(torch, dev, I.GEMV_SHAPES, args.steps)
     out = {
         "metric": "Q2_0 linear eff. TFLOP/s (M=1536) + packed-weight GB/s (M=1), % roofline",
         "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
@@ -517,7 +641,21 @@ def main():
         # the same achieved rates against this GPU's measured ceilings (the published peaks stay the reference)
         out["measured_peaks"] = peaks
         out["roofline"]["frac_measured"] = round(gemm_ach / peaks["mfma_bf16_tflops"], 4)
-        out["roofline_gemv"]["frac_measured"] = round(gemv_ach / peaks["hbm_read_gbs"], 4)
+        out["roofline_gemv"]["frac_measured_4gib"] = round(gemv_ach / peaks["hbm_read_gbs"], 4)
+    if read_ceiling is not None:
+        # like for like: the same bytes per launch, the same rotation, the same per-launch timing
+        out.setdefault("measured_peaks", {})["read_ceiling_gemv"] = read_ceiling
+        rd = read_ceiling["read"]
+        ceil_time = sum(v["us"] for v in rd.values()) * 1e-6
+        ceil_gbs = sum(v["bytes"] for v in rd.values()) / ceil_time / 1e9
+        out["roofline_gemv"]["ceiling_gbs_same_size"] = round(ceil_gbs, 1)
+        out["roofline_gemv"]["frac_measured"] = round(gemv_ach / ceil_gbs, 4)
+        for c in calls:
+            if c[0] == "gemv_m1":
+                key = c[4].split(" x")[0].replace("M=1 ", "")
+                if key in rd:
+                    d = parts[f"{c[0]} {c[4]}"]
+                    d["vs_read_ceiling"] = round(d["us"] / rd[key]["us"], 3)
     if layer_list is not None:
         out["layer_list"] = layer_list
     if split_proj is not None:
@@ -529,7 +667,13 @@ def main():
     if gemv_hot is not None:
         out["gemv_m1_hot_cache"] = gemv_hot
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline()
+        step_calls = {}
+        for c in calls:
+            fam = c[0]
+            kn = [int(t.split("=")[1]) for t in c[4].split() if t.startswith(("K=", "N="))][:2]
+            key = (fam,) if fam == "lowrank_r32" else (fam, kn[0], kn[1])
+            step_calls[key] = step_calls.get(key, 0.0) + c[1]
+        out["cpu_baseline"] = cpu_baseline(step_calls)
     print(json.dumps(out))
 
 

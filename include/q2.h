@@ -134,9 +134,11 @@ int q2_linear(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* sca
 
 /*
  * q2_lowrank_workspace_bytes - device bytes q2_linear_lowrank needs for M
- * rows and rank r: M * r * 4 rounded up to a multiple of 256 (0 when M or r
- * is 0).  Negative arguments, and M or r beyond what the linear accepts
- * (M > 2^46, r > 65535), give 0.
+ * rows and rank r: M * r8 * 4 rounded up to a multiple of 256, with r8 = r
+ * rounded up to a multiple of 8 (the bf16 hi and lo limbs of x A^T, padded
+ * rows); 0 when M or r is 0.  Negative arguments, and M or r beyond what the
+ * linear accepts (M > 2^46, r > 65535), give 0; a size beyond SIZE_MAX gives
+ * SIZE_MAX.
  */
 size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r);
 

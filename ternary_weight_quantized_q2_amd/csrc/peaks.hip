@@ -1,7 +1,8 @@
 // peaks.hip - measurement kernels for the benchmark (not part of the linear's
-// ABI): the bf16 matrix-core rate of a back-to-back MFMA loop and the HBM
-// read rate of a streaming read, against which the kernels' achieved rates
-// are also reported.
+// ABI): the bf16 matrix-core rate of a back-to-back MFMA loop, the HBM read
+// rate of a streaming read (of a large buffer, and of buffers the size of
+// one small streaming call's weights), and the fixed cost of a launch, against
+// which the kernels' achieved rates are also reported.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -56,9 +57,19 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* src, int6
   out[t] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
 
+// Does nothing: back-to-back launches of it give the fixed cost of a launch.
+__global__ __launch_bounds__(256) void empty_kernel() {}
+
 }  // namespace
 
 extern "C" {
+
+// Launches `blocks` x 256 threads of a kernel that does nothing.
+int q2peak_empty(int blocks, hipStream_t stream) {
+  if (blocks <= 0) return -1;
+  hipLaunchKernelGGL(empty_kernel, dim3((unsigned)blocks), dim3(256), 0, stream);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
 
 // Launches blocks x 256 threads of the MFMA loop; out must hold blocks * 256 floats.
 // Flops of one launch: blocks * 4 waves * iters * CHAINS * 16384.

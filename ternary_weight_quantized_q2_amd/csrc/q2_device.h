@@ -255,9 +255,12 @@ __device__ __forceinline__ uint64_t column_all(uint64_t b) {
 // weight of the block at zero).
 template <int DW>
 __device__ __forceinline__ uint64_t q2_part_zero(const uint32_t (&w)[DW]) {
-  uint64_t m = __builtin_amdgcn_ballot_w64(w[0] == 0x55555555u);
+  // codes dwords compared in pairs as 64-bit values: one compare per 32 codes
+  static_assert(DW % 2 == 0, "pairs of code dwords");
+  uint64_t m = ~0ull;
 #pragma unroll
-  for (int i = 1; i < DW; ++i) m &= __builtin_amdgcn_ballot_w64(w[i] == 0x55555555u);
+  for (int i = 0; i < DW; i += 2)
+    m &= __builtin_amdgcn_ballot_w64((((uint64_t)w[i + 1] << 32) | w[i]) == 0x5555555555555555ull);
   return m;
 }
 template <int DW>

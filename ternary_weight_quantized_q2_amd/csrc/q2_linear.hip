@@ -112,14 +112,20 @@ __device__ __forceinline__ float sum8_lanes(float v) {
 }
 
 // ---- low-rank epilogue operands -------------------------------------------
+// The limbs of x A^T are stored [M, 2 r8] (hi | lo), r8 = r rounded up to a
+// multiple of 8, the padding columns zero, so every row and both halves start
+// on a 16-byte boundary.
+__host__ __device__ __forceinline__ int lr_pad(int r) { return (r + 7) & ~7; }
+
 // A'' = [T_hi, T_hi, T_lo] (row m of the limbs), B'' = [B_hi, B_lo, B_hi] (row n of B),
 // so sum_q A''[m,q] B''[n,q] = T_hi B_hi + T_hi B_lo + T_lo B_hi.  With r % 8 == 0 the
 // eight elements of a lane group lie in one part and one aligned 16-byte run.
 __device__ __forceinline__ q2_u32x4 lr_afrag(const uint16_t* tl, int64_t m, int r, int q0, bool vec) {
   if (q0 >= 3 * r) return q2_u32x4{0u, 0u, 0u, 0u};
+  const int rs = lr_pad(r);
   if (vec) {
     const int part = q0 / r, jj = q0 - part * r;
-    return *reinterpret_cast<const q2_u32x4*>(tl + m * 2 * r + (part == 2 ? r : 0) + jj);
+    return *reinterpret_cast<const q2_u32x4*>(tl + m * 2 * rs + (part == 2 ? rs : 0) + jj);
   }
   uint32_t e[8];
 #pragma unroll
@@ -128,7 +134,7 @@ __device__ __forceinline__ q2_u32x4 lr_afrag(const uint16_t* tl, int64_t m, int 
     uint32_t v = 0;
     if (q < 3 * r) {
       const int part = q / r, jj = q - part * r;
-      v = tl[m * 2 * r + (part == 2 ? r : 0) + jj];
+      v = tl[m * 2 * rs + (part == 2 ? rs : 0) + jj];
     }
     e[k] = v;
   }
@@ -1121,7 +1127,7 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles) {
 // land.  Each wave copies whole 16-row activation tiles and computes their row
 // sums once its own copies have landed; one barrier per set publishes them.
 // Rows past M are clamped on the copy side and dropped at the store.
-template <int FMT, int MT, int NT, int KG, int NSET>
+template <int FMT, int MT, int NT, int KG, int NSET, bool LR>
 __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int tiles_m, int group_m, int kpart) {
   constexpr int W = 4 * KG;                                   // waves
   constexpr int BM = 16 * MT, BN = 64 * NT;
@@ -1135,7 +1141,11 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   constexpr int NST = NSET * KG;                              // block stages of the ring
   constexpr int OFF_W = NST * XSTAGE;
   constexpr int OFF_S = OFF_W + NST * WSTAGE;
-  constexpr int SMEM = OFF_S + NST * BM * 4;
+  // With the rank-r branch (r <= LR_RMAX): the tile's columns of B in a region
+  // of their own, copied at the start; the tile's rows of the x A^T limbs go
+  // to the ring slot that is free during the last set.
+  constexpr int OFF_B = (OFF_S + NST * BM * 4 + 15) & ~15;
+  constexpr int SMEM = OFF_B + (LR ? BN * (2 * LR_RMAX + 16) + 32 : 0);
   constexpr int NTASK = KG * MT;                              // 16-row activation tiles per set
   constexpr int XT = (NTASK + W - 1) / W;                     // tasks per wave (at most)
   constexpr int XUM = 4 * XT;                                 // activation copy units per wave
@@ -1149,6 +1159,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   static_assert(CPB % 64 == 0, "a code copy must not straddle two blocks");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   static_assert((KG - 1) * BM * BN * 4 <= OFF_S, "reduction buffer");
+  static_assert(!LR || (FMT == 0 && BM * (4 * LR_RMAX + 16) <= KG * XSTAGE), "low-rank limbs fit one ring slot");
   __shared__ __align__(16) uint8_t smem[SMEM];
   float (*const ss)[KG][BM] = reinterpret_cast<float (*)[KG][BM]>(smem + OFF_S);   // [slot][block of set][row]
 
@@ -1350,6 +1361,50 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
     asm volatile("" ::: "memory");
   };
 
+  // ---- the rank-r branch's operands (LR).  The tile's rows of the limbs
+  // (4 r8 bytes, r8 / 4 16-byte chunks each) go to the ring slot that is free
+  // during the last set, one chunk of padding after each row, so the sixteen
+  // rows one fragment read touches fall in different banks; rows past M are
+  // left to the resource's bounds.  B's rows n0 .. n0 + BN - 1, copied at the
+  // start into a region of their own: with r % 8 == 0 and an aligned start,
+  // r / 8 chunks per row plus one of padding; otherwise the row range as one
+  // byte run, from the 16-byte boundary b_off bytes below its start.
+  const int lr_r = LR ? a.r : 0;
+  const int lr_rs = lr_pad(lr_r);
+  const int t_cr = lr_rs / 4 + 1;                        // LDS chunks per limb row, padding included
+  const uint32_t b_off = LR ? (uint32_t)(reinterpret_cast<uintptr_t>(a.lr_b + n0 * lr_r) & 15u) : 0u;
+  const bool bvec = LR && (lr_r & 7) == 0 && b_off == 0;
+  const int b_cr = lr_r / 8 + 1;                         // LDS chunks per row of B when bvec
+  if constexpr (LR) {
+    const uint8_t* bsrc = reinterpret_cast<const uint8_t*>(a.lr_b + n0 * lr_r) - b_off;
+    const uint32_t bavail = (uint32_t)(ncols * 2 * lr_r) + b_off;
+    const __amdgpu_buffer_rsrc_t rb = buf_rsrc(bsrc, bavail);
+    const int bchunks = bvec ? BN * b_cr : (int)((bavail + 15) / 16);
+    for (int base = wv * 64; base < bchunks; base += 64 * W) {
+      const int idx = base + lane;
+      uint32_t src = (uint32_t)idx * 16u;
+      if (bvec) {
+        const int row = idx / b_cr, q = idx - row * b_cr;
+        src = (uint32_t)(row * (b_cr - 1) + min(q, b_cr - 2)) * 16u;   // the padding chunk repeats the last
+      }
+      if (idx < bchunks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(smem + OFF_B + base * 16), 16, src, 0, 0, 0);
+    }
+  }
+  auto issue_limbs = [&](int tslot) {
+    const __amdgpu_buffer_rsrc_t rt = buf_rsrc(a.lr_t + m0 * 2 * lr_rs, (uint32_t)(nrows * 4 * lr_rs));
+    const int tchunks = BM * t_cr;
+    for (int base = wv * 64; base < tchunks; base += 64 * W) {
+      const int idx = base + lane;
+      const int row = idx / t_cr, q = idx - row * t_cr;
+      const uint32_t src = (uint32_t)(row * (t_cr - 1) + min(q, t_cr - 2)) * 16u;
+      if (idx < tchunks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, (lds_void*)(smem + tslot * KG * XSTAGE + base * 16), 16, src, 0,
+                                                 0, 0);
+    }
+  };
+  int t_slot = 0;                         // ring slot holding the limbs
+
   q2_f32x4 acc[MT][NT];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -1443,6 +1498,12 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
       else stage_barrier<0>();
       const int cset = (s + NSET - 1 < NS) ? s + NSET - 1 : -1;       // the set copied during this one
       const int cslot = (slot + NSET - 1 >= NSET) ? slot - 1 : slot + NSET - 1;   // (s + NSET - 1) % NSET
+      if constexpr (LR) {
+        if (s == NS - 1) {                // no set follows: slot cslot is free until the end
+          t_slot = cslot;
+          issue_limbs(cslot);
+        }
+      }
       const int bp = kb0 + KG * s + kg;
       if (bp < kb) {
         q2_u32x4 bf[NT][4];
@@ -1463,9 +1524,77 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
       }
       slot = nslot;
     }
+  } else if constexpr (LR) {
+    issue_limbs(0);                       // K = 0: the branch alone
   }
   __builtin_amdgcn_s_waitcnt(0);          // every copy of this wave has landed
   __syncthreads();                        // and every wave is done reading the stages
+
+  const float fin = (FMT == 0) ? 4.f : 16.f;
+  if constexpr (LR) {
+    // The branch is added in y's units, so the block sums are scaled first
+    // (by a power of two: the reduction below gives the same sum).  Its K
+    // steps are shared out over the groups; of a split tile, part 0 adds it.
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] *= fin;
+    if (part == 0) {
+      const uint8_t* tls = smem + t_slot * KG * XSTAGE;
+      const uint8_t* bls = smem + OFF_B + b_off;          // (aligned rows when bvec)
+      const int ks = (3 * lr_rs + 31) / 32;
+      for (int t = kg; t < ks; t += KG) {
+        const int q0 = 32 * t + 8 * g;
+        const bool live = q0 < 3 * lr_rs;
+        const int prt = live ? q0 / lr_rs : 0, jj = q0 - prt * lr_rs;
+        q2_u32x4 bq[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int col = wn * (BN / 4) + 16 * j + c;
+          q2_u32x4 raw = q2_u32x4{0u, 0u, 0u, 0u};
+          if (live) {
+            if (bvec) {
+              raw = *reinterpret_cast<const q2_u32x4*>(bls + (col * b_cr + jj / 8) * 16);
+            } else {
+              // The copy's bounds check drops a dword that is only partly
+              // inside B, so an element in such a last dword comes from
+              // global memory instead.
+              const uint32_t bavail = (uint32_t)(ncols * 2 * lr_r) + b_off;
+              uint32_t h[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int jx = jj + e;
+                uint32_t hv = 0u;
+                if (jx < lr_r) {
+                  const uint32_t p = b_off + (uint32_t)(col * lr_r + jx) * 2u;
+                  if ((p & ~3u) + 4u <= bavail) hv = *reinterpret_cast<const uint16_t*>(smem + OFF_B + p);
+                  else if (p + 2u <= bavail) hv = a.lr_b[(n0 + col) * lr_r + jx];
+                }
+                h[e] = hv;
+              }
+              raw = q2_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+            }
+          }
+          q2_u32x4 v;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) v[d] = (prt == 1) ? f16x2_bf16_lo(raw[d]) : f16x2_bf16_hi(raw[d]);
+          bq[j] = v;
+        }
+        const int tq = ((prt == 2 ? lr_rs : 0) + jj) / 8;     // the limb chunk of this K step
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const q2_u32x4 aq = live ? *reinterpret_cast<const q2_u32x4*>(tls + ((16 * i + c) * t_cr + tq) * 16)
+                                   : q2_u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
+        }
+      }
+    }
+    __syncthreads();                      // the staged operands are read before the reduction overwrites them
+  }
+  const float fin_red = LR ? 1.f : fin;   // the scale still to apply after the group sum
 
   // Under accumulation the old y values of the row-major stores are loaded
   // now, while the tile is reduced.  A split tile adds its part into y with
@@ -1497,7 +1626,6 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
         for (int e = 0; e < 4; ++e) mine[((i * NT + j) * 4 + e) * 64 + lane] = acc[i][j][e];
   }
   __syncthreads();
-  const float fin = (FMT == 0) ? 4.f : 16.f;
   if (rows16) {
     // As in the K-pair kernel: the finished tile goes through LDS (rows padded
     // to OS floats) and is stored as 16-byte pieces of contiguous rows.
@@ -1513,7 +1641,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
             float v = acc[i][j][e];
 #pragma unroll
             for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
-            acc[i][j][e] = v * fin;
+            acc[i][j][e] = v * fin_red;
           }
     }
     __syncthreads();                      // the partial sums are read; their space takes the tile
@@ -1560,7 +1688,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
           float v = acc[i][j][e];
 #pragma unroll
           for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
-          v *= fin;
+          v *= fin_red;
           const int64_t m = m0 + 16 * i + 4 * g + e;
           if (a.row_scale && m < M) v *= a.row_scale[m];
           if (a.acc) v += yo[i][j][e];
@@ -1833,7 +1961,8 @@ hipError_t launch_quantize_rows(const uint16_t* x, uint16_t* xq, float* row_scal
 }
 
 // ============================================================================
-// x A^T for the low-rank branch: bf16 limbs [M, 2r] = (hi | lo)
+// x A^T for the low-rank branch: bf16 limbs [M, 2 r8] = (hi | lo), r8 = r
+// rounded up to a multiple of 8, padding columns zero
 // ============================================================================
 constexpr int LR_WAVES = 16;
 constexpr int LR_UNROLL = 6;     // k-steps per wave whose loads are issued together
@@ -1886,16 +2015,17 @@ __global__ __launch_bounds__(LR_WAVES * 64) void lowrank_t_kernel(const uint16_t
       sm = q2_f32x4{sm[0] + o[0], sm[1] + o[1], sm[2] + o[2], sm[3] + o[3]};
     }
     const int oc = blockIdx.y * 16 + c;                    // C layout: column = lane % 16
-    if (oc < r) {
+    const int rs = lr_pad(r);
+    if (oc < rs) {                                         // columns r .. rs-1 are the zero padding
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t row = (int64_t)blockIdx.x * 16 + 4 * g + e;
         if (row < M) {
-          const float t = sm[e];
+          const float t = oc < r ? sm[e] : 0.f;
           const uint16_t hi = f32_to_bf16_rn(t);
           const uint16_t lo = f32_to_bf16_rn(t - bf16_to_f32(hi));
-          tl[row * 2 * r + oc] = hi;
-          tl[row * 2 * r + r + oc] = lo;
+          tl[row * 2 * rs + oc] = hi;
+          tl[row * 2 * rs + rs + oc] = lo;
         }
       }
     }
@@ -2034,7 +2164,10 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, int ksplit, hipStream_t s
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t tiles = tiles_m * ((a.N + BN - 1) / BN);
   const int64_t KB = a.K / BLOCK_K;
-  if (a.r > 0 || (ksplit == 2 && a.acc) || (ksplit != 1 && ksplit != 2)) return hipErrorInvalidValue;
+  // The rank-r branch (Q2_0, r <= LR_RMAX) rides in the epilogue; of a split
+  // tile only the first part adds it.
+  if ((a.r > 0 && (FMT != 0 || a.r > LR_RMAX)) || (ksplit == 2 && a.acc) || (ksplit != 1 && ksplit != 2))
+    return hipErrorInvalidValue;
   const int kpart = (ksplit == 2) ? (int)((KB + 1) / 2) : 0;
   const int64_t grid = tiles * (kpart > 0 ? 2 : 1);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
@@ -2045,10 +2178,16 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, int ksplit, hipStream_t s
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gemm_kgroup_kernel<FMT, MT, NT, KG, NSET>), dim3((unsigned)grid), dim3(256 * KG), 0, stream,
-                     a, (int)tiles_m,
-                     kgroup_group_rows<FMT>(a, BM, (int)tiles_m, (int)((a.N + BN - 1) / BN), kpart > 0 ? 2 : 1),
-                     kpart);
+  const int group_m = kgroup_group_rows<FMT>(a, BM, (int)tiles_m, (int)((a.N + BN - 1) / BN), kpart > 0 ? 2 : 1);
+  if constexpr (FMT == 0) {
+    if (a.r > 0) {
+      hipLaunchKernelGGL((gemm_kgroup_kernel<FMT, MT, NT, KG, NSET, true>), dim3((unsigned)grid), dim3(256 * KG), 0,
+                         stream, a, (int)tiles_m, group_m, kpart);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kgroup_kernel<FMT, MT, NT, KG, NSET, false>), dim3((unsigned)grid), dim3(256 * KG), 0,
+                     stream, a, (int)tiles_m, group_m, kpart);
   return hipGetLastError();
 }
 
@@ -2101,12 +2240,14 @@ template <int FMT>
 static int gemm_auto_cfg(const LinearArgs& a) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
+  // The K-group kernels carry the rank-r branch (Q2_0, any r <= LR_RMAX) in
+  // their epilogue, so they take those calls as they take plain ones.
+  const bool kg_ok = a.r == 0 || (FMT == 0 && a.r <= LR_RMAX);
   const int64_t KB = a.K / BLOCK_K;
-  // Up to 384 rows without the low-rank branch: K-group tiles, the widest
-  // whose workgroup count still covers a good part of the chip (measured on
-  // the 3072 / 9216 / 12288 and 2560 / 9728 shapes); Q2_0 with long K keeps a
-  // third set in flight.
-  if (a.r == 0 && a.M <= 384) {
+  // Up to 384 rows: K-group tiles, the widest whose workgroup count still
+  // covers a good part of the chip (measured on the 3072 / 9216 / 12288 and
+  // 2560 / 9728 shapes); Q2_0 with long K keeps a third set in flight.
+  if (kg_ok && a.M <= 384) {
     const int narrow = (FMT == 0 && KB >= 64) ? CFG_KG2x1x4R3 : CFG_KG2x1x4;
     if (a.M <= 64) return tiles(32, 128) >= 128 ? CFG_KG2x2x4 : narrow;
     if (a.M <= 128) return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : narrow;
@@ -2114,7 +2255,7 @@ static int gemm_auto_cfg(const LinearArgs& a) {
     if (tiles(96, 192) >= 128) return CFG_KG6x3x2;     // 10 % ahead of the K-pair kernel at 384 rows
     return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : CFG_KG2x2x4;
   }
-  if (a.r == 0) {
+  if (kg_ok) {
     if (a.M <= 640) return tiles(32, 128) >= 400 ? CFG_KG2x2x2 : CFG_KG4x2x2;
     // The 96 x 192 K-group tile (the K-pair structure with rows past M
     // clamped, XCD-contiguous tiles; equal to the K-pair kernel at M = 1536,
@@ -2123,10 +2264,10 @@ static int gemm_auto_cfg(const LinearArgs& a) {
     if (tiles(96, 192) >= 160) return CFG_KG6x3x2;
     if (a.M >= 48 && tiles(48, 192) >= 256) return CFG_W48x192;
   }
-  // Otherwise prefer the largest tile that still gives a few waves of
-  // workgroups over the 256 compute units.
-  // Eight-wave 96 x 192 tiles when they fill the chip and M is a whole number
-  // of tiles (the low-rank branch only in its LDS-staged form).
+  // Otherwise (a branch of rank above LR_RMAX, or few tiles) prefer the
+  // largest tile that still gives a few waves of workgroups over the 256
+  // compute units.  Eight-wave 96 x 192 tiles when they fill the chip and M is
+  // a whole number of tiles (the low-rank branch only in its LDS-staged form).
   if (a.M % 96 == 0 && tiles(96, 192) >= 256 && (a.r == 0 || lr_lds)) return CFG_KPAIR;
   // 48 x 192 tiles run two workgroups (eight waves) per CU; with the low-rank
   // operands staged in LDS the tile no longer fits twice, so that case keeps 96 x 192.
@@ -2145,7 +2286,7 @@ static int gemm_auto_cfg(const LinearArgs& a) {
 template <int FMT>
 static GemmChoice gemm_auto_choice(const LinearArgs& a) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-  if (a.r == 0 && !a.acc && a.K / BLOCK_K >= 64) {
+  if ((a.r == 0 || (FMT == 0 && a.r <= LR_RMAX)) && !a.acc && a.K / BLOCK_K >= 64) {
     if (a.M <= 64 && tiles(32, 64) < 256) return {FMT == 0 ? CFG_KG2x1x4R3 : CFG_KG2x1x4, 2};
     if (a.M <= 128 && tiles(32, 128) < 256) return {CFG_KG2x2x4, 2};
     if (FMT == 0 && a.M > 256 && a.M <= 640 && tiles(96, 192) < 128) return {CFG_KG6x3x2, 2};
@@ -2175,7 +2316,7 @@ hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, int force
 hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* tl, int64_t M, int64_t K, int r,
                             hipStream_t stream) {
   const int64_t gx = (M + 15) / 16;
-  const int gy = (r + 15) / 16;
+  const int gy = (lr_pad(r) + 15) / 16;
   if (gx > 0x7fffffff || gy > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(lowrank_t_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(LR_WAVES * 64), 0, stream, x, A, tl, M,
                      K, r);

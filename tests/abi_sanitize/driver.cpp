@@ -35,7 +35,8 @@ int main() {
   // workspace sizes at and beyond the limits
   if (q2_lowrank_workspace_bytes(big, 32) != 0 || q2_lowrank_workspace_bytes(1536, big) != 0 ||
       q2_lowrank_workspace_bytes(small, 4) != 0 || q2_lowrank_workspace_bytes(3, 5) != 256 ||
-      q2_lowrank_workspace_bytes((int64_t)1 << 46, 65535) != ((size_t)1 << 48) * 65535u)
+      q2_lowrank_workspace_bytes((int64_t)1 << 46, 65528) != ((size_t)1 << 48) * 65528u ||
+      q2_lowrank_workspace_bytes((int64_t)1 << 46, 65535) != SIZE_MAX)
     ++failures;
   if (q2_a8_workspace_bytes(big, big) != 0 || q2_a8_workspace_bytes(small, 128) != 0 ||
       q2_a8_workspace_bytes(3, 128) != 1024 || q2_a8_workspace_bytes(1, big) != 0)

@@ -43,6 +43,8 @@ def test_strerror_and_workspace_size(lib):
     assert lib.q2_lowrank_workspace_bytes(1, 4) == 256
     assert lib.q2_lowrank_workspace_bytes(1536, 64) == 1536 * 64 * 4
     assert lib.q2_lowrank_workspace_bytes(3, 5) == 256
+    assert lib.q2_lowrank_workspace_bytes(100, 5) == 100 * 8 * 4 // 256 * 256 + 256     # r padded to 8
+    assert lib.q2_lowrank_workspace_bytes(1000, 33) == 1000 * 40 * 4
 
 
 def test_noalloc_argument_errors(lib):

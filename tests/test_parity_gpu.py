@@ -511,6 +511,47 @@ def test_lowrank_parity(m, k, n, r):
     assert_close(y, O.q2_linear_lowrank(xb, p_ref, s_ref, a, b), f"lowrank M={m} K={k} N={n} r={r}")
 
 
+LR_SHAPES = [(75, 1408, 333), (33, 128, 200), (130, 640, 700)]
+
+
+@pytest.mark.parametrize("ksplit", [1, 2])
+@pytest.mark.parametrize("r", [1, 5, 8, 32, 64])
+@pytest.mark.parametrize("cfg", KG_CFGS)
+def test_lowrank_every_kgroup_config(cfg, r, ksplit, force):
+    """The rank-r branch carried in the epilogue of every K-group
+    configuration: ragged M and N, ranks that are and are not multiples of 8,
+    the K blocks whole and in two parts (of a split tile only the first part
+    adds the branch), and B both at an aligned start and 2 bytes off it (the
+    byte-run copy of B)."""
+    force(path="gemm", tile=cfg, ksplit=ksplit)
+    for m, k, n in LR_SHAPES:
+        p_dev, s_dev, p_ref, s_ref, xb, x, a, b, A, B = lowrank_case(51, m, k, n, r)
+        ref = O.q2_linear_lowrank(xb, p_ref, s_ref, a, b)
+        y = q2.q2_linear_lowrank(x, p_dev, s_dev, A, B).cpu().numpy()
+        assert_close(y, ref, f"{cfg} k{ksplit} r={r} M={m} K={k} N={n}")
+        y_off = q2.q2_linear_lowrank(x, p_dev, s_dev, A, _offset_f16(B)).cpu().numpy()
+        assert np.array_equal(y_off, y), f"{cfg} k{ksplit} r={r}: B at an offset start changed the result"
+
+
+@pytest.mark.parametrize("cfg", KG_CFGS)
+def test_lowrank_kgroup_k_zero_and_accumulate(cfg, force):
+    force(path="gemm", tile=cfg)
+    m, n, r = 70, 300, 24
+    p_dev, s_dev, p_ref, s_ref, xb, x, a, b, A, B = lowrank_case(52, m, 512, n, r)
+    # K = 0: the branch of an empty x A^T is zero, so y = 0
+    x0 = torch.empty((m, 0), dtype=torch.bfloat16, device=DEV)
+    y0 = q2.q2_linear_lowrank(x0, torch.empty((n, 0), dtype=torch.uint8, device=DEV),
+                              torch.empty((n, 0), dtype=torch.float16, device=DEV),
+                              torch.empty((r, 0), dtype=torch.float16, device=DEV), B)
+    assert torch.all(y0 == 0)
+    base = torch.randn((m, n), device=DEV)
+    y = base.clone()
+    q2.q2_linear_ex(x, p_dev, s_dev, y=y, A=A, B=B, accumulate=True)
+    v = q2.q2_linear_lowrank(x, p_dev, s_dev, A, B)
+    assert torch.equal(y, base + v), "accumulation must give y_old + v exactly"
+    assert_close(v.cpu().numpy(), O.q2_linear_lowrank(xb, p_ref, s_ref, a, b), f"{cfg} accumulate")
+
+
 @pytest.mark.parametrize("r", I.LOWRANK["ranks"])
 def test_lowrank_full_shape_sampled(r):
     c = I.LOWRANK
