@@ -233,7 +233,7 @@ int q2_slice(const uint8_t* packed, const uint16_t* scales_f16, int64_t N, int64
 
 /*
  * q2_a8_workspace_bytes - device bytes q2_linear_a8 needs for M rows of K
- * inputs: M * K * 2 rounded up to 256 (the codes), plus M * 4 rounded up to
+ * inputs: M * K rounded up to 256 (the int8 codes), plus M * 4 rounded up to
  * 256 (the row scales); 0 when M or K is 0 or negative.
  */
 size_t q2_a8_workspace_bytes(int64_t M, int64_t K);
@@ -250,11 +250,15 @@ size_t q2_a8_workspace_bytes(int64_t M, int64_t K);
  *   x_bf16, packed, scales_f16, y, M, N, K   as q2_linear (x finite)
  *   workspace  device scratch of >= q2_a8_workspace_bytes(M, K) bytes,
  *              256-byte aligned, owned by the caller.  After the call it holds
- *              the codes as bf16 bit patterns [M, K] at offset 0 and the
- *              scales f32 [M] at offset M * K * 2 rounded up to 256.
- * The codes are exact in bf16, so the products stay exact and accumulate in
- * fp32; the row scale is applied once per output.  Asynchronous; calls that
- * share a workspace must be ordered on one stream.
+ *              the codes as int8 [M, K] at offset 0, each group of 16
+ *              consecutive codes of a row stored as a transposed 4 x 4 byte
+ *              matrix (byte 16 p + 4 j + i holds code 16 p + 4 i + j), and the
+ *              scales f32 [M] at offset M * K rounded up to 256.
+ * Each block's sum of code products, sum c[m, k] (q[n, k] - 1), is an integer
+ * computed exactly on the int8 matrix cores; it is multiplied by the block
+ * scale and accumulated in fp32, and the row scale is applied once per
+ * output.  Asynchronous; calls that share a workspace must be ordered on one
+ * stream.
  */
 int q2_linear_a8(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
                  float* y, int64_t M, int64_t N, int64_t K,
@@ -288,9 +292,13 @@ int q2_dequant(const uint8_t* packed, const uint16_t* scales_f16, float* w,
  * M <= 16) or "gemm" (always the GEMM).  tile: NULL or "" for the automatic
  * GEMM configuration, else a configuration name (kpair, w48x192, w96x192,
  * w64x128, w32x128, w32x64, kg2x1x4, kg4x2x2, kg2x1x2, kg2x2x4, kg2x2x2,
- * kg2x1x4r3, kg6x3x2); a forced configuration that cannot take a call's
- * shape makes that call fail with Q2_ERR_HIP.  ksplit: 0 automatic, 1 the
- * whole K in one workgroup, 2 the K blocks in two parts (K-group
+ * kg2x1x4r3, kg6x3x2), or an int8 configuration of q2_linear_a8 (a8_6x3x2,
+ * a8_4x2x2, a8_2x2x2, a8_2x1x4, a8_1x2x4, a8_1x1x4, a8_8x3x2, a8_6x3x1r3,
+ * a8_4x4x2, a8_6x3x2r3, a8_4x2x4, a8_6x2x2, a8_4x3x2), which leaves the bf16
+ * entry points automatic and vice versa; a forced configuration that cannot
+ * take a call's shape makes that call fail with Q2_ERR_HIP.  path applies to
+ * the bf16 entry points only, ksplit to both.  ksplit: 0 automatic, 1 the
+ * whole K in one workgroup, 2 the K blocks in two parts (K-group and int8
  * configurations of non-accumulating calls only, else Q2_ERR_HIP at the
  * call).  An unknown name or value gives Q2_ERR_ARG and changes nothing.
  * The environment variables Q2_FORCE_PATH, Q2_GEMM_TILE and Q2_GEMM_KSPLIT

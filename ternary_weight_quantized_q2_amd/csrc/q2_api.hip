@@ -102,9 +102,16 @@ int parse_path(const char* v) {
   return -1;
 }
 
+// bf16 GEMM configurations keep their numbers; the int8 ones (q2_linear_a8)
+// are numbered from kA8Base on.
+constexpr int kA8Base = 1000;
+
 int parse_cfg(const char* v) {
   if (v == nullptr || *v == 0) return 0;
-  return q2dev::gemm_config_id(v);
+  const int id = q2dev::gemm_config_id(v);
+  if (id >= 0) return id;
+  const int a8 = q2dev::a8_config_id(v);
+  return a8 > 0 ? kA8Base + a8 : a8;
 }
 
 int parse_ksplit(const char* v) {
@@ -125,18 +132,18 @@ void read_dispatch_env() {
 
 int linear_common(int fmt, const uint16_t* x, const uint8_t* w, const uint16_t* s, const uint16_t* z, float* y,
                   int64_t M, int64_t N, int64_t K, const uint16_t* lr_t, const uint16_t* lr_b, int64_t r,
-                  bool accumulate, hipStream_t stream, const float* row_scale = nullptr) {
+                  bool accumulate, hipStream_t stream) {
   q2dev::LinearArgs a;
   a.x = x; a.w = w; a.s = s; a.z = z; a.y = y;
   a.M = M; a.N = N; a.K = K;
   a.lr_t = lr_t; a.lr_b = lr_b; a.r = (int)r;
   a.acc = accumulate ? 1 : 0;
-  a.row_scale = row_scale;
   read_dispatch_env();
   int path = g_dispatch.path.load(std::memory_order_relaxed);
   if (path == 1 && M > 16) path = 0;
-  const int cfg = g_dispatch.cfg.load(std::memory_order_relaxed);
+  int cfg = g_dispatch.cfg.load(std::memory_order_relaxed);
   if (cfg < 0) return fail(Q2_ERR_ARG, "unknown Q2_GEMM_TILE configuration");
+  if (cfg >= kA8Base) cfg = 0;                        // an int8 configuration: automatic here
   const int ks = g_dispatch.ksplit.load(std::memory_order_relaxed);
   if (ks < 0) return fail(Q2_ERR_ARG, "Q2_GEMM_KSPLIT must be 1 or 2");
   return hip_status(q2dev::launch_linear(a, fmt, path, cfg, ks, stream),
@@ -240,7 +247,7 @@ int q2_set_dispatch(const char* path, const char* tile, int ksplit) {
 
 size_t q2_a8_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0 || M > ((int64_t)1 << 40) / K) return 0;
-  const size_t codes = ((size_t)M * (size_t)K * 2u + 255u) & ~(size_t)255u;
+  const size_t codes = ((size_t)M * (size_t)K + 255u) & ~(size_t)255u;
   return codes + (((size_t)M * 4u + 255u) & ~(size_t)255u);
 }
 
@@ -262,12 +269,19 @@ int q2_linear_a8(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* 
   if ((st = check_device())) return st;
   if (K == 0) return linear_common(0, x_bf16, packed, scales_f16, nullptr, y, M, N, K, nullptr, nullptr, 0, false,
                                    stream);
-  uint16_t* xq = static_cast<uint16_t*>(workspace);
-  float* rs = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                       (((size_t)M * (size_t)K * 2u + 255u) & ~(size_t)255u));
-  if ((st = hip_status(q2dev::launch_quantize_rows(x_bf16, xq, rs, M, K, stream), "8-bit quantisation launch")))
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  float* rs = reinterpret_cast<float*>(xq + (((size_t)M * (size_t)K + 255u) & ~(size_t)255u));
+  if ((st = hip_status(q2dev::launch_quantize_rows_i8(x_bf16, xq, rs, M, K, stream), "8-bit quantisation launch")))
     return st;
-  return linear_common(0, xq, packed, scales_f16, nullptr, y, M, N, K, nullptr, nullptr, 0, false, stream, rs);
+  read_dispatch_env();
+  const int cfg = g_dispatch.cfg.load(std::memory_order_relaxed);
+  if (cfg < 0) return fail(Q2_ERR_ARG, "unknown Q2_GEMM_TILE configuration");
+  const int ks = g_dispatch.ksplit.load(std::memory_order_relaxed);
+  if (ks < 0) return fail(Q2_ERR_ARG, "Q2_GEMM_KSPLIT must be 1 or 2");
+  q2dev::A8Args a;
+  a.xq = xq; a.w = packed; a.s = scales_f16; a.row_scale = rs; a.y = y;
+  a.M = M; a.N = N; a.K = K;
+  return hip_status(q2dev::launch_linear_a8(a, cfg >= kA8Base ? cfg - kA8Base : 0, ks, stream), "a8 linear launch");
 }
 
 size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r) {

@@ -70,6 +70,43 @@ __device__ __forceinline__ bool row_piece(int t, int tid, int64_t m0, int64_t M,
   return idx < BM * (BN / 4) && m0 + row < M && 4 * q < ncols;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes from `base` for untyped 32-bit loads
+// (stride 0; the third word selects the 32-bit data format).  A copy through
+// it takes a 32-bit per-lane offset and a wave-uniform scalar offset, so the
+// address arithmetic of the global-to-LDS copies stays in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all its LDS operations are done, then meet the other waves.  Unlike
+// __syncthreads this does not drain every outstanding load, so the
+// global-to-LDS copies of later blocks stay in flight across the barrier.
+// Vector-memory loads complete in issue order, so "at most N outstanding"
+// means everything issued before the last N has landed.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));   // vmcnt(N) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Consecutive workgroup ids are dispatched to the eight XCDs in turn.  This
+// hands each XCD a contiguous range of tile numbers instead, and the numbers
+// run over groups of group_m row tiles, row-fastest inside a group: with
+// group_m = all row tiles each XCD reads 1/8 of the weights and all of x (few
+// rows), with group_m = 1/8 of them each XCD reads 1/8 of x and all of the
+// weights (many rows), and in between the tile grid is cut into 8 blocks.
+__device__ __forceinline__ int xcd_tile(int b, int tiles) {
+  const int per = tiles >> 3, rem = tiles & 7;
+  const int xcd = b & 7, local = b >> 3;
+  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+}
+
 __device__ __forceinline__ q2_f32x4 mfma(q2_u32x4 a, q2_u32x4 b, q2_f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(q2_bf16x8, a),
                                                   __builtin_bit_cast(q2_bf16x8, b), c, 0, 0, 0);

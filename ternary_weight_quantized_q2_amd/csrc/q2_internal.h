@@ -19,7 +19,18 @@ struct LinearArgs {
   const uint16_t* lr_b;
   int r;
   int acc;               // 1: y += result (y is read), 0: y = result
-  const float* row_scale;  // non-null: output row m is multiplied by row_scale[m] (8-bit activations)
+};
+
+// The Q2_0 linear over 8-bit activations: int8 codes [M, K] (each group of 16
+// stored as a transposed 4 x 4 byte matrix, byte 4 j + i = element 4 i + j),
+// row scales [M]; y [M, N] fp32 = row scale * (codes W^T).
+struct A8Args {
+  const uint8_t* xq;
+  const uint8_t* w;
+  const uint16_t* s;
+  const float* row_scale;
+  float* y;
+  int64_t M, N, K;
 };
 
 // Path selection for tests: force_path 0 = automatic, 1 = force GEMV, 2 = force
@@ -30,8 +41,14 @@ struct LinearArgs {
 hipError_t launch_linear(const LinearArgs& a, int fmt, int force_path, int force_cfg, int force_ksplit,
                          hipStream_t stream);
 int gemm_config_id(const char* name);
-hipError_t launch_quantize_rows(const uint16_t* x, uint16_t* xq, float* row_scale, int64_t M, int64_t K,
-                                hipStream_t stream);
+hipError_t launch_quantize_rows_i8(const uint16_t* x, uint8_t* xq, float* row_scale, int64_t M, int64_t K,
+                                   hipStream_t stream);
+// force_cfg 0 = automatic, else the number a8_config_id gives for a name;
+// force_ksplit as for launch_linear.
+hipError_t launch_linear_a8(const A8Args& a, int force_cfg, int force_ksplit, hipStream_t stream);
+int a8_config_id(const char* name);
+// y[0 .. count) = 0 (before a K-split GEMM adds its parts into y).
+hipError_t launch_zero_y(float* y, int64_t count, hipStream_t stream);
 hipError_t launch_lowrank_t(const uint16_t* x, const uint16_t* A, uint16_t* t_limbs,
                             int64_t M, int64_t K, int r, hipStream_t stream);
 // The current device's four 64-bit error flags for the load-time checks (a

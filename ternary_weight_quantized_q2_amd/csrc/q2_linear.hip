@@ -179,31 +179,6 @@ __device__ __forceinline__ q2_u32x4 lr_bfrag(const uint16_t* B, int64_t n, int r
 // wait on global memory (r <= LR_RMAX, r % 8 == 0).
 constexpr int LR_RMAX = 64;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Buffer resource over `bytes` bytes from `base` for untyped 32-bit loads
-// (stride 0; the third word selects the 32-bit data format).  A copy through
-// it takes a 32-bit per-lane offset and a wave-uniform scalar offset, so the
-// address arithmetic of the global-to-LDS copies stays in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// and all its LDS operations are done, then meet the other waves.  Unlike
-// __syncthreads this does not drain every outstanding load, so the
-// global-to-LDS copies of later blocks stay in flight across the barrier.
-// Vector-memory loads complete in issue order, so "at most N outstanding"
-// means everything issued before the last N has landed.
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));   // vmcnt(N) expcnt(7) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Chunk swizzle of an activation row: chunk q of row r sits at position
 // q ^ row_swz(r), row_swz a bit rotation of r mod 16.  Plain q ^ (r & 15) is
 // conflict-free for 16 lanes in isolation but measured at two thirds of the
@@ -585,17 +560,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
     }
   }
 
-  if (a.row_scale) {                      // 8-bit activations: the row's scale
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t m = m0 + 16 * i + 4 * g + e;
-        const float rs = m < M ? a.row_scale[m] : 0.f;
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j][e] *= rs;
-      }
-  }
   if (a.acc) {                            // every old value in flight at once, then added
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -1063,7 +1027,6 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
       int row, q;
       if (row_piece<BM, BN, 512>(t, tid, m0, M, ncols, row, q)) {
         q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
-        if (a.row_scale) v *= a.row_scale[m0 + row];
         if (a.acc) v += yo4[t];
         __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
       }
@@ -1090,7 +1053,6 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
         for (int e = 0; e < 4; ++e) {
           float v = acc[i][j][e] + red[((i * NT + j) * 4 + e) * 64 + lane];
           const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (a.row_scale && m < M) v *= a.row_scale[m];
           if (a.acc) v += yo[i][j][e];
           if (m < M && n < N) __builtin_nontemporal_store(v, &a.y[m * N + n]);
         }
@@ -1102,18 +1064,6 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
 // ============================================================================
 // GEMM for few rows: KG groups of four waves split the K blocks
 // ============================================================================
-// Consecutive workgroup ids are dispatched to the eight XCDs in turn.  This
-// hands each XCD a contiguous range of tile numbers instead, and the numbers
-// run over groups of group_m row tiles, row-fastest inside a group: with
-// group_m = all row tiles each XCD reads 1/8 of the weights and all of x (few
-// rows), with group_m = 1/8 of them each XCD reads 1/8 of x and all of the
-// weights (many rows), and in between the tile grid is cut into 8 blocks.
-__device__ __forceinline__ int xcd_tile(int b, int tiles) {
-  const int per = tiles >> 3, rem = tiles & 7;
-  const int xcd = b & 7, local = b >> 3;
-  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
-}
-
 // With few activation rows a workgroup tile carries little matrix-core work
 // per block, and one wave per SIMD would expose every LDS, matrix-core and
 // barrier latency of a block in turn.  Here a workgroup of KG groups of four
@@ -1660,7 +1610,6 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
       int row, q;
       if (row_piece<BM, BN, 64 * W>(t, tid, m0, M, ncols, row, q)) {
         q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
-        if (a.row_scale) v *= a.row_scale[m0 + row];
         if (a.acc) v += yo4[t];
         __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
       }
@@ -1690,7 +1639,6 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
           for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
           v *= fin_red;
           const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (a.row_scale && m < M) v *= a.row_scale[m];
           if (a.acc) v += yo[i][j][e];
           if (m < M && n < N) {
             if (split) unsafeAtomicAdd(&a.y[m * N + n], v);
@@ -1894,70 +1842,11 @@ __global__ __launch_bounds__(GEMV_WAVES * 64) void gemv_kernel(LinearArgs a, int
       for (int e = 0; e < 4; ++e) {
         const int m = 4 * g + e;
         if (m < M) {
-          const float v = a.row_scale ? s[e] * a.row_scale[m] : s[e];
-          a.y[(int64_t)m * a.N + n] = a.acc ? v + yo[e] : v;
+          a.y[(int64_t)m * a.N + n] = a.acc ? s[e] + yo[e] : s[e];
         }
       }
     }
   }
-}
-
-// ============================================================================
-// 8-bit activations: per-row symmetric quantisation
-// ============================================================================
-// One workgroup per row: s = max |x| / 127 and code = round-half-even(x / s),
-// clamped to [-127, 127], both with IEEE float32 division; a row of zeros has
-// s = 0 and codes 0.  The codes are stored as bf16 bit patterns (every integer
-// up to 256 in magnitude is exact in bf16), so the exact-product linear
-// kernels multiply them unchanged, and s goes to the epilogue's row scale.
-constexpr int QZ_THREADS = 256;
-
-__global__ __launch_bounds__(QZ_THREADS) void quantize_rows_kernel(const uint16_t* x, uint16_t* xq, float* row_scale,
-                                                                   int64_t K) {
-  __shared__ float wmax[QZ_THREADS / 64];
-  const int64_t m = blockIdx.x;
-  const uint16_t* xr = x + m * K;
-  uint16_t* qr = xq + m * K;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  float amax = 0.f;
-  for (int64_t k = 8 * (int64_t)tid; k < K; k += 8 * QZ_THREADS) {     // K is a multiple of 128
-    const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(xr + k);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[d] << 16)));
-      amax = fmaxf(amax, fabsf(__builtin_bit_cast(float, v[d] & 0xFFFF0000u)));
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  if (lane == 0) wmax[wv] = amax;
-  __syncthreads();
-  amax = wmax[0];
-#pragma unroll
-  for (int w = 1; w < QZ_THREADS / 64; ++w) amax = fmaxf(amax, wmax[w]);
-  const float sc = amax / 127.0f;
-  if (tid == 0) row_scale[m] = sc;
-  for (int64_t k = 8 * (int64_t)tid; k < K; k += 8 * QZ_THREADS) {
-    const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(xr + k);
-    q2_u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      float c0 = 0.f, c1 = 0.f;
-      if (sc > 0.f) {
-        c0 = fminf(fmaxf(__builtin_rintf(__builtin_bit_cast(float, v[d] << 16) / sc), -127.f), 127.f);
-        c1 = fminf(fmaxf(__builtin_rintf(__builtin_bit_cast(float, v[d] & 0xFFFF0000u) / sc), -127.f), 127.f);
-      }
-      o[d] = (__builtin_bit_cast(uint32_t, c0 + 0.0f) >> 16) | (__builtin_bit_cast(uint32_t, c1 + 0.0f) & 0xFFFF0000u);
-    }
-    *reinterpret_cast<q2_u32x4*>(qr + k) = o;
-  }
-}
-
-hipError_t launch_quantize_rows(const uint16_t* x, uint16_t* xq, float* row_scale, int64_t M, int64_t K,
-                                hipStream_t stream) {
-  if (M > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)M), dim3(QZ_THREADS), 0, stream, x, xq, row_scale, K);
-  return hipGetLastError();
 }
 
 // ============================================================================
@@ -2154,6 +2043,12 @@ __global__ __launch_bounds__(256) void zero_y_kernel(float* y, int64_t count) {
   if (t0 < count - tail) y[tail + t0] = 0.0f;
 }
 
+hipError_t launch_zero_y(float* y, int64_t count, hipStream_t stream) {
+  const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 4096);
+  hipLaunchKernelGGL(zero_y_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, y, count);
+  return hipGetLastError();
+}
+
 // ksplit 2: the K blocks in two parts, each tile's two workgroups adding
 // into y (zeroed first).  Two fp32 additions onto zero give the same result in
 // either order, so a split call is still run-to-run deterministic; it cannot
@@ -2172,10 +2067,7 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, int ksplit, hipStream_t s
   const int64_t grid = tiles * (kpart > 0 ? 2 : 1);
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (kpart > 0) {
-    const int64_t count = a.M * a.N;
-    const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 4096);
-    hipLaunchKernelGGL(zero_y_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.y, count);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_zero_y(a.y, a.M * a.N, stream);
     if (e != hipSuccess) return e;
   }
   const int group_m = kgroup_group_rows<FMT>(a, BM, (int)tiles_m, (int)((a.N + BN - 1) / BN), kpart > 0 ? 2 : 1);

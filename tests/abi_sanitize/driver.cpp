@@ -39,7 +39,7 @@ int main() {
       q2_lowrank_workspace_bytes((int64_t)1 << 46, 65535) != SIZE_MAX)
     ++failures;
   if (q2_a8_workspace_bytes(big, big) != 0 || q2_a8_workspace_bytes(small, 128) != 0 ||
-      q2_a8_workspace_bytes(3, 128) != 1024 || q2_a8_workspace_bytes(1, big) != 0)
+      q2_a8_workspace_bytes(3, 128) != 768 || q2_a8_workspace_bytes(1, big) != 0)
     ++failures;
 
   auto u16 = [](void* p) { return static_cast<const uint16_t*>(p); };

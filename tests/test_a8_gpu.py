@@ -2,6 +2,10 @@
 oracle.  The codes and row scales, which float32 arithmetic decides, must be
 bit-exact (both sides divide in IEEE float32 and round half to even); the
 product is held to the linear's tolerance against the oracle's y = s * (c W^T).
+
+The workspace holds the codes as int8 [M, K] with every group of 16 codes of
+a row stored as a transposed 4 x 4 byte matrix (byte 4 j + i of a group is
+code 4 i + j), then the f32 row scales at M * K rounded up to 256 bytes.
 """
 import numpy as np
 import pytest
@@ -39,8 +43,9 @@ def run_a8(xb, p, s, n):
     ws = torch.zeros(max(q2.a8_workspace_bytes(m, k), 1), dtype=torch.uint8, device=DEV)
     y = q2.q2_linear_a8(dev_bits(xb, torch.bfloat16), p, s, workspace=ws)
     torch.cuda.synchronize()
-    off = (m * k * 2 + 255) // 256 * 256
-    codes = ws[:m * k * 2].view(torch.int16).cpu().numpy().view(np.uint16).reshape(m, k)
+    off = (m * k + 255) // 256 * 256
+    stored = ws[:m * k].cpu().numpy().view(np.int8).reshape(m, k // 16, 4, 4)
+    codes = stored.transpose(0, 1, 3, 2).reshape(m, k).astype(np.int32)
     scales = ws[off:off + 4 * m].view(torch.float32).cpu().numpy()
     return y.cpu().numpy(), codes, scales
 
@@ -52,29 +57,44 @@ def test_a8_codes_and_product(m, n, k):
     xb = a8_inputs(61, m, k)
     y, codes, scales = run_a8(xb, p, s, n)
     q_ref, s8_ref = O.quantize_rows_a8(xb)
-    got = (codes.astype(np.uint32) << 16).view(np.float32)
-    assert np.array_equal(got, q_ref.astype(np.float32)), "codes"
+    assert np.array_equal(codes, q_ref), "codes"
     assert np.array_equal(scales.view(np.uint32), s8_ref.view(np.uint32)), "row scales"
     assert_close(y, O.q2_linear_a8(xb, p_ref, s_ref), f"a8 M={m} N={n} K={k}")
 
 
-A8_CFGS = ["kpair", "w48x192", "w64x128", "w32x64", "kg2x1x4", "kg4x2x2", "kg2x2x2", "kg6x3x2"]
+A8_CFGS = ["a8_6x3x2", "a8_4x2x2", "a8_2x2x2", "a8_2x1x4", "a8_1x2x4", "a8_1x1x4", "a8_8x3x2", "a8_6x3x1r3",
+           "a8_4x4x2", "a8_6x3x2r3", "a8_4x2x4", "a8_6x2x2", "a8_4x3x2"]
+A8_PATHS = [(c, s) for c in A8_CFGS for s in (1, 2)]
 
 
-A8_PATHS = [(c, "1") for c in A8_CFGS + ["gemv"]] + [(c, "2") for c in A8_CFGS if c.startswith("kg")]
-
-
-@pytest.mark.parametrize("cfg,split", A8_PATHS)
-def test_a8_every_path(cfg, split, force):
-    m, n, k = (8, 333, 1280) if cfg == "gemv" else (192, 333, 1280)
-    force(path="gemv" if cfg == "gemv" else "gemm")
-    if cfg != "gemv":
-        force(tile=cfg)
-        force(ksplit=int(split))
+@pytest.mark.parametrize("m", [13, 75, 200])
+@pytest.mark.parametrize("cfg,split", A8_PATHS, ids=[f"{c}-k{s}" for c, s in A8_PATHS])
+def test_a8_every_config(cfg, split, m, force):
+    """Every int8 configuration, whole K and split, on ragged M and N and 11
+    blocks of K (the last set of every ring partial)."""
+    n, k = 333, 1408
+    force(tile=cfg, ksplit=split)
     p, s, p_ref, s_ref = q2_weights(62, n, k)
     xb = a8_inputs(62, m, k)
-    y, _, _ = run_a8(xb, p, s, n)
-    assert_close(y, O.q2_linear_a8(xb, p_ref, s_ref), f"a8 {cfg} split={split}")
+    y, codes, _ = run_a8(xb, p, s, n)
+    assert np.array_equal(codes, O.quantize_rows_a8(xb)[0]), "codes"
+    assert_close(y, O.q2_linear_a8(xb, p_ref, s_ref), f"a8 {cfg} split={split} M={m}")
+
+
+@pytest.mark.parametrize("regime", I.ACT_REGIMES)
+@pytest.mark.parametrize("cfg", ["a8_6x3x2", "a8_1x2x4"])
+def test_a8_activation_regimes(cfg, regime, force):
+    """N(8, 1), an outlier channel at 2^12, and rows near 2^100 and 2^116."""
+    m, n, k = 40, 333, 1408
+    force(tile=cfg)
+    p, s, p_ref, s_ref = q2_weights(66, n, k)
+    xb = I.activations_regime_bf16(66, m, k, regime)
+    y, codes, scales = run_a8(xb, p, s, n)
+    q_ref, s8_ref = O.quantize_rows_a8(xb)
+    assert np.array_equal(codes, q_ref), "codes"
+    assert np.array_equal(scales.view(np.uint32), s8_ref.view(np.uint32)), "row scales"
+    assert np.all(np.isfinite(y))
+    assert_close(y, O.q2_linear_a8(xb, p_ref, s_ref), f"a8 {regime} {cfg}")
 
 
 @pytest.mark.parametrize("m,k,n", [(1536, 3072, 9216), (384, 12288, 3072)])
@@ -116,19 +136,16 @@ def _extreme_rows(k):
     return I.f32_to_bf16_bits(x)
 
 
-@pytest.mark.parametrize("cfg", ["gemv", "gemm"])
+@pytest.mark.parametrize("cfg", ["a8_1x2x4", "a8_2x1x4"])
 def test_a8_extreme_rows(cfg, force):
     n, k = 200, 640
-    force(path=cfg)
-    if cfg == "gemm":
-        force(tile="kg2x1x4")
+    force(tile=cfg)
     p, s, p_ref, s_ref = q2_weights(65, n, k)
     xb = _extreme_rows(k)
     y, codes, scales = run_a8(xb, p, s, n)
     q_ref, s8_ref = O.quantize_rows_a8(xb)
     assert s8_ref[2] > 0 and s8_ref[2] < np.finfo(np.float32).tiny      # the subnormal-scale row is exercised
-    got = (codes.astype(np.uint32) << 16).view(np.float32)
-    assert np.array_equal(got, q_ref.astype(np.float32)), "codes"
+    assert np.array_equal(codes, q_ref), "codes"
     assert np.array_equal(scales.view(np.uint32), s8_ref.view(np.uint32)), "row scales"
     ref = O.q2_linear_a8(xb, p_ref, s_ref)
     rows = [0, 1, 3, 4, 5, 6]

@@ -153,8 +153,8 @@ def test_slice_argument_errors(lib):
 def test_a8_argument_errors(lib):
     A8 = lib.q2_linear_a8
     assert lib.q2_a8_workspace_bytes(0, 128) == 0 and lib.q2_a8_workspace_bytes(4, 0) == 0
-    assert lib.q2_a8_workspace_bytes(3, 128) == 768 + 256
-    assert lib.q2_a8_workspace_bytes(1536, 3072) == 1536 * 3072 * 2 + 1536 * 4 + 0
+    assert lib.q2_a8_workspace_bytes(3, 128) == 512 + 256            # int8 codes, then row scales
+    assert lib.q2_a8_workspace_bytes(1536, 3072) == 1536 * 3072 + 1536 * 4
     need = lib.q2_a8_workspace_bytes(16, 256)
     assert A8(FAKE, FAKE, FAKE, FAKE, 16, 8, 100, FAKE, need, None) == q2.Q2_ERR_SHAPE
     assert A8(FAKE, FAKE, FAKE, FAKE, 16, 8, 256, FAKE, need - 1, None) == q2.Q2_ERR_WORKSPACE

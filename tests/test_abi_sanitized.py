@@ -28,7 +28,7 @@ def test_abi_validation_under_sanitizers(tmp_path):
         pytest.fail("hipcc is needed to build the sanitized driver")
     csrc = build_lib.CSRC
     kernel_objs = []
-    for name in ("q2_linear.hip", "q2_pack.hip"):
+    for name in ("q2_linear.hip", "q2_a8.hip", "q2_pack.hip"):
         obj = os.path.join(build_lib.OBJ_DIR, name + ".o")
         if not os.path.exists(obj):                    # the library build leaves these behind
             build_lib._compile(os.path.join(csrc, name))

@@ -212,13 +212,25 @@ def test_accumulate_zero_weight_keeps_y(path, tile, force):
     assert torch.equal(y, y0), "adding a zero product must leave y unchanged"
 
 
-@pytest.mark.parametrize("path,tile", [("gemv", None), ("gemm", "kg6x3x2"), ("gemm", "kpair")])
-def test_a8_zero_weight_is_exactly_zero(path, tile, force):
-    force(path=path, tile=tile)
-    m = rows_for(path, tile)
+A8_ZERO = [("a8_6x3x2", 1), ("a8_6x3x2", 2), ("a8_1x2x4", 1), ("a8_2x1x4", 2), ("a8_6x3x1r3", 1)]
+
+
+@pytest.mark.parametrize("tile,ksplit", A8_ZERO)
+def test_a8_zero_weight_is_exactly_zero(tile, ksplit, force):
+    """8-bit activations: a block sum of codes times (1 - 1) is the integer 0,
+    so W = 0 gives y = 0, and all-zero rows among others give zero columns."""
+    force(tile=tile, ksplit=ksplit)
+    m = 75
     codes, scales = zero_weight(N, K, 116)
     p, s, _, _ = packed(codes, scales)
     _, x = x_regime(117, m, K, "mean8")
     y = q2.q2_linear_a8(x, p, s)
     torch.cuda.synchronize()
     assert torch.all(y == 0)
+    zr = np.arange(1, N, 4)
+    codes, scales = zero_weight(N, K, 118, zero_rows=zr)
+    p, s, p_ref, s_ref = packed(codes, scales)
+    xb, x = x_regime(119, m, K, "outlier")
+    y = q2.q2_linear_a8(x, p, s).cpu().numpy()
+    assert not np.any(y[:, zr])
+    assert_close(y, O.q2_linear_a8(xb, p_ref, s_ref), f"a8 zero rows among others, {tile} k{ksplit}")

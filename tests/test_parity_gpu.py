@@ -151,7 +151,9 @@ def test_linear_identity_is_exact(path, m):
 
 
 SHAPES = [(1, 1, 128), (1, 17, 384), (3, 130, 1280), (4, 64, 256), (7, 1000, 256), (16, 257, 512), (17, 65, 640),
-          (33, 200, 128), (100, 333, 384), (257, 190, 1024), (96, 192, 3072), (300, 450, 2048)]
+          (33, 200, 128), (100, 333, 384), (257, 190, 1024), (96, 192, 3072), (300, 450, 2048),
+          # the GEMV's twelve-row workgroups (N / 16 below the CU count), with a ragged last workgroup
+          (1, 2501, 384), (5, 3070, 640), (16, 4000, 256)]
 
 
 @pytest.mark.parametrize("path", ["auto", "gemm"], indirect=True)
@@ -626,7 +628,8 @@ def q4_case(cfg, m, k, n):
 
 
 @pytest.mark.parametrize("path", ["auto", "gemm"], indirect=True)
-@pytest.mark.parametrize("m,n,k", [(1, 64, 256), (5, 77, 384), (16, 300, 1280), (17, 100, 256), (128, 257, 640)])
+@pytest.mark.parametrize("m,n,k", [(1, 64, 256), (5, 77, 384), (16, 300, 1280), (17, 100, 256), (128, 257, 640),
+                                   (1, 2501, 384), (9, 3070, 256)])
 def test_q4_ragged(path, m, n, k):
     p4, s, z, xb, x, P, S, Z = q4_case(90, m, k, n)
     y = q2.q4_linear(x, P, S, Z).cpu().numpy()

@@ -318,6 +318,8 @@ def test_graph_replays_match_eager():
                   q2.lowrank_workspace_bytes(192, 32)))
     cases.append(("a8", 100, 1280, 333, lambda x, y, ws: q2.q2_linear_a8(x, p2, s2, y=y, workspace=ws),
                   q2.a8_workspace_bytes(100, 1280)))
+    cases.append(("a8 split", 64, 12288, 384, lambda x, y, ws: q2.q2_linear_a8(x, p, s, y=y, workspace=ws),
+                  q2.a8_workspace_bytes(64, 12288)))
     p4, s4, z4 = I.q4_weights(54, 333, 1280)
     P4, S4, Z4 = torch.from_numpy(p4).to(DEV), dev_bits(s4, torch.float16), dev_bits(z4, torch.float16)
     cases.append(("q4", 64, 1280, 333, lambda x, y, ws: q2.q4_linear(x, P4, S4, Z4, y), 0))
