@@ -432,7 +432,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="profiling mode: run warmup + steps eagerly and "
                     "print only the wall time (no graph, no per-call events)")
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
-                    "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref")
+                    "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref, a8_m1536")
     ap.add_argument("--extras", action="store_true",
                     help="also time the split output projection, the quarter-size first step, the 8-bit "
                          "activation linear and the hot-cache GEMV (they launch the step's kernels at other shapes "
@@ -515,6 +515,17 @@ def main():
                       lambda xq=xq, P=P, S=S, Z=Z, yq=yq: q2.q4_linear(xq, P, S, Z, yq),
                       f"M={I.Q4_M} K={k} N={n}"))
 
+    if "a8_m1536" in args.only.split(","):
+        # the 8-bit activation linear on the M = 1536 shapes (profiling only;
+        # its timing beside the bf16 linear is the a8_linear report of --extras)
+        for k, n in I.GEMM_SHAPES:
+            p8, s8 = q2w(310, n, k)
+            y8 = torch.empty((m, n), device=dev)
+            ws8 = torch.empty(q2.a8_workspace_bytes(m, k), dtype=torch.uint8, device=dev)
+            calls.append(("a8_m1536", 2.0 * m * n * k, Q2_BYTES_PER_WEIGHT * n * k,
+                          lambda k=k, p8=p8, s8=s8, y8=y8, ws8=ws8: q2.q2_linear_a8(x_by_k[k], p8, s8, y=y8,
+                                                                                    workspace=ws8),
+                          f"8-bit activations M={m} K={k} N={n}"))
     if "copy_ref" in args.only.split(","):
         # calibration for the HBM counters: a plain streaming kernel of known size
         # (256 MiB read + 256 MiB written)

@@ -292,15 +292,16 @@ int q2_dequant(const uint8_t* packed, const uint16_t* scales_f16, float* w,
  * M <= 16) or "gemm" (always the GEMM).  tile: NULL or "" for the automatic
  * GEMM configuration, else a configuration name (kpair, w48x192, w96x192,
  * w64x128, w32x128, w32x64, kg2x1x4, kg4x2x2, kg2x1x2, kg2x2x4, kg2x2x2,
- * kg2x1x4r3, kg6x3x2), or an int8 configuration of q2_linear_a8 (a8_6x3x2,
- * a8_4x2x2, a8_2x2x2, a8_2x1x4, a8_1x2x4, a8_1x1x4, a8_8x3x2, a8_6x3x1r3,
- * a8_4x4x2, a8_6x3x2r3, a8_4x2x4, a8_6x2x2, a8_4x3x2), which leaves the bf16
- * entry points automatic and vice versa; a forced configuration that cannot
- * take a call's shape makes that call fail with Q2_ERR_HIP.  path applies to
- * the bf16 entry points only, ksplit to both.  ksplit: 0 automatic, 1 the
- * whole K in one workgroup, 2 the K blocks in two parts (K-group and int8
- * configurations of non-accumulating calls only, else Q2_ERR_HIP at the
- * call).  An unknown name or value gives Q2_ERR_ARG and changes nothing.
+ * kg2x1x4r3, kg6x3x2), or an int8
+ * configuration of q2_linear_a8 (a8_6x3x2, a8_4x2x2, a8_2x2x2, a8_2x1x4,
+ * a8_1x2x4, a8_1x1x4, a8_8x3x2, a8_6x3x1r3, a8_4x4x2, a8_6x3x2r3, a8_4x2x4,
+ * a8_6x2x2, a8_4x3x2), which leaves the bf16 entry points automatic and vice
+ * versa; a forced configuration that cannot take a call's shape makes that
+ * call fail with Q2_ERR_HIP.  path applies to the bf16 entry points only,
+ * ksplit to both.  ksplit: 0 automatic, 1 the whole K in one workgroup, 2 the
+ * K blocks in two parts (K-group and int8 configurations of non-accumulating
+ * calls only, else Q2_ERR_HIP at the call).  An unknown name or value gives
+ * Q2_ERR_ARG and changes nothing.
  * The environment variables Q2_FORCE_PATH, Q2_GEMM_TILE and Q2_GEMM_KSPLIT
  * (same values) are read once, at the first linear call, as the initial
  * setting.  Results never depend on it beyond fp32 summation order.

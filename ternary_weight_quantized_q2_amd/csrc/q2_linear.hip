@@ -1077,6 +1077,25 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
 // land.  Each wave copies whole 16-row activation tiles and computes their row
 // sums once its own copies have landed; one barrier per set publishes them.
 // Rows past M are clamped on the copy side and dropped at the store.
+// s_waitcnt vmcnt(n) for a uniform n in [LO, HI], by binary search over
+// compile-time counts (the count is an immediate of the instruction).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));   // vmcnt(N) only
+  asm volatile("" ::: "memory");
+}
+template <int LO, int HI>
+__device__ __forceinline__ void vm_wait_range(int n) {
+  if constexpr (LO == HI) {
+    vm_wait<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) vm_wait_range<LO, MID>(n);
+    else vm_wait_range<MID + 1, HI>(n);
+  }
+}
+
 template <int FMT, int MT, int NT, int KG, int NSET, bool LR>
 __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int tiles_m, int group_m, int kpart) {
   constexpr int W = 4 * KG;                                   // waves
@@ -1105,6 +1124,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   constexpr int NU = XUM + NWU;
   constexpr int UPT = (NU + MT - 1) / MT;                     // copy units issued per row tile
   static_assert(NSET == 2 || NSET == 3, "ring depth");
+  static_assert((NSET - 1) * (4 * XT + NWU) <= 63, "copies in flight fit the vmcnt field");
   static_assert(XT <= 2, "activation tasks per wave");
   static_assert(CPB % 64 == 0, "a code copy must not straddle two blocks");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
@@ -1311,21 +1331,23 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
     asm volatile("" ::: "memory");
   };
 
-  // ---- the rank-r branch's operands (LR).  The tile's rows of the limbs
-  // (4 r8 bytes, r8 / 4 16-byte chunks each) go to the ring slot that is free
-  // during the last set, one chunk of padding after each row, so the sixteen
-  // rows one fragment read touches fall in different banks; rows past M are
-  // left to the resource's bounds.  B's rows n0 .. n0 + BN - 1, copied at the
-  // start into a region of their own: with r % 8 == 0 and an aligned start,
-  // r / 8 chunks per row plus one of padding; otherwise the row range as one
-  // byte run, from the 16-byte boundary b_off bytes below its start.
+  // ---- the rank-r branch (LR; of a split tile, part 0 carries it).  Its
+  // operands are copied first: B's rows n0 .. n0 + BN - 1 into a region of
+  // their own (with r % 8 == 0 and an aligned start, r / 8 chunks per row plus
+  // one of padding; otherwise the row range as one byte run, from the 16-byte
+  // boundary b_off bytes below its start), and the tile's rows of the x A^T
+  // limbs (4 r8 bytes, r8 / 4 16-byte chunks each, one chunk of padding after
+  // each row so the sixteen rows one fragment read touches fall in different
+  // banks; rows past M left to the resource's bounds) into ring slot NSET - 1,
+  // which no set occupies before set NSET - 1 is copied during set 0.  The
+  // branch's matrix-core steps then run while the first set's copies land.
   const int lr_r = LR ? a.r : 0;
   const int lr_rs = lr_pad(lr_r);
   const int t_cr = lr_rs / 4 + 1;                        // LDS chunks per limb row, padding included
   const uint32_t b_off = LR ? (uint32_t)(reinterpret_cast<uintptr_t>(a.lr_b + n0 * lr_r) & 15u) : 0u;
   const bool bvec = LR && (lr_r & 7) == 0 && b_off == 0;
   const int b_cr = lr_r / 8 + 1;                         // LDS chunks per row of B when bvec
-  if constexpr (LR) {
+  if (LR && part == 0) {
     const uint8_t* bsrc = reinterpret_cast<const uint8_t*>(a.lr_b + n0 * lr_r) - b_off;
     const uint32_t bavail = (uint32_t)(ncols * 2 * lr_r) + b_off;
     const __amdgpu_buffer_rsrc_t rb = buf_rsrc(bsrc, bavail);
@@ -1353,13 +1375,77 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
                                                  0, 0);
     }
   };
-  int t_slot = 0;                         // ring slot holding the limbs
 
   q2_f32x4 acc[MT][NT];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The branch (x A^T) B^T into acc, from the limbs in ring slot tslot and B
+  // in its region, then divided by the final scale factor (a power of two, so
+  // exactly) since the block sums are added in those units.  Its K steps are
+  // shared out over the groups.
+  auto lr_branch = [&](int tslot) {
+    const uint8_t* tls = smem + tslot * KG * XSTAGE;
+    const uint8_t* bls = smem + OFF_B + b_off;          // (aligned rows when bvec)
+    const int ks = (3 * lr_rs + 31) / 32;
+    for (int t = kg; t < ks; t += KG) {
+      const int q0 = 32 * t + 8 * g;
+      const bool live = q0 < 3 * lr_rs;
+      const int prt = live ? q0 / lr_rs : 0, jj = q0 - prt * lr_rs;
+      q2_u32x4 bq[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int col = wn * (BN / 4) + 16 * j + c;
+        q2_u32x4 raw = q2_u32x4{0u, 0u, 0u, 0u};
+        if (live) {
+          if (bvec) {
+            raw = *reinterpret_cast<const q2_u32x4*>(bls + (col * b_cr + jj / 8) * 16);
+          } else {
+            // The copy's bounds check drops a dword that is only partly
+            // inside B, so an element in such a last dword comes from
+            // global memory instead.
+            const uint32_t bavail = (uint32_t)(ncols * 2 * lr_r) + b_off;
+            uint32_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int jx = jj + e;
+              uint32_t hv = 0u;
+              if (jx < lr_r) {
+                const uint32_t p = b_off + (uint32_t)(col * lr_r + jx) * 2u;
+                if ((p & ~3u) + 4u <= bavail) hv = *reinterpret_cast<const uint16_t*>(smem + OFF_B + p);
+                else if (p + 2u <= bavail) hv = a.lr_b[(n0 + col) * lr_r + jx];
+              }
+              h[e] = hv;
+            }
+            raw = q2_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+          }
+        }
+        q2_u32x4 v;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v[d] = (prt == 1) ? f16x2_bf16_lo(raw[d]) : f16x2_bf16_hi(raw[d]);
+        bq[j] = v;
+      }
+      const int tq = ((prt == 2 ? lr_rs : 0) + jj) / 8;     // the limb chunk of this K step
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const q2_u32x4 aq = live ? *reinterpret_cast<const q2_u32x4*>(tls + ((16 * i + c) * t_cr + tq) * 16)
+                                 : q2_u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
+      }
+    }
+    const float inv = (FMT == 0) ? 0.25f : 0.0625f;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] *= inv;
+  };
+  // Wait until at most the copies of k sets (uniform) of this wave are in flight.
+  auto wait_sets = [&](int k) { vm_wait_range<0, 63>(k * set_units); };
 
   // Decode of one block's weights for this wave's columns (from its weight stage).
   auto decode = [&](const uint8_t* wst, int blk, q2_u32x4 (&bf)[NT][4], float (&dc)[NT], float (&zc)[NT]) {
@@ -1431,29 +1517,33 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   // the barrier publishes them and marks set s - 1 done, so its slot receives
   // the copies of set s + NSET - 1 during set s.  With NSET = 2 a set's weight
   // copies are the last ones waited for (vmcnt(0) at its top barrier); with
-  // NSET = 3 each wave has waited for all of set s's copies at the end of set
-  // s - 1, leaving only the copies of set s + 1 in flight.
-  if (NS > 0) {
-    issue_set(0, 0);
-    if constexpr (NSET == 3) {
-      if (NS > 1) issue_set(1, 1);
-      wait_copies(NS > 1 ? set_units : 0);
-    } else {
-      wait_copies(NWU);
+  // a deeper ring each wave has waited for all of set s's copies at the end
+  // of set s - 1, leaving the copies of up to NSET - 2 later sets in flight.
+  // The first NSET - 1 sets are issued at the start.
+  const int pre = NS < NSET - 1 ? NS : NSET - 1;         // sets issued before the loop
+  if constexpr (LR) {
+    if (part == 0) issue_limbs(NSET - 1);
+  }
+  for (int q = 0; q < pre; ++q) issue_set(q, q);
+  if constexpr (LR) {
+    if (part == 0) {
+      // B and the limbs were issued before the sets' copies, so they have
+      // landed once only those may be in flight.
+      wait_sets(pre);
+      __syncthreads();
+      lr_branch(NSET - 1);
     }
+  }
+  if (NS > 0) {
+    if constexpr (NSET >= 3) wait_sets(pre - 1);
+    else wait_copies(NWU);
     row_sums(0, 0);
     int slot = 0;
     for (int s = 0; s < NS; ++s) {
-      if constexpr (NSET == 3) stage_barrier<63>();
+      if constexpr (NSET >= 3) stage_barrier<63>();
       else stage_barrier<0>();
       const int cset = (s + NSET - 1 < NS) ? s + NSET - 1 : -1;       // the set copied during this one
       const int cslot = (slot + NSET - 1 >= NSET) ? slot - 1 : slot + NSET - 1;   // (s + NSET - 1) % NSET
-      if constexpr (LR) {
-        if (s == NS - 1) {                // no set follows: slot cslot is free until the end
-          t_slot = cslot;
-          issue_limbs(cslot);
-        }
-      }
       const int bp = kb0 + KG * s + kg;
       if (bp < kb) {
         q2_u32x4 bf[NT][4];
@@ -1467,84 +1557,22 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
       if (s + 1 < NS) {
         // The copies of set s + 1 have landed once only those issued after
         // them may be in flight: with two sets its own weight copies, with
-        // three the copies of set s + 2 issued during this set.
-        if constexpr (NSET == 3) wait_copies(cset >= 0 ? set_units : 0);
-        else wait_copies(NWU);
+        // more the copies of the sets s + 2 .. s + NSET - 1 issued so far.
+        if constexpr (NSET >= 3) {
+          const int last = (s + NSET - 1 < NS) ? s + NSET - 1 : NS - 1;   // last set issued
+          wait_sets(last - (s + 1));
+        } else {
+          wait_copies(NWU);
+        }
         row_sums(s + 1, nslot);
       }
       slot = nslot;
     }
-  } else if constexpr (LR) {
-    issue_limbs(0);                       // K = 0: the branch alone
   }
   __builtin_amdgcn_s_waitcnt(0);          // every copy of this wave has landed
   __syncthreads();                        // and every wave is done reading the stages
 
-  const float fin = (FMT == 0) ? 4.f : 16.f;
-  if constexpr (LR) {
-    // The branch is added in y's units, so the block sums are scaled first
-    // (by a power of two: the reduction below gives the same sum).  Its K
-    // steps are shared out over the groups; of a split tile, part 0 adds it.
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] *= fin;
-    if (part == 0) {
-      const uint8_t* tls = smem + t_slot * KG * XSTAGE;
-      const uint8_t* bls = smem + OFF_B + b_off;          // (aligned rows when bvec)
-      const int ks = (3 * lr_rs + 31) / 32;
-      for (int t = kg; t < ks; t += KG) {
-        const int q0 = 32 * t + 8 * g;
-        const bool live = q0 < 3 * lr_rs;
-        const int prt = live ? q0 / lr_rs : 0, jj = q0 - prt * lr_rs;
-        q2_u32x4 bq[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const int col = wn * (BN / 4) + 16 * j + c;
-          q2_u32x4 raw = q2_u32x4{0u, 0u, 0u, 0u};
-          if (live) {
-            if (bvec) {
-              raw = *reinterpret_cast<const q2_u32x4*>(bls + (col * b_cr + jj / 8) * 16);
-            } else {
-              // The copy's bounds check drops a dword that is only partly
-              // inside B, so an element in such a last dword comes from
-              // global memory instead.
-              const uint32_t bavail = (uint32_t)(ncols * 2 * lr_r) + b_off;
-              uint32_t h[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int jx = jj + e;
-                uint32_t hv = 0u;
-                if (jx < lr_r) {
-                  const uint32_t p = b_off + (uint32_t)(col * lr_r + jx) * 2u;
-                  if ((p & ~3u) + 4u <= bavail) hv = *reinterpret_cast<const uint16_t*>(smem + OFF_B + p);
-                  else if (p + 2u <= bavail) hv = a.lr_b[(n0 + col) * lr_r + jx];
-                }
-                h[e] = hv;
-              }
-              raw = q2_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-            }
-          }
-          q2_u32x4 v;
-#pragma unroll
-          for (int d = 0; d < 4; ++d) v[d] = (prt == 1) ? f16x2_bf16_lo(raw[d]) : f16x2_bf16_hi(raw[d]);
-          bq[j] = v;
-        }
-        const int tq = ((prt == 2 ? lr_rs : 0) + jj) / 8;     // the limb chunk of this K step
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const q2_u32x4 aq = live ? *reinterpret_cast<const q2_u32x4*>(tls + ((16 * i + c) * t_cr + tq) * 16)
-                                   : q2_u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
-        }
-      }
-    }
-    __syncthreads();                      // the staged operands are read before the reduction overwrites them
-  }
-  const float fin_red = LR ? 1.f : fin;   // the scale still to apply after the group sum
+  const float fin_red = (FMT == 0) ? 4.f : 16.f;   // the scale still to apply after the group sum
 
   // Under accumulation the old y values of the row-major stores are loaded
   // now, while the tile is reduced.  A split tile adds its part into y with
