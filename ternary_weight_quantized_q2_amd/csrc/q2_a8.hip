@@ -478,7 +478,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_a8_kernel(A8Args a, int tiles_m
 #pragma unroll
     for (int t = 0; t < RP; ++t) {
       int row, q;
-      if (row_piece<BM, BN, 64 * W>(t, tid, m0, M, ncols, row, q)) {
+      if (row_piece<BM, BN, 64 * W>(t, tid, (int)nrows, (int)ncols, row, q)) {
         q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
         v *= a.row_scale[m0 + row];
         __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));

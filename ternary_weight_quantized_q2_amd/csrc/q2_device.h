@@ -61,13 +61,15 @@ __device__ __forceinline__ q2_f32x4 y_old4(const q2_f32x4* p, bool valid) {
 
 // Piece t of the row-major stores of a BM x BN output tile by THREADS
 // threads: 16 bytes at tile row `row`, columns 4q .. 4q+3.  False when the
-// piece is past the tile, past row M - 1 or past the ncols valid columns.
+// piece is past the tile or past its nrows valid rows or ncols valid columns
+// (tile-relative 32-bit counts, so no 64-bit row index lives across the
+// kernel's main loop).
 template <int BM, int BN, int THREADS>
-__device__ __forceinline__ bool row_piece(int t, int tid, int64_t m0, int64_t M, int64_t ncols, int& row, int& q) {
+__device__ __forceinline__ bool row_piece(int t, int tid, int nrows, int ncols, int& row, int& q) {
   const int idx = tid + t * THREADS;
   row = idx / (BN / 4);
   q = idx - row * (BN / 4);
-  return idx < BM * (BN / 4) && m0 + row < M && 4 * q < ncols;
+  return idx < BM * (BN / 4) && row < nrows && 4 * q < ncols;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;

@@ -977,7 +977,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
 #pragma unroll
     for (int t = 0; t < RP; ++t) {
       int row, q;
-      const bool v = row_piece<BM, BN, 512>(t, tid, m0, M, ncols, row, q);
+      const bool v = row_piece<BM, BN, 512>(t, tid, (int)((M - m0) < BM ? (M - m0) : BM), (int)ncols, row, q);
       yo4[t] = y_old4(reinterpret_cast<const q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]), v);
     }
   }
@@ -1025,7 +1025,7 @@ __global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles
 #pragma unroll
     for (int t = 0; t < RP; ++t) {
       int row, q;
-      if (row_piece<BM, BN, 512>(t, tid, m0, M, ncols, row, q)) {
+      if (row_piece<BM, BN, 512>(t, tid, (int)((M - m0) < BM ? (M - m0) : BM), (int)ncols, row, q)) {
         q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
         if (a.acc) v += yo4[t];
         __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
@@ -1390,50 +1390,85 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
     const uint8_t* tls = smem + tslot * KG * XSTAGE;
     const uint8_t* bls = smem + OFF_B + b_off;          // (aligned rows when bvec)
     const int ks = (3 * lr_rs + 31) / 32;
-    for (int t = kg; t < ks; t += KG) {
-      const int q0 = 32 * t + 8 * g;
-      const bool live = q0 < 3 * lr_rs;
-      const int prt = live ? q0 / lr_rs : 0, jj = q0 - prt * lr_rs;
-      q2_u32x4 bq[NT];
+    if (bvec && (lr_rs & 31) == 0) {
+      // Every K step lies inside one part (T_hi B_hi, T_hi B_lo, T_lo B_hi),
+      // the same for all lanes: all of a step's fragments are read first,
+      // then only the needed half of B's split is formed.
+      const int spp = lr_rs / 32;                        // steps per part
+      for (int t = kg; t < ks; t += KG) {
+        const int prt = t / spp;                         // uniform
+        const int jj = (t - prt * spp) * 32 + 8 * g;
+        const int tq = ((prt == 2 ? lr_rs : 0) + jj) / 8;
+        q2_u32x4 raw[NT], aq[MT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int col = wn * (BN / 4) + 16 * j + c;
-        q2_u32x4 raw = q2_u32x4{0u, 0u, 0u, 0u};
-        if (live) {
-          if (bvec) {
-            raw = *reinterpret_cast<const q2_u32x4*>(bls + (col * b_cr + jj / 8) * 16);
-          } else {
-            // The copy's bounds check drops a dword that is only partly
-            // inside B, so an element in such a last dword comes from
-            // global memory instead.
-            const uint32_t bavail = (uint32_t)(ncols * 2 * lr_r) + b_off;
-            uint32_t h[8];
+        for (int j = 0; j < NT; ++j)
+          raw[j] = *reinterpret_cast<const q2_u32x4*>(bls + ((wn * (BN / 4) + 16 * j + c) * b_cr + jj / 8) * 16);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int jx = jj + e;
-              uint32_t hv = 0u;
-              if (jx < lr_r) {
-                const uint32_t p = b_off + (uint32_t)(col * lr_r + jx) * 2u;
-                if ((p & ~3u) + 4u <= bavail) hv = *reinterpret_cast<const uint16_t*>(smem + OFF_B + p);
-                else if (p + 2u <= bavail) hv = a.lr_b[(n0 + col) * lr_r + jx];
-              }
-              h[e] = hv;
-            }
-            raw = q2_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-          }
+        for (int i = 0; i < MT; ++i)
+          aq[i] = *reinterpret_cast<const q2_u32x4*>(tls + ((16 * i + c) * t_cr + tq) * 16);
+        q2_u32x4 bq[NT];
+        if (prt == 1) {
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) bq[j][d] = f16x2_bf16_lo(raw[j][d]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) bq[j][d] = f16x2_bf16_hi(raw[j][d]);
         }
-        q2_u32x4 v;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) v[d] = (prt == 1) ? f16x2_bf16_lo(raw[d]) : f16x2_bf16_hi(raw[d]);
-        bq[j] = v;
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq[i], bq[j], acc[i][j]);
       }
-      const int tq = ((prt == 2 ? lr_rs : 0) + jj) / 8;     // the limb chunk of this K step
-#pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        const q2_u32x4 aq = live ? *reinterpret_cast<const q2_u32x4*>(tls + ((16 * i + c) * t_cr + tq) * 16)
-                                 : q2_u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
+    } else {
+      for (int t = kg; t < ks; t += KG) {
+        const int q0 = 32 * t + 8 * g;
+        const bool live = q0 < 3 * lr_rs;
+        const int prt = live ? q0 / lr_rs : 0, jj = q0 - prt * lr_rs;
+        q2_u32x4 bq[NT];
+  #pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int col = wn * (BN / 4) + 16 * j + c;
+          q2_u32x4 raw = q2_u32x4{0u, 0u, 0u, 0u};
+          if (live) {
+            if (bvec) {
+              raw = *reinterpret_cast<const q2_u32x4*>(bls + (col * b_cr + jj / 8) * 16);
+            } else {
+              // The copy's bounds check drops a dword that is only partly
+              // inside B, so an element in such a last dword comes from
+              // global memory instead.
+              const uint32_t bavail = (uint32_t)(ncols * 2 * lr_r) + b_off;
+              uint32_t h[8];
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int jx = jj + e;
+                uint32_t hv = 0u;
+                if (jx < lr_r) {
+                  const uint32_t p = b_off + (uint32_t)(col * lr_r + jx) * 2u;
+                  if ((p & ~3u) + 4u <= bavail) hv = *reinterpret_cast<const uint16_t*>(smem + OFF_B + p);
+                  else if (p + 2u <= bavail) hv = a.lr_b[(n0 + col) * lr_r + jx];
+                }
+                h[e] = hv;
+              }
+              raw = q2_u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+            }
+          }
+          q2_u32x4 v;
+  #pragma unroll
+          for (int d = 0; d < 4; ++d) v[d] = (prt == 1) ? f16x2_bf16_lo(raw[d]) : f16x2_bf16_hi(raw[d]);
+          bq[j] = v;
+        }
+        const int tq = ((prt == 2 ? lr_rs : 0) + jj) / 8;     // the limb chunk of this K step
+  #pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const q2_u32x4 aq = live ? *reinterpret_cast<const q2_u32x4*>(tls + ((16 * i + c) * t_cr + tq) * 16)
+                                   : q2_u32x4{0u, 0u, 0u, 0u};
+  #pragma unroll
+          for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
+        }
       }
     }
     const float inv = (FMT == 0) ? 0.25f : 0.0625f;
@@ -1586,7 +1621,7 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
 #pragma unroll
     for (int t = 0; t < RP; ++t) {
       int row, q;
-      const bool v = row_piece<BM, BN, 64 * W>(t, tid, m0, M, ncols, row, q);
+      const bool v = row_piece<BM, BN, 64 * W>(t, tid, (int)nrows, (int)ncols, row, q);
       yo4[t] = y_old4(reinterpret_cast<const q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]), v);
     }
   }
@@ -1636,13 +1671,17 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
 #pragma unroll
     for (int t = 0; t < RP; ++t) {
       int row, q;
-      if (row_piece<BM, BN, 64 * W>(t, tid, m0, M, ncols, row, q)) {
+      if (row_piece<BM, BN, 64 * W>(t, tid, (int)nrows, (int)ncols, row, q)) {
         q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
         if (a.acc) v += yo4[t];
         __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
       }
     }
   } else if (kg == 0) {
+    // Tile-relative 32-bit row and column indices against the tile's valid
+    // counts (no 64-bit index is then live across the main loop).
+    float* const yt = a.y + m0 * N + n0;
+    const int nr = (int)nrows, nc = (int)ncols;
     float yo[MT][NT][4];
     if (a.acc) {                          // every old value in flight at once, then added
 #pragma unroll
@@ -1651,26 +1690,26 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
         for (int j = 0; j < NT; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int64_t m = m0 + 16 * i + 4 * g + e, n = nw + 16 * j + c;
-            yo[i][j][e] = y_old(&a.y[m * N + n], m < M && n < N);
+            const int mr = 16 * i + 4 * g + e, cr = wn * (BN / 4) + 16 * j + c;
+            yo[i][j][e] = y_old(&yt[(int64_t)mr * N + cr], mr < nr && cr < nc);
           }
     }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int64_t n = nw + 16 * j + c;
+        const int cr = wn * (BN / 4) + 16 * j + c;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float v = acc[i][j][e];
 #pragma unroll
           for (int q = 1; q < KG; ++q) v += red[(((q - 1) * 4 + wn) * PART) + ((i * NT + j) * 4 + e) * 64 + lane];
           v *= fin_red;
-          const int64_t m = m0 + 16 * i + 4 * g + e;
+          const int mr = 16 * i + 4 * g + e;
           if (a.acc) v += yo[i][j][e];
-          if (m < M && n < N) {
-            if (split) unsafeAtomicAdd(&a.y[m * N + n], v);
-            else __builtin_nontemporal_store(v, &a.y[m * N + n]);
+          if (mr < nr && cr < nc) {
+            if (split) unsafeAtomicAdd(&yt[(int64_t)mr * N + cr], v);
+            else __builtin_nontemporal_store(v, &yt[(int64_t)mr * N + cr]);
           }
         }
       }
