@@ -505,8 +505,11 @@ def main():
                   Q2_BYTES_PER_WEIGHT * lr["N"] * lr["K"],
                   lambda: q2.q2_linear_lowrank(xl, lp, ls, A, B, y=yl, workspace=ws),
                   f"M={lr['M']} K={lr['K']} N={lr['N']} r={r}"))
-    # 4-bit encoder linears
+    # 4-bit encoder linears; their binding roofline counts every algorithmic
+    # byte (packed weights with scales and zero points, x in bf16, y in fp32)
+    q4_all_bytes = {}
     for k, n in I.Q4_SHAPES:
+        q4_all_bytes[f"M={I.Q4_M} K={k} N={n}"] = Q4_BYTES_PER_WEIGHT * n * k + 2.0 * I.Q4_M * k + 4.0 * I.Q4_M * n
         p4, s4, z4 = I.q4_weights(340, n, k)
         P, S, Z = u8(p4), bits(s4, torch.float16), bits(z4, torch.float16)
         xq = bits(I.activations_bf16(341, I.Q4_M, k), torch.bfloat16)
@@ -607,6 +610,11 @@ def main():
              "weight_gbs": round(wbytes / t / 1e9, 2)}
         d["frac"] = round((wbytes / t / 1e9) / PEAK_HBM_GBS, 4) if fam == "gemv_m1" else \
             round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        if fam == "q4_m128":
+            # binding roofline: the longer of the flops at the bf16 peak and all bytes at the HBM peak
+            t_bind = max(flops / (PEAK_BF16_TFLOPS * 1e12), q4_all_bytes[label] / (PEAK_HBM_GBS * 1e9))
+            d["binding_us"] = round(t_bind * 1e6, 3)
+            d["frac_binding"] = round(t_bind / t, 4)
         parts[f"{fam} {label}"] = d
         fam_time[fam] = fam_time.get(fam, 0.0) + t
         fam_flops[fam] = fam_flops.get(fam, 0.0) + flops

@@ -290,7 +290,7 @@ int q2_dequant(const uint8_t* packed, const uint16_t* scales_f16, float* w,
  * whole process; not needed for correct use.  path: NULL, "" or "auto"
  * (M <= 16 runs the GEMV, larger M the GEMM), "gemv" (the GEMV whenever
  * M <= 16) or "gemm" (always the GEMM).  tile: NULL or "" for the automatic
- * GEMM configuration, else a configuration name (kpair, w48x192, w96x192,
+ * GEMM configuration, else a configuration name (w48x192, w96x192,
  * w64x128, w32x128, w32x64, kg2x1x4, kg4x2x2, kg2x1x2, kg2x2x4, kg2x2x2,
  * kg2x1x4r3, kg6x3x2), or an int8
  * configuration of q2_linear_a8 (a8_6x3x2, a8_4x2x2, a8_2x2x2, a8_2x1x4,

@@ -5,16 +5,13 @@
 // magic-number OR, and 16x16x32 bf16 MFMAs accumulate each 128-wide block
 // from a start value of -1.25 (or -(1 + z/16)) times the block's row sums,
 // after which one FMA per output applies the block's f16 scale.
-//  * gemm_kpair_kernel (the rank-r branch at M a multiple of 96 with enough
-//    96 x 192 tiles): eight waves, the two on each SIMD taking alternate K
-//    blocks of the same output columns; partial sums added once at the end,
-//    the branch in its epilogue.
-//  * gemm_kgroup_kernel (the linear without the branch, from a few rows to the
-//    largest M, any raggedness): the same idea for KG groups of four waves and
-//    16 MT x 64 NT tiles, in XCD-contiguous tile order, optionally with the K
-//    blocks split over two workgroups.
-//  * gemm_kernel (the low-rank branch outside the K-pair kernel's reach, narrow
-//    mid-size outputs): four waves splitting N, one block per barrier.
+//  * gemm_kgroup_kernel (M > 16, any raggedness, the rank-r branch up to
+//    r = 64 in its prologue): KG groups of four waves on a 16 MT x 64 NT tile,
+//    the groups taking alternate K blocks of the same output columns and
+//    summed once at the end, in XCD-contiguous tile order, optionally with
+//    the K blocks split over two workgroups.
+//  * gemm_kernel (the rank-r branch above r = 64 or with the 4-bit format,
+//    narrow mid-size outputs): four waves splitting N, one block per barrier.
 //  * gemv_kernel (M <= 16): a workgroup owns 16 weight rows; its waves split
 //    K, stream the codes with coalesced loads, transpose them through LDS into
 //    the matrix-core layout and finish with a fixed-order reduction.
@@ -588,485 +585,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 }
 
 // ============================================================================
-// GEMM at 96 x 192 with eight waves: the two waves of a SIMD split the K blocks
+// GEMM: KG groups of four waves split the K blocks
 // ============================================================================
-// Wave w owns the 96 x 48 output columns (w & 3) and the K blocks of parity
-// w >> 2, so the two waves sharing a SIMD (w and w + 4) compute the same output
-// tile from alternate blocks: per SIMD and block there is one wave's decode
-// and rescale (as with a single 96-row wave) but two waves to hide latency.
-// Their partial accumulators are summed once, through LDS, at the end (the
-// block-scaled sum is linear in the blocks).  One iteration covers a pair of
-// blocks: the pair's copies were issued during the previous iteration into the
-// other half of a two-pair ring.  The pair's activations form twelve 16-row
-// tasks; each wave copies its own tasks and, once its copies have landed,
-// computes their row sums on the matrix cores, so the only barrier is the one
-// that starts an iteration.
-template <int FMT, bool LR>
-__global__ __launch_bounds__(512) void gemm_kpair_kernel(LinearArgs a, int tiles_m) {
-  constexpr int BM = 96, BN = 192, MT = 6, NT = 3;
-  constexpr int DW = WFmt<FMT>::LANE_DW;
-  constexpr int BBYTES = WFmt<FMT>::BLOCK_BYTES;
-  constexpr int XSTAGE = BM * 256;                           // one activation block
-  constexpr int CODE_SLOT = (FMT == 0) ? 512 * 16 : 768 * 16; // one block's codes (2-bit: 384 chunks padded to 512)
-  constexpr int WSTAGE = CODE_SLOT + ((FMT == 0) ? 1024 : 2048);
-  constexpr int CU = (FMT == 0) ? 2 : 3;                     // code copies per thread per pair
-  constexpr int OFF_W = 4 * XSTAGE;
-  constexpr int OFF_S = OFF_W + 4 * WSTAGE;
-  constexpr int SMEM = OFF_S + 4 * BM * 4;
-  static_assert(SMEM <= 160 * 1024, "LDS budget");
-  static_assert(3 * XSTAGE >= 4 * 96 * 48 * 4, "reduction buffer");
-  __shared__ __align__(16) uint8_t smem[SMEM];
-  float (*const ss)[2][BM] = reinterpret_cast<float (*)[2][BM]>(smem + OFF_S);   // [slot][block of pair][row]
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wv & 3, par = wv >> 2;
-  const int c = lane & 15, g = lane >> 4;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t nw = n0 + wn * (BN / 4);
-  const int64_t M = a.M, N = a.N, K = a.K, KB = K / BLOCK_K;
-  const int64_t row_bytes = (FMT == 0) ? K / 4 : K / 2;
-  // Block indices in 32 bits (K <= 2^24): uniform 64-bit compares would run on the vector ALU.
-  const int kb = (int)KB;
-  const uint32_t k2b = (uint32_t)(K * 2);                  // activation row bytes
-  const NatConsts kc = (FMT == 0) ? q2_nat_consts() : q4_nat_consts();
-
-  // ---- copy sources.  Activations are copied in 16-row tasks: the pair has
-  // twelve (block q = t / 6, row tile t % 6), wave wv owns tasks wv and, for
-  // wv < 4, wv + 8 -- the same tasks whose row sums it computes, so it can wait
-  // for its own copies alone.  Copy k (0..3) of a task fills rows 4k .. 4k+3
-  // of the tile; lane l covers row 4k + (l >> 4), chunk position l & 15.
-  // M is a multiple of 96 here, so no activation row needs clamping.  The
-  // lane's source offset for copy k is its row offset (a multiple of 256) with
-  // the swizzled chunk in the low byte: row_swz(4k + (l >> 4)) = k | ((l >> 4) << 2).
-  const int xtasks = wv < 4 ? 2 : 1;
-  const uint32_t xsrc = (uint32_t)((lane >> 4) * K * 2) | (uint32_t)(((lane & 15) ^ ((lane >> 4) << 2)) << 4);
-  // Code copy v of wave wv: chunk index ci = (v * 8 + wv) * 64 + lane of the
-  // pair, block ci / CPB, chunk ci % CPB of that block.
-  constexpr int CPB = CODE_SLOT / 16;                          // chunk slots per block
-  uint32_t woff[CU];
-#pragma unroll
-  for (int v = 0; v < CU; ++v) {
-    const int ci = (v * 8 + wv) * 64 + lane;
-    const int pos = ci % CPB;
-    int col, unit;
-    if constexpr (FMT == 0) {
-      col = pos >> 1;
-      col = col < BN ? col : BN - 1;
-      unit = ((pos & 1) ^ ((col >> 2) & 1)) << 4;
-    } else {
-      col = pos >> 2;
-      unit = ((pos & 3) ^ ((col >> 1) & 3)) << 4;
-    }
-    const int64_t gc = (n0 + col < N) ? col : N - 1 - n0;
-    woff[v] = (uint32_t)(gc * row_bytes + unit);
-  }
-  // Scale / zero word: wave wv covers block (wv >> 2) of the pair, columns (wv & 3) * 64 + lane.
-  // Each is copied as the aligned word that holds it, through a resource
-  // based 4 bytes below the tile's first scale (zero point): with h the
-  // half-word position of the column's block-0 value, the word of block blk
-  // sits at so_e (blk even) or so_o (blk odd) plus 2 blk.
-  int64_t sgc = (wv & 3) * 64 + lane;
-  sgc = sgc < BN ? sgc : BN - 1;
-  sgc = (n0 + sgc < N) ? sgc : N - 1 - n0;                    // column from n0
-  const int64_t ncols = (N - n0) < BN ? (N - n0) : BN;
-  const uint32_t svl = (uint32_t)(2 * sgc * KB);
-  const uint32_t sbytes = (uint32_t)(2 * ncols * KB + 8);
-  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(reinterpret_cast<const uint8_t*>(a.s + n0 * KB) - 4, sbytes);
-  const uint32_t sh = (uint32_t)(((uintptr_t)(a.s + n0 * KB) + svl) >> 1) & 1u;
-  const uint32_t so_e = svl + 4 - 2 * sh, so_o = svl + 2 + 2 * sh;
-  __amdgpu_buffer_rsrc_t rz = rs;
-  uint32_t zo_e = 0, zo_o = 0;
-  if constexpr (FMT == 1) {
-    rz = buf_rsrc(reinterpret_cast<const uint8_t*>(a.z + n0 * KB) - 4, sbytes);
-    const uint32_t zh = (uint32_t)(((uintptr_t)(a.z + n0 * KB) + svl) >> 1) & 1u;
-    zo_e = svl + 4 - 2 * zh;
-    zo_o = svl + 2 + 2 * zh;
-  }
-  // Activation and code resources over the tile's rows (whole 96-row tiles
-  // here) and the tile's weight rows.
-  const __amdgpu_buffer_rsrc_t rx = buf_rsrc(a.x + m0 * K, (uint32_t)(BM * K * 2));
-  const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.w + n0 * row_bytes, (uint32_t)(ncols * row_bytes));
-
-  // ---- read side
-  int aoff[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) aoff[t] = c * 256 + (((4 * g + t) ^ row_swz(c)) << 4);
-  const int coff = (FMT == 0) ? c * 32 + ((((g >> 1) ^ ((c >> 2) & 1)) << 4) | ((g & 1) << 3))
-                              : c * 64 + ((g ^ ((c >> 1) & 3)) << 4);
-  uint32_t shalf = 0, zhalf = 0;
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    int64_t r = nw + 16 * j + c;
-    r = r < N ? r : N - 1;
-    shalf |= (uint32_t)((((uintptr_t)(a.s + r * KB)) >> 1) & 1) << j;
-    if constexpr (FMT == 1) zhalf |= (uint32_t)((((uintptr_t)(a.z + r * KB)) >> 1) & 1) << j;
-  }
-
-  // Copies of the pair starting at block b2, one unit at a time: units 0-7 the
-  // activation copies of this wave's tasks (4 per task), then the codes, the
-  // scale words [and zero words].  Blocks past the end re-copy the last one.
-  constexpr int XUM = 8;
-  constexpr int NU = XUM + CU + ((FMT == 0) ? 1 : 2);
-  constexpr int NWU = NU - XUM;           // weight copies, issued after the activations
-  auto task_of = [&](int k2, int& q, int& it) {
-    const int task = wv + 8 * k2;
-    q = task >= 6 ? 1 : 0;
-    it = task - 6 * q;
-  };
-  auto issue_unit = [&](int unit, int b2, int slot) {
-    if (unit < XUM) {
-      const int k2 = unit >> 2, kk = unit & 3;
-      if (k2 < xtasks) {
-        int q, it;
-        task_of(k2, q, it);
-        int blk = b2 + q;
-        blk = blk < kb ? blk : kb - 1;
-        const int r0 = 16 * it + 4 * kk;                         // first tile row of this copy
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(smem + (2 * slot + q) * XSTAGE + r0 * 256), 16,
-                                                 xsrc ^ (uint32_t)(kk << 4),
-                                                 (uint32_t)blk * 256u + (uint32_t)r0 * k2b, 0, 0);
-      }
-    } else if (unit < XUM + CU) {
-      const int v = unit - XUM;
-      const int ci0 = (v * 8 + wv) * 64;                       // uniform
-      const int q = ci0 / CPB;
-      int blk = b2 + q;
-      blk = blk < kb ? blk : kb - 1;
-      // The offset goes through a local: with the array element itself as
-      // the operand, the host compilation pass drops this kernel's launch stub.
-      const uint32_t wo = woff[v];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rw, (lds_void*)(smem + OFF_W + (2 * slot + q) * WSTAGE + (ci0 - q * CPB) * 16), 16, wo,
-          (uint32_t)blk * (uint32_t)BBYTES, 0, 0);
-    } else {
-      int blk = b2 + (wv >> 2);
-      blk = blk < kb ? blk : kb - 1;
-      const int dst = OFF_W + (2 * slot + (wv >> 2)) * WSTAGE + CODE_SLOT + (wv & 3) * 256;
-      const bool odd = (blk & 1) != 0;
-      if (unit == XUM + CU) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(smem + dst), 4, odd ? so_o : so_e,
-                                                 2u * (uint32_t)blk, 0, 0);
-      } else if constexpr (FMT == 1) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_void*)(smem + dst + 1024), 4, odd ? zo_o : zo_e,
-                                                 2u * (uint32_t)blk, 0, 0);
-      }
-    }
-  };
-  // Low-rank operands into the two activation stages starting at stage st0.
-  // The tile's rows of T (whole 96-row tiles here) and its columns of B are
-  // each one contiguous byte range in global memory, copied as such in 16-byte
-  // units (both ranges are multiples of 1024 bytes since r % 8 == 0); the
-  // source of B's columns past N is clamped to its last 16 bytes.
-  auto issue_lr = [&](int st0) {
-    const int r = a.r;
-    const uint8_t* tsrc = reinterpret_cast<const uint8_t*>(a.lr_t + m0 * 2 * r);
-    const int tbytes = BM * 4 * r;
-    for (int base = wv * 1024; base < tbytes; base += 8 * 1024)
-      __builtin_amdgcn_global_load_lds(tsrc + (uint64_t)(uint32_t)(base + lane * 16),
-                                       (lds_void*)(smem + st0 * XSTAGE + base), 16, 0, 0);
-    const uint8_t* bsrc = reinterpret_cast<const uint8_t*>(a.lr_b + n0 * r);
-    const int64_t bavail = (N - n0) * 2 * r;               // bytes of B from column n0 on
-    const int bbytes = BN * 2 * r;
-    for (int base = wv * 1024; base < bbytes; base += 8 * 1024) {
-      int64_t off = base + lane * 16;
-      off = off + 16 <= bavail ? off : bavail - 16;
-      __builtin_amdgcn_global_load_lds(bsrc + off, (lds_void*)(smem + (st0 + 1) * XSTAGE + base), 16, 0, 0);
-    }
-  };
-  auto afrag = [&](const uint8_t* st, int i, int t) -> q2_u32x4 {
-    return *reinterpret_cast<const q2_u32x4*>(st + i * 4096 + aoff[t]);
-  };
-
-  const uint32_t sone = (FMT == 0) ? 0xBFA0BFA0u : 0xBF80BF80u;   // bf16 -1.25 / -1 pairs
-  const q2_u32x4 sones = q2_u32x4{sone, sone, sone, sone};
-  // Row sums of this wave's tasks of the pair starting at block b2 (slot `slot`).
-  auto row_sums = [&](int b2, int slot) {
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      if (k2 < xtasks) {
-        int q, it;
-        task_of(k2, q, it);
-        if (b2 + q < kb) {
-          const uint8_t* st = smem + (2 * slot + q) * XSTAGE;
-          q2_f32x4 s4 = q2_f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < 4; ++t) s4 = mfma(afrag(st, it, t), sones, s4);
-          if (c == 0) *reinterpret_cast<q2_f32x4*>(&ss[slot][q][16 * it + 4 * g]) = s4;
-        }
-      }
-    }
-  };
-
-  q2_f32x4 acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = q2_f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Decode of one block's weights for this wave's columns (from its weight stage).
-  auto decode = [&](const uint8_t* wst, int blk, q2_u32x4 (&bf)[NT][4], float (&dc)[NT], float (&zc)[NT]) {
-    const uint32_t pmask = (uint32_t)(blk & 1) ? 0xFFu : 0u;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int col0 = wn * (BN / 4) + 16 * j;
-      uint32_t w[DW];
-      if constexpr (FMT == 0) {
-        const q2_u32x2 v = *reinterpret_cast<const q2_u32x2*>(wst + col0 * 32 + coff);
-        w[0] = v[0]; w[1] = v[1];
-      } else {
-        const q2_u32x4 v = *reinterpret_cast<const q2_u32x4*>(wst + col0 * 64 + coff);
-        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-      }
-      decode_block_nat<FMT>(w, bf[j], kc);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + (col0 + c) * 4);
-      uint32_t zb = 0;
-      if constexpr (FMT == 1) {
-        const uint32_t zw = *reinterpret_cast<const uint32_t*>(wst + CODE_SLOT + 1024 + (col0 + c) * 4);
-        zb = zw >> ((((zhalf ^ pmask) >> j) & 1) * 16);
-      }
-      block_scale<FMT>(w, sw >> ((((shalf ^ pmask) >> j) & 1) * 16), zb, dc[j], zc[j]);
-    }
-  };
-  // MFMAs of one block over the staged activations `st`, row sums `sb`.
-  // Fragments of tile i+1 are read while tile i's MFMAs run; each tile is
-  // rescaled right after its MFMAs (the SIMD's other wave covers the wait).
-  // The next pair's copies (nb2 >= 0) are issued two units per row tile, so the
-  // vector-memory path works in the background of the MFMAs.
-  auto mainblk = [&](const uint8_t* st, const float* sb, const q2_u32x4 (&bf)[NT][4], const float (&dc)[NT],
-                     const float (&zc)[NT], int nb2, int nslot) {
-    q2_u32x4 a0[4], a1[4];
-    q2_f32x4 s0, s1;
-    auto rd = [&](int i, q2_u32x4 (&av)[4], q2_f32x4& s4) {
-      s4 = *reinterpret_cast<const q2_f32x4*>(&sb[16 * i + 4 * g]);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) av[t] = afrag(st, i, t);
-    };
-    auto tile = [&](int i, const q2_u32x4 (&av)[4], q2_f32x4 s4) {
-      q2_f32x4 tmp[NT];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          tmp[j] = mfma(av[t], bf[j][t], t == 0 ? block_cinit<FMT>(s4, zc[j]) : tmp[j]);
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(dc[j], tmp[j][e], acc[i][j][e]);
-    };
-    rd(0, a0, s0);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      if (nb2 >= 0) {                     // tiles 0-3: activation copies, tile 4: weight copies
-        if (i < 4) {
-#pragma unroll
-          for (int un = 2 * i; un < 2 * i + 2; ++un) issue_unit(un, nb2, nslot);
-        } else if (i == 4) {
-#pragma unroll
-          for (int un = XUM; un < NU; ++un) issue_unit(un, nb2, nslot);
-        }
-      }
-      if (i & 1) {
-        if (i + 1 < MT) rd(i + 1, a0, s0);
-        tile(i, a1, s1);
-      } else {
-        if (i + 1 < MT) rd(i + 1, a1, s1);
-        tile(i, a0, s0);
-      }
-    }
-  };
-  // This wave's activation copies of the next pair have landed once only its
-  // NWU weight copies (issued after them) may still be in flight.
-  auto next_row_sums = [&](int nb2, int nslot) {
-    if (nb2 >= 0) {
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt((NWU & 15) | (7 << 4) | (15 << 8) | ((NWU >> 4) << 14));   // vmcnt(NWU)
-      asm volatile("" ::: "memory");
-      row_sums(nb2, nslot);
-    }
-  };
-
-  // Iteration ip covers the pair (2ip, 2ip+1) in ring slot ip & 1.  At its
-  // top barrier the pair's copies and row sums are complete; each wave then
-  // decodes its block and runs its MFMAs, issuing its copies of the next pair
-  // along the way, and finally computes the row sums of the tasks it copied
-  // (after its own copies have landed), which the next top barrier publishes.
-  // There is no other barrier, so the two waves of a SIMD drift apart and one
-  // decodes while the other multiplies.
-  int lr_st0 = 2;                         // activation stages holding the low-rank operands
-  if (KB > 0) {
-    for (int un = 0; un < NU; ++un) issue_unit(un, 0, 0);
-    next_row_sums(0, 0);
-    for (int ip = 0; 2 * ip < kb; ++ip) {
-      const int slot = (int)(ip & 1);
-      stage_barrier<0>();                 // the pair's copies and row sums are complete; the previous pair is done
-      const int nb2 = (2 * ip + 2 < kb) ? 2 * ip + 2 : -1;       // next pair, copied during the MFMAs
-      if constexpr (LR) {
-        if (nb2 < 0) {
-          lr_st0 = 2 * (slot ^ 1);
-          issue_lr(lr_st0);
-        }
-      }
-      const int bp = 2 * ip + par;
-      q2_u32x4 bf[NT][4];
-      float dc[NT], zc[NT];
-      decode(smem + OFF_W + (2 * slot + par) * WSTAGE, bp, bf, dc, zc);
-      if (bp < kb) {
-        mainblk(smem + (2 * slot + par) * XSTAGE, ss[slot][par], bf, dc, zc, nb2, slot ^ 1);
-      } else if (nb2 >= 0) {
-        for (int un = 0; un < NU; ++un) issue_unit(un, nb2, slot ^ 1);
-      }
-      next_row_sums(nb2, slot ^ 1);
-    }
-  } else if constexpr (LR) {
-    issue_lr(lr_st0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);          // every copy of this wave has landed
-  __syncthreads();
-
-  const float fin = (FMT == 0) ? 4.f : 16.f;
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][j][e] *= fin;
-
-  if constexpr (LR) {
-    // Both waves of a column group add the branch to their partial sums, the
-    // branch's K steps alternating between them.
-    {
-      const uint16_t* lt = reinterpret_cast<const uint16_t*>(smem + lr_st0 * XSTAGE);
-      const uint16_t* lb = reinterpret_cast<const uint16_t*>(smem + (lr_st0 + 1) * XSTAGE);
-      const int r = a.r;
-      const int ks = (3 * r + 31) / 32;
-      for (int t = par; t < ks; t += 2) {
-        const int q0 = 32 * t + 8 * g;
-        const bool lv = q0 < 3 * r;
-        const int part = q0 / r, jj = q0 - part * r;
-        q2_u32x4 bq[NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const int col = wn * (BN / 4) + 16 * j + c;
-          q2_u32x4 v = q2_u32x4{0u, 0u, 0u, 0u};
-          if (lv) {
-            const q2_u32x4 raw = *reinterpret_cast<const q2_u32x4*>(&lb[col * r + jj]);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) v[d] = (part == 1) ? f16x2_bf16_lo(raw[d]) : f16x2_bf16_hi(raw[d]);
-          }
-          bq[j] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const q2_u32x4 aq =
-              lv ? *reinterpret_cast<const q2_u32x4*>(&lt[(16 * i + c) * 2 * r + (part == 2 ? r : 0) + jj])
-                 : q2_u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int j = 0; j < NT; ++j) acc[i][j] = mfma(aq, bq[j], acc[i][j]);
-        }
-      }
-    }
-  }
-  // Under accumulation the old y values of the row-major stores are loaded
-  // now, while the tile is reduced.
-  const bool rows16 = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
-  constexpr int RP = (BM * (BN / 4) + 511) / 512;
-  q2_f32x4 yo4[RP];
-  if (a.acc && rows16) {
-#pragma unroll
-    for (int t = 0; t < RP; ++t) {
-      int row, q;
-      const bool v = row_piece<BM, BN, 512>(t, tid, (int)((M - m0) < BM ? (M - m0) : BM), (int)ncols, row, q);
-      yo4[t] = y_old4(reinterpret_cast<const q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]), v);
-    }
-  }
-  // Every wave is done reading activations and low-rank operands: the reduction
-  // buffer may overwrite them.
-  __syncthreads();
-
-  // Parity-1 partial sums -> LDS -> added by the parity-0 wave of the same columns.
-  float* red = reinterpret_cast<float*>(smem) + wn * (MT * NT * 4 * 64);
-  if (par == 1) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[((i * NT + j) * 4 + e) * 64 + lane] = acc[i][j][e];
-  }
-  __syncthreads();
-  if (rows16) {
-    // The finished tile goes through LDS once more (rows padded to OS floats,
-    // so the writes are conflict-free), and every lane then stores 16
-    // contiguous bytes of a row: whole lines reach memory instead of the
-    // 64-byte pieces of the matrix-core layout.
-    constexpr int OS = BN + 4;
-    static_assert(BM * OS * 4 <= SMEM, "output tile");
-    if (par == 0) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] += red[((i * NT + j) * 4 + e) * 64 + lane];
-    }
-    __syncthreads();                      // the partial sums are read; their space takes the tile
-    float* const out = reinterpret_cast<float*>(smem);
-    if (par == 0) {
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) out[(16 * i + 4 * g + e) * OS + wn * (BN / 4) + 16 * j + c] = acc[i][j][e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < RP; ++t) {
-      int row, q;
-      if (row_piece<BM, BN, 512>(t, tid, (int)((M - m0) < BM ? (M - m0) : BM), (int)ncols, row, q)) {
-        q2_f32x4 v = *reinterpret_cast<const q2_f32x4*>(&out[row * OS + 4 * q]);
-        if (a.acc) v += yo4[t];
-        __builtin_nontemporal_store(v, reinterpret_cast<q2_f32x4*>(&a.y[(m0 + row) * N + n0 + 4 * q]));
-      }
-    }
-  } else if (par == 0) {
-    float yo[MT][NT][4];
-    if (a.acc) {                          // every old value in flight at once, then added
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t m = m0 + 16 * i + 4 * g + e, n = nw + 16 * j + c;
-            yo[i][j][e] = y_old(&a.y[m * N + n], m < M && n < N);
-          }
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int64_t n = nw + 16 * j + c;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = acc[i][j][e] + red[((i * NT + j) * 4 + e) * 64 + lane];
-          const int64_t m = m0 + 16 * i + 4 * g + e;
-          if (a.acc) v += yo[i][j][e];
-          if (m < M && n < N) __builtin_nontemporal_store(v, &a.y[m * N + n]);
-        }
-      }
-    }
-  }
-}
-
-// ============================================================================
-// GEMM for few rows: KG groups of four waves split the K blocks
-// ============================================================================
-// With few activation rows a workgroup tile carries little matrix-core work
-// per block, and one wave per SIMD would expose every LDS, matrix-core and
-// barrier latency of a block in turn.  Here a workgroup of KG groups of four
+// One wave per SIMD would expose every LDS, matrix-core and barrier latency of
+// a block in turn, and with few activation rows a tile carries little
+// matrix-core work per block.  Here a workgroup of KG groups of four
 // waves owns a BM x BN tile (BM = 16 MT, BN = 64 NT); wave w computes the
 // BM x 16 NT columns w & 3 from the blocks KG s + (w >> 2) of each set s of KG
 // consecutive blocks, so a SIMD runs KG independent waves on the same output
@@ -1640,8 +1163,8 @@ __global__ __launch_bounds__(256 * KG) void gemm_kgroup_kernel(LinearArgs a, int
   }
   __syncthreads();
   if (rows16) {
-    // As in the K-pair kernel: the finished tile goes through LDS (rows padded
-    // to OS floats) and is stored as 16-byte pieces of contiguous rows.
+    // The finished tile goes through LDS (rows padded to OS floats) and is
+    // stored as 16-byte pieces of contiguous rows.
     constexpr int OS = BN + 4;
     static_assert(BM * OS * 4 <= SMEM, "output tile");
     if (kg == 0) {
@@ -2055,22 +1578,6 @@ static hipError_t run_gemv(const LinearArgs& a, hipStream_t stream) {
   return run_gemv_w<FMT, 4>(a, stream);
 }
 
-template <int FMT>
-static hipError_t run_gemm_kpair(const LinearArgs& a, hipStream_t stream) {
-  const int64_t tiles_m = (a.M + 95) / 96;
-  const int64_t tiles = tiles_m * ((a.N + 191) / 192);
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  if constexpr (FMT == 0) {
-    if (a.r > 0) {
-      hipLaunchKernelGGL((gemm_kpair_kernel<FMT, true>), dim3((unsigned)tiles), dim3(512), 0, stream, a,
-                         (int)tiles_m);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((gemm_kpair_kernel<FMT, false>), dim3((unsigned)tiles), dim3(512), 0, stream, a, (int)tiles_m);
-  return hipGetLastError();
-}
-
 // Row tiles per group of the K-group tile order.  Cutting the tile grid into
 // p row parts times 8 / p column parts, one block per XCD, makes the XCDs
 // together read the weights p times and x 8 / p times, the latter only while
@@ -2153,11 +1660,11 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, int ksplit, hipStream_t s
 // GEMM kernel configurations.  The automatic choice picks one of them; tests
 // can force any by name (gemm_config_id), so every configuration is exercised
 // whatever shapes the automatic choice gives it.
-static const char* const kGemmCfgNames[] = {"auto",    "kpair",   "w48x192", "w96x192", "w64x128",
-                                            "w32x128", "w32x64",  "kg2x1x4", "kg4x2x2", "kg2x1x2",
-                                            "kg2x2x4", "kg2x2x2", "kg2x1x4r3", "kg6x3x2"};
-enum GemmCfg { CFG_AUTO, CFG_KPAIR, CFG_W48x192, CFG_W96x192, CFG_W64x128, CFG_W32x128, CFG_W32x64, CFG_KG2x1x4,
-               CFG_KG4x2x2, CFG_KG2x1x2, CFG_KG2x2x4, CFG_KG2x2x2, CFG_KG2x1x4R3, CFG_KG6x3x2, CFG_COUNT };
+static const char* const kGemmCfgNames[] = {"auto",    "w48x192", "w96x192", "w64x128", "w32x128",
+                                            "w32x64",  "kg2x1x4", "kg4x2x2", "kg2x1x2", "kg2x2x4",
+                                            "kg2x2x2", "kg2x1x4r3", "kg6x3x2"};
+enum GemmCfg { CFG_AUTO, CFG_W48x192, CFG_W96x192, CFG_W64x128, CFG_W32x128, CFG_W32x64, CFG_KG2x1x4, CFG_KG4x2x2,
+               CFG_KG2x1x2, CFG_KG2x2x4, CFG_KG2x2x2, CFG_KG2x1x4R3, CFG_KG6x3x2, CFG_COUNT };
 static_assert(sizeof kGemmCfgNames / sizeof kGemmCfgNames[0] == CFG_COUNT, "configuration names");
 
 int gemm_config_id(const char* name) {
@@ -2169,11 +1676,7 @@ int gemm_config_id(const char* name) {
 template <int FMT>
 static hipError_t run_gemm_cfg(const LinearArgs& a, int cfg, int ksplit, hipStream_t stream) {
   if (cfg < CFG_KG2x1x4 && ksplit != 1) return hipErrorInvalidValue;   // only K-group tiles split K
-  const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
   switch (cfg) {
-    case CFG_KPAIR:   // whole 96-row tiles; the branch only in its LDS-staged form
-      if (a.M % 96 != 0 || (a.r > 0 && !lr_lds)) return hipErrorInvalidValue;
-      return run_gemm_kpair<FMT>(a, stream);
     case CFG_W48x192: return run_gemm<FMT, 48, 192>(a, stream);
     case CFG_W96x192: return run_gemm<FMT, 96, 192>(a, stream);
     case CFG_W64x128: return run_gemm<FMT, 64, 128>(a, stream);
@@ -2200,7 +1703,7 @@ static int gemm_auto_cfg(const LinearArgs& a) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   const bool lr_lds = FMT == 0 && a.r > 0 && a.r <= LR_RMAX && lowrank_vec(a);
   // The K-group kernels carry the rank-r branch (Q2_0, any r <= LR_RMAX) in
-  // their epilogue, so they take those calls as they take plain ones.
+  // their prologue, so they take those calls as they take plain ones.
   const bool kg_ok = a.r == 0 || (FMT == 0 && a.r <= LR_RMAX);
   const int64_t KB = a.K / BLOCK_K;
   // Up to 384 rows: K-group tiles, the widest whose workgroup count still
@@ -2211,24 +1714,20 @@ static int gemm_auto_cfg(const LinearArgs& a) {
     if (a.M <= 64) return tiles(32, 128) >= 128 ? CFG_KG2x2x4 : narrow;
     if (a.M <= 128) return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : narrow;
     if (a.M <= 256) return tiles(32, 128) >= 400 ? (FMT == 0 ? CFG_KG2x2x2 : CFG_KG2x1x2) : CFG_KG2x2x4;
-    if (tiles(96, 192) >= 128) return CFG_KG6x3x2;     // 10 % ahead of the K-pair kernel at 384 rows
+    if (tiles(96, 192) >= 128) return CFG_KG6x3x2;
     return tiles(64, 128) >= 128 ? CFG_KG4x2x2 : CFG_KG2x2x4;
   }
   if (kg_ok) {
     if (a.M <= 640) return tiles(32, 128) >= 400 ? CFG_KG2x2x2 : CFG_KG4x2x2;
-    // The 96 x 192 K-group tile (the K-pair structure with rows past M
-    // clamped, XCD-contiguous tiles; equal to the K-pair kernel at M = 1536,
-    // 5-14 % faster at M = 768) for any M once it gives enough workgroups,
+    // The 96 x 192 K-group tile for any M once it gives enough workgroups,
     // else two 48 x 192 workgroups per CU.
     if (tiles(96, 192) >= 160) return CFG_KG6x3x2;
     if (a.M >= 48 && tiles(48, 192) >= 256) return CFG_W48x192;
   }
-  // Otherwise (a branch of rank above LR_RMAX, or few tiles) prefer the
-  // largest tile that still gives a few waves of workgroups over the 256
-  // compute units.  Eight-wave 96 x 192 tiles when they fill the chip and M is
-  // a whole number of tiles (the low-rank branch only in its LDS-staged form).
-  if (a.M % 96 == 0 && tiles(96, 192) >= 256 && (a.r == 0 || lr_lds)) return CFG_KPAIR;
-  // 48 x 192 tiles run two workgroups (eight waves) per CU; with the low-rank
+  // Otherwise (a branch of rank above LR_RMAX or with the 4-bit format, or
+  // few tiles) the four-wave kernel, with the largest tile that still gives a
+  // few waves of workgroups over the 256 compute units.  48 x 192 tiles run
+  // two workgroups (eight waves) per CU; with the low-rank
   // operands staged in LDS the tile no longer fits twice, so that case keeps 96 x 192.
   if (!lr_lds && a.M >= 48 && tiles(48, 192) >= 512) return CFG_W48x192;
   if (a.M >= 96 && tiles(96, 192) >= 256) return CFG_W96x192;

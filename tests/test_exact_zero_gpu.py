@@ -46,7 +46,7 @@ def assert_close(y, ref, what=""):
     assert r["ok"], f"{what}: rel_l2={r['rel_l2']:.3e} row_ratio={r['row_ratio']:.3e}"
 
 
-GEMM_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
+GEMM_CFGS = ["w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
              "kg2x1x4", "kg4x2x2", "kg2x1x2", "kg2x2x4", "kg2x2x2", "kg2x1x4r3", "kg6x3x2"]
 # (path, tile, K split): the GEMV, every GEMM configuration whole, every K-group configuration split
 LAUNCHES = ([("gemv", None, 0)] + [("gemm", c, 1) for c in GEMM_CFGS] +
@@ -58,7 +58,7 @@ N, K = 333, 1408          # ragged N; 11 blocks, so the last K set of every conf
 def rows_for(path, tile):
     if path == "gemv":
         return 13
-    return 96 if tile == "kpair" else 75     # the K-pair kernel takes whole 96-row tiles
+    return 75
 
 
 def zero_weight(n, k, seed, zero_rows=None):
@@ -176,7 +176,7 @@ def test_q4_non_integer_zero_point_is_not_zero(force):
     assert np.all(y != 0)
 
 
-LR_LAUNCHES = [("gemv", None), ("gemm", "kpair"), ("gemm", "w48x192"), ("gemm", "w96x192"), ("gemm", "w64x128"),
+LR_LAUNCHES = [("gemv", None), ("gemm", "kg6x3x2"), ("gemm", "w48x192"), ("gemm", "w96x192"), ("gemm", "w64x128"),
                ("gemm", "w32x128"), ("gemm", "w32x64"), ("auto", None)]
 
 

@@ -186,7 +186,7 @@ def test_linear_tile_configs(m, n, k):
 # Every GEMM kernel configuration, forced through the test-only Q2_GEMM_TILE
 # override, on shapes with ragged M and N, block counts that leave the last
 # K set partial or shorter than one set, a single block and K = 0.
-GEMM_CFGS = ["kpair", "w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
+GEMM_CFGS = ["w48x192", "w96x192", "w64x128", "w32x128", "w32x64",
              "kg2x1x4", "kg4x2x2", "kg2x1x2", "kg2x2x4", "kg2x2x2", "kg2x1x4r3", "kg6x3x2"]
 CFG_SHAPES = [(75, 200, 1408), (128, 2560, 384), (33, 1000, 128), (40, 100, 0), (256, 700, 2560), (96, 333, 640)]
 _cfg_ref = {}
@@ -206,8 +206,6 @@ def _cfg_case(m, n, k):
 @pytest.mark.parametrize("cfg", GEMM_CFGS)
 @pytest.mark.parametrize("m,n,k", CFG_SHAPES)
 def test_forced_gemm_configs(cfg, m, n, k, force):
-    if cfg == "kpair":
-        m = 96 * ((m + 95) // 96)          # this configuration takes whole 96-row tiles only
     (x, p, s, ref), (x4, P, S, Z, ref4) = _cfg_case(m, n, k)
     force(tile=cfg)
     y = torch.full((m, n), float("nan"), device=DEV)
@@ -220,7 +218,7 @@ def test_forced_gemm_configs(cfg, m, n, k, force):
     assert_close(y4.cpu().numpy(), ref4, f"q4 {cfg} M={m} N={n} K={k}")
 
 
-@pytest.mark.parametrize("cfg", ["kpair", "kg6x3x2", "w48x192"])
+@pytest.mark.parametrize("cfg", ["kg6x3x2", "w48x192", "w96x192"])
 def test_output_not_16_byte_aligned(cfg, force):
     """y 4 bytes past a 16-byte boundary takes the per-element store path."""
     m, n, k = 192, 400, 640
@@ -242,9 +240,10 @@ def test_forced_gemm_config_errors(force):
     assert e.value.status == q2.Q2_ERR_ARG
     force(tile=None)                # the refused name changed nothing; the call runs
     q2.q2_linear(x, p, s)
-    force(tile="kpair")          # 75 rows are not whole 96-row tiles
+    force(tile="kg6x3x2")        # the K-group branch takes ranks up to 64 only
+    p65, s65, _, _, _, x65, _, _, A65, B65 = lowrank_case(24, 40, 256, 100, 65)
     with pytest.raises(q2.Q2Error) as e:
-        q2.q2_linear(x, p, s)
+        q2.q2_linear_lowrank(x65, p65, s65, A65, B65)
     assert e.value.status == q2.Q2_ERR_HIP
 
 
@@ -372,7 +371,7 @@ def _edge_weight(n, k, regime):
 
 
 @pytest.mark.parametrize("regime", ["mixed", "subnormal", "large"])
-@pytest.mark.parametrize("cfg,m", [("gemv", 1), ("gemv", 13), ("auto", 96), ("kpair", 192), ("kg6x3x2", 100),
+@pytest.mark.parametrize("cfg,m", [("gemv", 1), ("gemv", 13), ("auto", 96), ("w96x192", 192), ("kg6x3x2", 100),
                                    ("kg2x1x4r3", 40), ("w48x192", 75), ("kg2x2x4", 33)])
 def test_linear_scale_and_code_extremes(cfg, m, regime, force):
     n, k = 333, 1408
@@ -690,7 +689,7 @@ def _lowrank_regime(shape, regime, seed):
 
 
 @pytest.mark.parametrize("regime", ["ordinary", "subnormal", "large"])
-@pytest.mark.parametrize("cfg,m,r", [("gemv", 3, 32), ("gemv", 16, 5), ("auto", 192, 32), ("kpair", 96, 64),
+@pytest.mark.parametrize("cfg,m,r", [("gemv", 3, 32), ("gemv", 16, 5), ("auto", 192, 32), ("kg6x3x2", 96, 64),
                                      ("w48x192", 75, 32), ("w64x128", 40, 8), ("w32x64", 33, 5)])
 def test_lowrank_branch_alone_extremes(cfg, m, r, regime, force):
     """Every code 1, so W = 0 exactly whatever the (non-zero) block scales and
