@@ -432,7 +432,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="profiling mode: run warmup + steps eagerly and "
                     "print only the wall time (no graph, no per-call events)")
     ap.add_argument("--only", default="", help="comma-separated call families to run (for profiling): "
-                    "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref, a8_m1536")
+                    "gemm_m1536, gemv_m1, lowrank_r32, q4_m128, copy_ref, a8_m1536, lowrank_r4, lowrank_r64")
     ap.add_argument("--extras", action="store_true",
                     help="also time the split output projection, the quarter-size first step, the 8-bit "
                          "activation linear and the hot-cache GEMV (they launch the step's kernels at other shapes "
@@ -529,6 +529,16 @@ def main():
                           lambda k=k, p8=p8, s8=s8, y8=y8, ws8=ws8: q2.q2_linear_a8(x_by_k[k], p8, s8, y=y8,
                                                                                     workspace=ws8),
                           f"8-bit activations M={m} K={k} N={n}"))
+    for rr in (4, 64):
+        if f"lowrank_r{rr}" in args.only.split(","):
+            # the rank-r linear at the other ranks of the layer list (profiling only)
+            ar, br = I.lowrank_factors(331, rr, lr["K"], lr["N"])
+            Ar, Br = bits(ar, torch.float16), bits(br, torch.float16)
+            wsr = torch.empty(q2.lowrank_workspace_bytes(lr["M"], rr), dtype=torch.uint8, device=dev)
+            calls.append((f"lowrank_r{rr}", 2.0 * lr["M"] * lr["N"] * lr["K"] + 2.0 * lr["M"] * rr * (lr["K"] + lr["N"]),
+                          Q2_BYTES_PER_WEIGHT * lr["N"] * lr["K"],
+                          lambda Ar=Ar, Br=Br, wsr=wsr: q2.q2_linear_lowrank(xl, lp, ls, Ar, Br, y=yl, workspace=wsr),
+                          f"M={lr['M']} K={lr['K']} N={lr['N']} r={rr}"))
     if "copy_ref" in args.only.split(","):
         # calibration for the HBM counters: a plain streaming kernel of known size
         # (256 MiB read + 256 MiB written)
@@ -685,7 +695,7 @@ def main():
         out["a8_linear"] = a8
     if gemv_hot is not None:
         out["gemv_m1_hot_cache"] = gemv_hot
-    if not args.no_cpu:
+    if not args.no_cpu and not args.only:         # the oracle is timed on the whole step only
         step_calls = {}
         for c in calls:
             fam = c[0]
