@@ -153,8 +153,9 @@ size_t q2_lowrank_workspace_bytes(int64_t M, int64_t r);
  *   workspace  device scratch of >= q2_lowrank_workspace_bytes(M, r) bytes,
  *              256-byte aligned, owned by the caller; overwritten.
  * x A^T is computed once per call (into the workspace) and B (x A^T) is
- * added inside the epilogue of the Q2_0 kernel.  Asynchronous; calls that
- * share a workspace must be ordered on one stream.
+ * added inside the Q2_0 linear kernel, into the same accumulators as the
+ * quantised product.  Asynchronous; calls that share a workspace must be
+ * ordered on one stream.
  */
 int q2_linear_lowrank(const uint16_t* x_bf16, const uint8_t* packed, const uint16_t* scales_f16,
                       const uint16_t* A_f16, const uint16_t* B_f16, int64_t r,

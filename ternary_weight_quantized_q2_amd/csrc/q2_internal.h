@@ -6,8 +6,9 @@
 namespace q2dev {
 
 // One linear call: x [M, K] bf16, weights in format fmt (0 = Q2_0, 1 = 4-bit),
-// y [M, N] fp32.  lr_t / lr_b / r describe an optional low-rank term added
-// in the epilogue (lr_t = bf16 limbs [M, 2r] of x A^T, lr_b = B f16 [N, r]).
+// y [M, N] fp32.  lr_t / lr_b / r describe an optional low-rank term the
+// kernels add into their accumulators (lr_t = bf16 limbs [M, 2r] of x A^T,
+// lr_b = B f16 [N, r]).
 struct LinearArgs {
   const uint16_t* x;
   const uint8_t* w;

@@ -16,7 +16,9 @@
 //    K, stream the codes with coalesced loads, transpose them through LDS into
 //    the matrix-core layout and finish with a fixed-order reduction.
 //  * lowrank_t_kernel: x A^T once per call, as bf16 hi/lo limbs, for the
-//    branch y += (x A^T) B^T that the GEMM and GEMV epilogues add.
+//    branch y += (x A^T) B^T that the GEMMs and the GEMV add into their
+//    accumulators (the K-group kernel in its prologue, the four-wave kernel
+//    after its last block, the GEMV in one wave while the others stream).
 //
 // Every summation order is fixed, so results are bitwise reproducible.  The
 // GEMMs write y with non-temporal stores: the fp32 outputs (tens of MB) would
@@ -108,7 +110,7 @@ __device__ __forceinline__ float sum8_lanes(float v) {
   return v;
 }
 
-// ---- low-rank epilogue operands -------------------------------------------
+// ---- low-rank operands -----------------------------------------------------
 // The limbs of x A^T are stored [M, 2 r8] (hi | lo), r8 = r rounded up to a
 // multiple of 8, the padding columns zero, so every row and both halves start
 // on a 16-byte boundary.
@@ -171,9 +173,10 @@ __device__ __forceinline__ q2_u32x4 lr_bfrag(const uint16_t* B, int64_t n, int r
 // ============================================================================
 // GEMM, M > 16
 // ============================================================================
-// With LR, the workgroup's rows of the low-rank limbs x A^T and its columns of B
-// are copied into LDS in the prologue, so the epilogue's extra MFMA steps never
-// wait on global memory (r <= LR_RMAX, r % 8 == 0).
+// With LR, the four-wave kernel copies the workgroup's rows of the low-rank
+// limbs x A^T and its columns of B into LDS in the prologue, so the extra MFMA
+// steps after its last block never wait on global memory (r <= LR_RMAX,
+// r % 8 == 0).  The K-group kernel takes the branch up to the same rank.
 constexpr int LR_RMAX = 64;
 
 // Chunk swizzle of an activation row: chunk q of row r sits at position
@@ -1633,7 +1636,7 @@ static hipError_t run_gemm_kgroup(const LinearArgs& a, int ksplit, hipStream_t s
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t tiles = tiles_m * ((a.N + BN - 1) / BN);
   const int64_t KB = a.K / BLOCK_K;
-  // The rank-r branch (Q2_0, r <= LR_RMAX) rides in the epilogue; of a split
+  // The rank-r branch (Q2_0, r <= LR_RMAX) rides in the prologue; of a split
   // tile only the first part adds it.
   if ((a.r > 0 && (FMT != 0 || a.r > LR_RMAX)) || (ksplit == 2 && a.acc) || (ksplit != 1 && ksplit != 2))
     return hipErrorInvalidValue;

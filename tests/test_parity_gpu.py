@@ -519,7 +519,7 @@ LR_SHAPES = [(75, 1408, 333), (33, 128, 200), (130, 640, 700)]
 @pytest.mark.parametrize("r", [1, 5, 8, 32, 64])
 @pytest.mark.parametrize("cfg", KG_CFGS)
 def test_lowrank_every_kgroup_config(cfg, r, ksplit, force):
-    """The rank-r branch carried in the epilogue of every K-group
+    """The rank-r branch carried in the prologue of every K-group
     configuration: ragged M and N, ranks that are and are not multiples of 8,
     the K blocks whole and in two parts (of a split tile only the first part
     adds the branch), and B both at an aligned start and 2 bytes off it (the
