@@ -598,9 +598,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(LinearArgs a, int tiles_m, in
 // consecutive blocks, so a SIMD runs KG independent waves on the same output
 // columns while every block's weights are still decoded once per workgroup.
 // The KG partial sums are added in group order, through LDS, at the end.
-// A ring of NSET sets: the copies of set s + NSET - 1 are issued during set s,
-// spread over its row tiles, so with three sets a copy has two sets' time to
-// land.  Each wave copies whole 16-row activation tiles and computes their row
+// A ring of NSET sets: the copies of set s + NSET - 1 are issued during set s
+// (handed out a few per row tile; the compiler may issue them together at the
+// top of the set), so with three sets a copy has two sets' time to land.  Each wave copies whole 16-row activation tiles and computes their row
 // sums once its own copies have landed; one barrier per set publishes them.
 // Rows past M are clamped on the copy side and dropped at the store.
 // s_waitcnt vmcnt(n) for a uniform n in [LO, HI], by binary search over
