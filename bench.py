@@ -14,7 +14,7 @@ TFLOP/s (2 M N K per linear, low-rank flops added) of the whole step; the
 per-row figures (TFLOP/s for M > 1, packed-weight GB/s for M = 1) and their
 roofline fractions are reported beside it.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu] [--extras] [--dense-ref]
 """
 import argparse
 import hashlib
@@ -296,6 +296,58 @@ def measure_a8(torch, q2, I, dev, reps=20):
             "tflops_bf16": round(tot_f / tot_b / 1e12, 3), "calls": out}
 
 
+def measure_dense_bf16(torch, q2, I, dev, reps=20):
+    """A vendor dense GEMM as context for the M = 1536 Q2_0 linear: torch.mm on
+    bf16 x and bf16 W (hipBLASLt; W already dense, nothing decoded), with fp32
+    and with bf16 outputs, beside the Q2_0 linear on the same activations and
+    shapes in the same process.  Both rotate two weight copies, as the step
+    does.  Reported on its own (--dense-ref), never part of the step."""
+    m = I.GEMM_M
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(995)
+    out, tot = {}, {"f": 0.0, "q2": 0.0, "f32": 0.0, "b16": 0.0}
+    for k, n in I.GEMM_SHAPES:
+        x = torch.from_numpy(I.activations_bf16(300 + k, m, k).view(np.int16)).to(dev).view(torch.bfloat16)
+        qs = [q2.q2_pack(torch.from_numpy(I.q2_codes_fast(996 + i, n, k)).to(dev),
+                         torch.from_numpy(I.q2_scales(996 + i, n, k)).to(dev)) for i in range(2)]
+        ws = [(torch.randn(n, k, generator=gen, device=dev) * 0.02).to(torch.bfloat16) for _ in range(2)]
+        y32 = torch.empty((m, n), device=dev)
+        y16 = torch.empty((m, n), device=dev, dtype=torch.bfloat16)
+        st = {"q": 0, "a": 0, "b": 0}
+
+        def q2call():
+            p, s = qs[st["q"] % 2]
+            st["q"] += 1
+            q2.q2_linear(x, p, s, y=y32)
+
+        def dense32():
+            torch.mm(x, ws[st["a"] % 2].t(), out_dtype=torch.float32, out=y32)
+            st["a"] += 1
+
+        def dense16():
+            torch.mm(x, ws[st["b"] % 2].t(), out=y16)
+            st["b"] += 1
+        f = 2.0 * m * n * k
+        tq = _best_graph_time(torch, q2call, reps)
+        try:
+            t32 = _best_graph_time(torch, dense32, reps)
+        except Exception:                     # fp32 output not offered by this torch build
+            t32 = None
+        t16 = _best_graph_time(torch, dense16, reps)
+        out[f"K={k} N={n}"] = {"us_q2": round(tq * 1e6, 3),
+                               "us_dense_f32_out": None if t32 is None else round(t32 * 1e6, 3),
+                               "us_dense_bf16_out": round(t16 * 1e6, 3)}
+        tot["f"] += f
+        tot["q2"] += tq
+        tot["b16"] += t16
+        tot["f32"] = None if (t32 is None or tot["f32"] is None) else tot["f32"] + t32
+    res = {"shape": f"M={m}", "tflops_q2": round(tot["f"] / tot["q2"] / 1e12, 3),
+           "tflops_dense_bf16_out": round(tot["f"] / tot["b16"] / 1e12, 3),
+           "tflops_dense_f32_out": None if tot["f32"] is None else round(tot["f"] / tot["f32"] / 1e12, 3),
+           "calls": out}
+    return res
+
+
 def measure_peaks(torch, dev):
     """This GPU's measured ceilings, reported beside the published ones: a
     back-to-back bf16 16x16x32 MFMA loop (eight independent accumulators per
@@ -440,6 +492,9 @@ def main():
                          "roofline figures)")
     ap.add_argument("--no-layer-list", action="store_true",
                     help="skip the 100-linear rank-32 layer list report")
+    ap.add_argument("--dense-ref", action="store_true",
+                    help="only time torch's dense bf16 GEMM (hipBLASLt) beside the Q2_0 linear at the M=1536 "
+                         "shapes and print that report (context for the MFMA roofline; no step is run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -453,6 +508,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q2.load()
+    if args.dense_ref:
+        print(json.dumps({"dense_bf16_reference": measure_dense_bf16(torch, q2, I, dev)}))
+        return
 
     def u8(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
