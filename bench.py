@@ -300,8 +300,9 @@ def measure_dense_bf16(torch, q2, I, dev, reps=20):
     """A vendor dense GEMM as context for the M = 1536 Q2_0 linear: torch.mm on
     bf16 x and bf16 W (hipBLASLt; W already dense, nothing decoded), with fp32
     and with bf16 outputs, beside the Q2_0 linear on the same activations and
-    shapes in the same process.  Both rotate two weight copies, as the step
-    does.  Reported on its own (--dense-ref), never part of the step."""
+    shapes in the same process, and the same at the 4-bit M = 128 shapes
+    beside the 4-bit linear.  The M = 1536 calls rotate two weight copies, as
+    the step does.  Reported on its own (--dense-ref), never part of the step."""
     m = I.GEMM_M
     gen = torch.Generator(device=dev)
     gen.manual_seed(995)
@@ -345,6 +346,36 @@ def measure_dense_bf16(torch, q2, I, dev, reps=20):
            "tflops_dense_bf16_out": round(tot["f"] / tot["b16"] / 1e12, 3),
            "tflops_dense_f32_out": None if tot["f32"] is None else round(tot["f"] / tot["f32"] / 1e12, 3),
            "calls": out}
+    # the 4-bit encoder shapes at M = 128, beside the 4-bit linear
+    q4 = {}
+    for k, n in I.Q4_SHAPES:
+        x = torch.from_numpy(I.activations_bf16(341, I.Q4_M, k).view(np.int16)).to(dev).view(torch.bfloat16)
+        p4, s4, z4 = I.q4_weights(997, n, k)
+        P = torch.from_numpy(p4).to(dev)
+        S = torch.from_numpy(s4.view(np.int16)).to(dev).view(torch.float16)
+        Z = torch.from_numpy(z4.view(np.int16)).to(dev).view(torch.float16)
+        ws = [(torch.randn(n, k, generator=gen, device=dev) * 0.02).to(torch.bfloat16) for _ in range(2)]
+        y32 = torch.empty((I.Q4_M, n), device=dev)
+        y16 = torch.empty((I.Q4_M, n), device=dev, dtype=torch.bfloat16)
+        st = {"a": 0, "b": 0}
+
+        def dense32():
+            torch.mm(x, ws[st["a"] % 2].t(), out_dtype=torch.float32, out=y32)
+            st["a"] += 1
+
+        def dense16():
+            torch.mm(x, ws[st["b"] % 2].t(), out=y16)
+            st["b"] += 1
+        tq = _best_graph_time(torch, lambda: q2.q4_linear(x, P, S, Z, y32), reps)
+        try:
+            t32 = _best_graph_time(torch, dense32, reps)
+        except Exception:
+            t32 = None
+        t16 = _best_graph_time(torch, dense16, reps)
+        q4[f"M={I.Q4_M} K={k} N={n}"] = {"us_q4": round(tq * 1e6, 3),
+                                         "us_dense_f32_out": None if t32 is None else round(t32 * 1e6, 3),
+                                         "us_dense_bf16_out": round(t16 * 1e6, 3)}
+    res["q4_m128"] = q4
     return res
 
 
